@@ -1,0 +1,154 @@
+"""fp64 CPU oracle for paged-KV decode -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use this package; the product path never does.  It wraps
+``oracle.c`` (plain C, built with gcc into ``liboracle.so``) through ctypes and
+shares nothing with the HIP library.
+
+Inputs are host tensors or arrays holding the *stored* bytes (torch CPU
+tensors of dtype float32 / float16 / bfloat16 / float8_e4m3fn, int32 tables and
+lengths, int64 slot mappings).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+ORC_F32, ORC_F16, ORC_BF16, ORC_FP8 = 0, 1, 2, 3
+STATUS = {
+    0: "ok",
+    1: "bad argument",
+    2: "block id outside the pool",
+    3: "context longer than the table row",
+    4: "slot outside the pool",
+    5: "duplicate slot",
+    6: "out of memory",
+}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
+                               "-shared", "-fPIC", _SRC, "-o", tmp, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
+            lib.oracle_paged_decode.restype = i32
+            lib.oracle_paged_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp] + [i64] * 7 + [dbl] * 3 + [i32]
+            lib.oracle_cache_write.restype = i32
+            lib.oracle_cache_write.argtypes = [vp, vp, i32, vp, vp, i32, vp] + [i64] * 5 + [ctypes.c_float] * 2
+            lib.oracle_f16_to_double.restype = dbl
+            lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_bf16_to_double.restype = dbl
+            lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+            lib.oracle_fp8_to_double.restype = dbl
+            lib.oracle_fp8_to_double.argtypes = [ctypes.c_uint8]
+            lib.oracle_float_to_fp8.restype = ctypes.c_uint8
+            lib.oracle_float_to_fp8.argtypes = [ctypes.c_float]
+            _lib = lib
+    return _lib
+
+
+def _code(t) -> int:
+    import torch
+
+    return {
+        torch.float32: ORC_F32,
+        torch.float16: ORC_F16,
+        torch.bfloat16: ORC_BF16,
+        torch.float8_e4m3fn: ORC_FP8,
+    }[t.dtype]
+
+
+def _host(t, dtype=None):
+    import torch
+
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(t)
+    t = t.detach().to("cpu")
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.contiguous()
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, num_kv_heads: int,
+                 k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1) -> np.ndarray:
+    """Reference decode; returns float64 [num_seqs, num_heads, head_dim]."""
+    import torch
+
+    lib = _load()
+    q, k_cache, v_cache = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, torch.int32)
+    cl = _host(context_lens, torch.int32)
+    S, H, D = q.shape
+    NB, bs, Hkv, Dk = k_cache.shape
+    if Hkv != num_kv_heads or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q / num_kv_heads")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache dtypes differ")
+    W = bt.shape[1] if bt.dim() == 2 else 0
+    out = np.empty((S, H, D), dtype=np.float64)
+    rc = lib.oracle_paged_decode(out.ctypes.data, q.data_ptr(), _code(q), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 _code(k_cache), bt.data_ptr(), cl.data_ptr(), S, H, Hkv, D, NB, bs, W,
+                                 float(scale), float(k_scale), float(v_scale), int(nthreads))
+    if rc != 0:
+        raise OracleError(f"oracle_paged_decode: {STATUS.get(rc, rc)}")
+    return out
+
+
+def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Reference cache write on host copies; returns new (k_cache, v_cache) CPU tensors."""
+    import torch
+
+    lib = _load()
+    k, v = _host(k), _host(v)
+    kc, vc = _host(k_cache).clone(), _host(v_cache).clone()
+    sm = _host(slot_mapping, torch.int64)
+    N, Hkv, D = k.shape
+    NB, bs = kc.shape[0], kc.shape[1]
+    rc = lib.oracle_cache_write(k.data_ptr(), v.data_ptr(), _code(k), kc.data_ptr(), vc.data_ptr(), _code(kc),
+                                sm.data_ptr(), N, Hkv, D, NB, bs, float(k_scale), float(v_scale))
+    if rc != 0:
+        raise OracleError(f"oracle_cache_write: {STATUS.get(rc, rc)}")
+    return kc, vc
+
+
+def f16_to_double(bits: int) -> float:
+    return _load().oracle_f16_to_double(bits)
+
+
+def bf16_to_double(bits: int) -> float:
+    return _load().oracle_bf16_to_double(bits)
+
+
+def fp8_to_double(code: int) -> float:
+    return _load().oracle_fp8_to_double(code)
+
+
+def float_to_fp8(x: float) -> int:
+    return int(_load().oracle_float_to_fp8(x))
