@@ -1,0 +1,204 @@
+"""Paged decode benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch: the cache write of
+each sequence's new token, then paged decode (partition kernel + log-sum-exp
+merge) over the workload's context lengths.  Inputs are resident in HBM before
+timing starts; steps rotate over several independent input sets so that
+consecutive steps do not hit in the 256 MB Infinity Cache.
+
+Prints ONE JSON line: effective KV bandwidth (logical K/V bytes of every valid
+token per step / step time) in GB/s, tokens/s, the partition kernel's roofline
+position (HIP events on its stream), and the fp64 CPU oracle's throughput on
+the same workload as a reported baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "paged decode effective KV HBM GB/s (% of MI355X peak) and tokens/s at 1 GPU"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="llama7b")
+    ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own setting")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU: this build has no multi-GPU path "
+                         "(decode shards by sequence or kv head with no exchange); run with --gpus 1\n")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_447_amd as pa
+    from pa_workloads import algorithmic_bytes, get_config, kv_bytes, make_inputs, make_layout
+
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    pa.load_library()  # fails loudly if libpa.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = get_config(args.config)
+    part = cfg.partition_size if args.partition_size < 0 else args.partition_size
+    layout = make_layout(cfg)
+    ctx = layout.context_lens
+    step_kv = kv_bytes(cfg, ctx)
+    step_alg = algorithmic_bytes(cfg, ctx)
+    pool_bytes = 2 * cfg.num_blocks * cfg.block_size * cfg.num_kv_heads * cfg.head_dim * \
+        {"f32": 4, "f16": 2, "bf16": 2, "fp8": 1}[cfg.kv_dtype]
+    nsets = max(2, math.ceil(1e9 / max(1, step_kv)))
+    nsets = min(nsets, max(2, int(40e9 // pool_bytes)))
+    sets = []
+    for i in range(nsets):
+        inp = make_inputs(cfg, layout, dev, seed_offset=i)
+        inp["out"] = torch.empty_like(inp["q"])
+        inp["ws"] = pa.new_workspace(inp["q"], inp["block_tables"], cfg.block_size, cfg.num_kv_heads, part)
+        sets.append(inp)
+    host0 = None
+    if not args.no_cpu_baseline:  # generator bytes of set 0, before any kernel touches them
+        host0 = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in sets[0].items() if k not in ("out", "ws")}
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step(inp, mark=None):
+        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
+        pa.decode(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                  cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
+                  v_scale=inp["v_scale"], partition_size=part, workspace=inp["ws"], stream=sptr, mark_event=mark)
+
+    for i in range(args.warmup):
+        step(sets[i % nsets])
+    torch.cuda.synchronize()
+
+    # timed region 1: whole steps back to back
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(sets[i % nsets])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    # timed region 2: the same steps with events around the partition kernel
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:  # materialise the underlying hipEvents
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        inp = sets[i % nsets]
+        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
+        evs[i][0].record(stream)
+        pa.decode(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                  cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
+                  v_scale=inp["v_scale"], partition_size=part, workspace=inp["ws"], stream=sptr,
+                  mark_event=evs[i][1])
+    torch.cuda.synchronize()
+    part_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    for inp in sets:
+        if not torch.isfinite(inp["out"]).all():
+            raise RuntimeError("non-finite decode output")
+
+    achieved = step_alg / (part_ms * 1e-3) / 1e9
+    value = step_kv / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "fp8": "fp8-e4m3 kv / f16"}[cfg.kv_dtype],
+        "data": "synthetic (seeded N(0,1) values, seeded block allocator)",
+        "config": {
+            "workload": cfg.name,
+            "num_seqs": cfg.num_seqs,
+            "num_heads": cfg.num_heads,
+            "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "kv_dtype": cfg.kv_dtype,
+            "mean_context": float(np.mean(ctx)),
+            "partition_size": part or pa.partition_size(cfg.num_seqs, cfg.num_kv_heads, cfg.max_blocks_per_seq,
+                                                        cfg.block_size),
+            "input_sets": nsets,
+            "kv_bytes_per_step": step_kv,
+        },
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "kernel": "decode_partition (paged K/V gather + QK + online softmax + PV)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel_ms": round(part_ms, 5),
+            "algorithmic_bytes_per_launch": step_alg,
+        },
+        "cpu_baseline": None,
+    }
+
+    if host0 is not None:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        nthreads = max(1, min(cores, 64))
+        kc, vc = oracle.cache_write(host0["k_new"], host0["v_new"], host0["k_cache"], host0["v_cache"],
+                                    host0["slot_mapping"], host0["k_scale"], host0["v_scale"], inplace=True)
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            oracle.cache_write(host0["k_new"], host0["v_new"], kc, vc, host0["slot_mapping"], host0["k_scale"],
+                               host0["v_scale"], inplace=True)
+            oracle.paged_decode(host0["q"], kc, vc, host0["block_tables"], host0["context_lens"], cfg.softmax_scale,
+                                cfg.num_kv_heads, host0["k_scale"], host0["v_scale"], nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {
+            "value": round(step_kv * reps / el / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{reps} full {cfg.name} steps (cache write + fp64 decode of all {cfg.num_seqs} sequences), "
+                      f"{el:.1f} s wall, {nthreads} threads",
+            "tokens_per_s": round(cfg.num_seqs * reps / el, 2),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

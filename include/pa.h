@@ -1,0 +1,168 @@
+/*
+ * pa.h -- C ABI of the paged-KV decode library (libpa.so) for AMD gfx950.
+ *
+ * Two operations, both defined on the pages this library follows:
+ *
+ *   pa_decode       attention of one query token per head over a KV cache kept
+ *                   in fixed-size physical blocks, found through a per-sequence
+ *                   block table and bounded by per-sequence context lengths
+ *                   (page "vLLM推理引擎架构：PagedAttention机制与高吞吐推理",
+ *                   section 2.3 "PagedAttention Kernel": the kernel takes
+ *                   output, query, key_cache, value_cache, block_tables,
+ *                   context_lens and block_size, fills the caller's output,
+ *                   locates each token's block through the table and
+ *                   accumulates attention across blocks; the logical-to-physical
+ *                   translation itself is section 5.1 of page
+ *                   "vLLM框架中的KV cache优化与PagedAttention机制详解").
+ *   pa_cache_write  scatter of new tokens' K/V rows into physical slots
+ *                   (slot = block * block_size + offset, the address rule of
+ *                   page "Paged KVCache：大模型推理显存管理优化方案", section 2.3).
+ *
+ * Conventions shared by every entry point
+ *   - Every buffer is device memory owned by the caller.  No call allocates or
+ *     frees device memory, and no call synchronises with the host: work is
+ *     enqueued on opts->stream (NULL = the null stream) and the call returns.
+ *   - Tensors are described by pa_tensor: a device pointer, a pa_dtype, a rank
+ *     and per-dimension sizes and strides counted in ELEMENTS.  The last
+ *     dimension must be contiguous (stride 1); the data pointer and every
+ *     other stride (in bytes) must be multiples of 16.
+ *   - Errors are returned as pa_status; a thread-local message with the
+ *     details is available from pa_last_error().  Validation happens on the
+ *     host before anything is enqueued, so a non-OK return enqueued nothing
+ *     (except PA_ERR_HIP, reported if a launch itself fails).
+ *   - Contents of device memory are trusted: a block-table entry outside
+ *     [0, num_blocks) or a context length above max_blocks_per_seq *
+ *     block_size does not fault -- the kernel clamps it -- but the result for
+ *     that sequence is then unspecified.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_API __attribute__((visibility("default")))
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3, /* OCP e4m3fn: bias 7, max 448, no infinities, NaN = S.1111.111 */
+  PA_I32 = 4,
+  PA_I64 = 5,
+} pa_dtype;
+
+typedef struct pa_tensor {
+  void *data;        /* device pointer */
+  int32_t dtype;     /* pa_dtype */
+  int32_t ndim;      /* number of valid entries in shape/stride, 1..4 */
+  int64_t shape[4];
+  int64_t stride[4]; /* in elements */
+} pa_tensor;
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_DTYPE = -2,       /* unsupported dtype or dtype combination */
+  PA_ERR_SHAPE = -3,       /* ranks or sizes disagree */
+  PA_ERR_LAYOUT = -4,      /* inner dimension not contiguous, or misaligned */
+  PA_ERR_UNSUPPORTED = -5, /* head_dim / block_size / group size outside the built set */
+  PA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_ARG = -7,         /* a scalar argument out of range (scale, partition size, ...) */
+  PA_ERR_HIP = -8,         /* the HIP runtime reported an error while enqueuing */
+} pa_status;
+
+/* Options common to both operations.  A NULL opts means all defaults. */
+typedef struct pa_opts {
+  float k_scale;          /* fp8 caches: stored value = code * k_scale; ignored otherwise.  0 = 1.0 */
+  float v_scale;          /* likewise for the value cache.  0 = 1.0 */
+  int32_t partition_size; /* decode: tokens per context partition, a multiple of block_size;
+                             0 = library choice (pa_decode_partition_size) */
+  uint32_t flags;         /* reserved, must be 0 */
+  void *workspace;        /* decode: device scratch of >= pa_decode_workspace_size() bytes */
+  size_t workspace_bytes;
+  void *stream;           /* hipStream_t the work is enqueued on; NULL = null stream */
+  void *mark_event;       /* decode, optional hipEvent_t recorded on the stream between the
+                             partition kernel and the log-sum-exp merge (for timing); NULL = none */
+} pa_opts;
+
+/* Partition size pa_decode uses when opts->partition_size is 0.  Depends on the
+ * shapes only (never on device-resident context lengths). */
+PA_API int32_t pa_decode_partition_size(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq,
+                                 int32_t block_size);
+
+/* Bytes of workspace pa_decode needs for these shapes and partition size
+ * (0 = library choice).  Returns 0 when a single partition covers every
+ * sequence: then no workspace is needed.  Layout, all fp32: per (sequence,
+ * query head, partition) a running max and a running sum, then the
+ * unnormalised head_dim-long output of that partition. */
+PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
+                                       int64_t head_dim, int64_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_size);
+
+/*
+ * pa_decode -- paged attention decode.
+ *
+ *   out          [num_seqs, num_heads, head_dim], dtype = q's dtype or PA_F32.
+ *                out[s, h, :] = softmax_t(scale * q[s,h,:] . K_t) . V_t over the
+ *                first context_lens[s] tokens t of sequence s, where token t
+ *                lives at k_cache[block_tables[s, t / block_size], t % block_size,
+ *                h / (num_heads / num_kv_heads), :] (and likewise in v_cache).
+ *                A sequence with context length 0 gets zeros.
+ *   q            [num_seqs, num_heads, head_dim]: PA_F32, PA_F16 or PA_BF16.
+ *   k_cache,
+ *   v_cache      [num_blocks, block_size, num_kv_heads, head_dim], same shape and
+ *                dtype: PA_F32 / PA_F16 / PA_BF16 equal to q's dtype, or PA_FP8_E4M3
+ *                with an F16 or BF16 q (values are code * opts->k_scale / v_scale).
+ *   block_tables [num_seqs, max_blocks_per_seq] PA_I32; only the first
+ *                ceil(context_lens[s] / block_size) entries of row s are read.
+ *   context_lens [num_seqs] PA_I32.
+ *   block_size   tokens per block: 16 or 32; must equal k_cache.shape[1].
+ *   scale        softmax scale (finite, > 0).
+ *   num_kv_heads must equal k_cache.shape[2] and divide num_heads.
+ *   head_dim     (q.shape[2]) 64 or 128.
+ * Work: one workgroup per (sequence, kv head, context partition); with more
+ * than one partition a second kernel merges partitions by log-sum-exp, using
+ * opts->workspace.
+ */
+PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
+                           pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
+                           const pa_opts *opts);
+
+/*
+ * pa_cache_write -- scatter new tokens into the paged cache.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim]; dtype equal to the
+ *                 cache's, or PA_F32 / PA_F16 / PA_BF16 for an fp8 cache.
+ *   k_cache,
+ *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim], same shape/dtype.
+ *   slot_mapping  [num_tokens] PA_I64 or PA_I32.  Token n goes to block
+ *                 slot / block_size, offset slot % block_size.  Slots < 0 and
+ *                 slots >= num_blocks * block_size are skipped.  Slots must be
+ *                 distinct (duplicates race); writing into a block that several
+ *                 sequences share is the caller's responsibility.
+ * Same-dtype writes copy the bytes.  fp8 writes store
+ * round-to-nearest-even(x / scale) saturated to +-448 (NaN stays NaN), the
+ * division done in fp32, with scale = opts->k_scale / v_scale.
+ */
+PA_API pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor v_cache,
+                                pa_tensor slot_mapping, const pa_opts *opts);
+
+/* Static description of a status code. */
+PA_API const char *pa_status_string(pa_status s);
+
+/* Thread-local detail for the last non-OK status returned on this thread. */
+PA_API const char *pa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+PA_API const char *pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

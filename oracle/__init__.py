@@ -121,13 +121,22 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
     return out
 
 
-def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0):
-    """Reference cache write on host copies; returns new (k_cache, v_cache) CPU tensors."""
+def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0,
+                inplace: bool = False):
+    """Reference cache write; returns (k_cache, v_cache) as CPU tensors.
+
+    With ``inplace`` the given contiguous CPU caches are updated and returned;
+    otherwise host copies are made first."""
     import torch
 
     lib = _load()
     k, v = _host(k), _host(v)
-    kc, vc = _host(k_cache).clone(), _host(v_cache).clone()
+    if inplace:
+        kc, vc = k_cache, v_cache
+        if kc.device.type != "cpu" or not kc.is_contiguous() or not vc.is_contiguous():
+            raise ValueError("inplace cache_write needs contiguous CPU caches")
+    else:
+        kc, vc = _host(k_cache).clone(), _host(v_cache).clone()
     sm = _host(slot_mapping, torch.int64)
     N, Hkv, D = k.shape
     NB, bs = kc.shape[0], kc.shape[1]

@@ -1,0 +1,215 @@
+"""Python binding of libpa.so, the gfx950 paged-KV decode library.
+
+The functions here only marshal torch tensors into the C ABI of include/pa.h
+(device pointers, dtypes, shapes, strides, the current HIP stream) and turn
+status codes into exceptions.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  Importing works without a GPU (so the ABI can
+be inspected); calling an operation needs the built library and a GPU.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "LIB_PATH",
+    "PaError",
+    "load_library",
+    "decode",
+    "cache_write",
+    "workspace_size",
+    "partition_size",
+    "new_workspace",
+    "version",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = range(6)
+
+STATUS_NAMES = {
+    0: "PA_OK",
+    -1: "PA_ERR_NULL",
+    -2: "PA_ERR_DTYPE",
+    -3: "PA_ERR_SHAPE",
+    -4: "PA_ERR_LAYOUT",
+    -5: "PA_ERR_UNSUPPORTED",
+    -6: "PA_ERR_WORKSPACE",
+    -7: "PA_ERR_ARG",
+    -8: "PA_ERR_HIP",
+}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("ndim", ctypes.c_int32),
+        ("shape", ctypes.c_int64 * 4),
+        ("stride", ctypes.c_int64 * 4),
+    ]
+
+
+class PaOpts(ctypes.Structure):
+    _fields_ = [
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
+        ("partition_size", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stream", ctypes.c_void_p),
+        ("mark_event", ctypes.c_void_p),
+    ]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpa.so; raise if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_447_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.pa_decode_partition_size.restype = i32
+    lib.pa_decode_partition_size.argtypes = [i64, i64, i64, i32]
+    lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.pa_decode.restype = i32
+    lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_cache_write.restype = i32
+    lib.pa_cache_write.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [i32]
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_error.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().pa_version().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {
+        torch.float32: PA_F32,
+        torch.float16: PA_F16,
+        torch.bfloat16: PA_BF16,
+        torch.float8_e4m3fn: PA_FP8_E4M3,
+        torch.int32: PA_I32,
+        torch.int64: PA_I64,
+    }
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def describe(t) -> PaTensor:
+    """pa_tensor view of a torch tensor (no copy; the tensor must stay alive)."""
+    if t.dim() > 4 or t.dim() < 1:
+        raise ValueError("tensors of rank 1..4 only")
+    d = PaTensor()
+    d.data = t.data_ptr()
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _check_device(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _current_stream(t) -> int:
+    import torch
+
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _raise(lib, status: int):
+    raise PaError(status, lib.pa_last_error().decode(errors="replace"))
+
+
+def partition_size(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int, block_size: int) -> int:
+    return int(load_library().pa_decode_partition_size(num_seqs, num_kv_heads, max_blocks_per_seq, block_size))
+
+
+def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int,
+                   block_size: int, partition_size: int = 0) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                       max_blocks_per_seq, block_size, partition_size))
+
+
+def new_workspace(q, block_tables, block_size: int, num_kv_heads: int, partition_size: int = 0):
+    """A caller-owned workspace tensor sized for this decode shape (None if not needed)."""
+    import torch
+
+    S, H, D = q.shape
+    n = workspace_size(S, H, num_kv_heads, D, block_tables.shape[1], block_size, partition_size)
+    if n == 0:
+        return None
+    return torch.empty(n // 4 + 4, dtype=torch.float32, device=q.device)
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float, num_kv_heads: int,
+           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0, workspace=None, stream=None,
+           mark_event=None):
+    """pa_decode: fill ``out`` [S, H, D] with paged attention over the cache; returns ``out``.
+
+    ``workspace`` is a device tensor of at least workspace_size() bytes when more
+    than one partition is possible; it is allocated here if not given.
+    """
+    lib = load_library()
+    _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
+    if workspace is None:
+        workspace = new_workspace(q, block_tables, block_size, num_kv_heads, partition_size)
+    o = PaOpts()
+    o.k_scale = k_scale
+    o.v_scale = v_scale
+    o.partition_size = partition_size
+    o.flags = 0
+    if workspace is not None:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.stream = stream if stream is not None else _current_stream(q)
+    o.mark_event = mark_event.cuda_event if mark_event is not None else None
+    st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
+                       describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+    """pa_cache_write: scatter rows of k, v [N, Hkv, D] into the caches at slot_mapping [N]."""
+    lib = load_library()
+    _check_device(k, v, k_cache, v_cache, slot_mapping)
+    o = PaOpts()
+    o.k_scale = k_scale
+    o.v_scale = v_scale
+    o.stream = stream if stream is not None else _current_stream(k)
+    st = lib.pa_cache_write(describe(k), describe(v), describe(k_cache), describe(v_cache), describe(slot_mapping),
+                            ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return k_cache, v_cache

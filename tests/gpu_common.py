@@ -1,0 +1,72 @@
+"""Shared pieces of the GPU tests: run one decode step through the C ABI, and the
+same step through the oracle on host copies of the generator's bytes."""
+
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_447_amd as pa
+from pa_workloads import make_inputs, make_layout
+
+NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
+# max |gpu - oracle| allowed, by KV dtype: q-dtype output / fp32 output.  The
+# q-dtype bound is the stated target; the fp32-output bound isolates the
+# kernel's own error (fp32 accumulation, hardware exp2) from output rounding.
+TOL_OUT = {"f32": 2e-3, "f16": 2e-3, "bf16": 2e-3, "fp8": 3e-2}
+TOL_F32 = {"f32": 1e-5, "f16": 1e-4, "bf16": 1e-4, "fp8": 1e-3}
+
+
+def log(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def host_inputs(inp: dict) -> dict:
+    """Host copies of the generator's tensors, taken before any kernel runs."""
+    return {k: (v.detach().cpu().contiguous() if torch.is_tensor(v) else v) for k, v in inp.items()}
+
+
+def gpu_cache_write(cfg, inp):
+    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+
+
+def gpu_decode(cfg, inp, out_dtype=None, partition_size=None, context_lens=None, stream=None, out=None):
+    q = inp["q"]
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    part = cfg.partition_size if partition_size is None else partition_size
+    pa.decode(out, q, inp["k_cache"], inp["v_cache"], inp["block_tables"],
+              inp["context_lens"] if context_lens is None else context_lens, cfg.block_size, cfg.softmax_scale,
+              cfg.num_kv_heads, k_scale=inp["k_scale"], v_scale=inp["v_scale"], partition_size=part,
+              stream=stream)
+    return out
+
+
+def oracle_step(cfg, host: dict, context_lens=None):
+    """Oracle cache write (in place on the host copies), then oracle decode."""
+    kc, vc = oracle.cache_write(host["k_new"], host["v_new"], host["k_cache"], host["v_cache"],
+                                host["slot_mapping"], host["k_scale"], host["v_scale"], inplace=True)
+    ref = oracle.paged_decode(host["q"], kc, vc, host["block_tables"],
+                              host["context_lens"] if context_lens is None else context_lens,
+                              cfg.softmax_scale, cfg.num_kv_heads, host["k_scale"], host["v_scale"],
+                              nthreads=NTHREADS)
+    return ref, kc, vc
+
+
+def max_abs_err(out: torch.Tensor, ref: np.ndarray) -> float:
+    got = out.detach().cpu().to(torch.float64).numpy()
+    assert np.isfinite(got).all(), "non-finite output"
+    return float(np.abs(got - ref).max()) if got.size else 0.0
+
+
+def setup(cfg, device="cuda"):
+    layout = make_layout(cfg)
+    inp = make_inputs(cfg, layout, device)
+    return layout, inp

@@ -1,0 +1,199 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/pa.h
+declares, and rejects bad arguments on the host before anything is enqueued.
+
+Every call here fails validation by construction (the fake device pointers are
+never dereferenced), so these tests launch nothing, on any machine.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_447_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PA_API\s+[\w\s\*]+?\b(pa_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pa.LIB_PATH):
+        pytest.fail("libpa.so is not built (python -m paged_kv_cache_447_amd.build)")
+    return pa.load_library()
+
+
+def test_header_declares_the_two_operations():
+    syms = declared_symbols()
+    for s in ("pa_decode", "pa_cache_write", "pa_decode_workspace_size", "pa_status_string", "pa_last_error"):
+        assert s in syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), f"{s} declared in pa.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert re.match(r"^\d+\.\d+\.\d+$", pa.version())
+    for code in pa.STATUS_NAMES:
+        assert lib.pa_status_string(code)
+    assert lib.pa_status_string(0) == b"ok"
+
+
+def T(shape, dtype, data=FAKE, strides=None):
+    t = pa.PaTensor()
+    t.data = data
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(shape):
+            strides.insert(0, acc)
+            acc *= n
+    for i, n in enumerate(shape):
+        t.shape[i] = n
+        t.stride[i] = strides[i]
+    return t
+
+
+def good_decode(S=4, H=8, Hkv=2, D=128, NB=64, bs=16, W=8, kv=pa.PA_F16, q=pa.PA_F16):
+    return dict(out=T([S, H, D], q), q=T([S, H, D], q), k=T([NB, bs, Hkv, D], kv), v=T([NB, bs, Hkv, D], kv),
+                bt=T([S, W], pa.PA_I32), cl=T([S], pa.PA_I32), bs=bs, scale=0.088, hkv=Hkv)
+
+
+def call_decode(lib, a, opts=None):
+    o = opts or pa.PaOpts()
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["bs"], a["scale"], a["hkv"],
+                         ctypes.byref(o))
+
+
+def expect(lib, status, want, needle=None):
+    assert status == want, (pa.STATUS_NAMES.get(status), lib.pa_last_error())
+    if needle:
+        assert needle in lib.pa_last_error().decode()
+
+
+def test_decode_null_pointer(lib):
+    a = good_decode()
+    a["q"] = T([4, 8, 128], pa.PA_F16, data=0)
+    expect(lib, call_decode(lib, a), -1, "q")
+
+
+def test_decode_dtype_errors(lib):
+    a = good_decode(kv=pa.PA_BF16)
+    expect(lib, call_decode(lib, a), -2)  # q f16 with bf16 cache
+    a = good_decode(kv=pa.PA_FP8_E4M3, q=pa.PA_F32)
+    expect(lib, call_decode(lib, a), -2)  # fp8 cache needs f16/bf16 q
+    a = good_decode()
+    a["bt"] = T([4, 8], pa.PA_I64)
+    expect(lib, call_decode(lib, a), -2, "block_tables")
+    a = good_decode()
+    a["out"] = T([4, 8, 128], pa.PA_BF16)
+    expect(lib, call_decode(lib, a), -2, "out")
+
+
+def test_decode_shape_errors(lib):
+    a = good_decode()
+    a["bs"] = 32  # disagrees with k_cache.shape[1]
+    expect(lib, call_decode(lib, a), -3, "block_size")
+    a = good_decode()
+    a["hkv"] = 3
+    expect(lib, call_decode(lib, a), -3)
+    a = good_decode(H=6, Hkv=4)
+    expect(lib, call_decode(lib, a), -3, "multiple")
+    a = good_decode()
+    a["cl"] = T([5], pa.PA_I32)
+    expect(lib, call_decode(lib, a), -3, "context_lens")
+    a = good_decode()
+    a["v"] = T([65, 16, 2, 128], pa.PA_F16)
+    expect(lib, call_decode(lib, a), -3)
+
+
+def test_decode_layout_errors(lib):
+    a = good_decode()
+    a["q"] = T([4, 8, 128], pa.PA_F16, strides=[1024, 128, 2])
+    expect(lib, call_decode(lib, a), -4, "contiguous")
+    a = good_decode()
+    a["k"] = T([64, 16, 2, 128], pa.PA_F16, data=FAKE + 8)
+    expect(lib, call_decode(lib, a), -4, "aligned")
+    a = good_decode()
+    a["q"] = T([4, 8, 128], pa.PA_F16, strides=[1028, 129, 1])
+    expect(lib, call_decode(lib, a), -4, "stride")
+
+
+def test_decode_unsupported(lib):
+    expect(lib, call_decode(lib, good_decode(D=96)), -5, "head_dim")
+    expect(lib, call_decode(lib, good_decode(bs=8)), -5, "block_size")
+    expect(lib, call_decode(lib, good_decode(H=32, Hkv=2)), -5, "group")
+
+
+def test_decode_argument_errors(lib):
+    a = good_decode()
+    a["scale"] = float("nan")
+    expect(lib, call_decode(lib, a), -7, "scale")
+    o = pa.PaOpts()
+    o.partition_size = 24  # not a multiple of 16
+    expect(lib, call_decode(lib, good_decode(), o), -7, "partition")
+    o = pa.PaOpts()
+    o.flags = 1
+    expect(lib, call_decode(lib, good_decode(), o), -7, "flags")
+
+
+def test_decode_missing_workspace(lib):
+    o = pa.PaOpts()
+    o.partition_size = 16  # 8 blocks of 16 -> 8 partitions -> workspace required
+    expect(lib, call_decode(lib, good_decode(), o), -6, "workspace")
+    need = lib.pa_decode_workspace_size(4, 8, 2, 128, 8, 16, 16)
+    assert need == 4 * 8 * 8 * (2 + 128) * 4
+    o.workspace = FAKE
+    o.workspace_bytes = need - 4
+    expect(lib, call_decode(lib, good_decode(), o), -6)
+
+
+def test_workspace_size_zero_when_one_partition(lib):
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 8, 16, 128) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 2, 128, 8, 16, 0) == 0  # 128 tokens < default partition
+
+
+def test_partition_heuristic(lib):
+    for S, hkv, W, bs in [(32, 32, 128, 16), (64, 40, 256, 16), (128, 8, 256, 32), (8, 32, 2048, 16), (1, 1, 1, 16)]:
+        p = lib.pa_decode_partition_size(S, hkv, W, bs)
+        assert p > 0 and p % bs == 0
+
+
+def good_write(N=4, Hkv=2, D=128, NB=64, bs=16, kin=pa.PA_F16, kc=pa.PA_F16, slot=pa.PA_I64):
+    return [T([N, Hkv, D], kin), T([N, Hkv, D], kin), T([NB, bs, Hkv, D], kc), T([NB, bs, Hkv, D], kc),
+            T([N], slot)]
+
+
+def call_write(lib, args, opts=None):
+    return lib.pa_cache_write(*args, ctypes.byref(opts or pa.PaOpts()))
+
+
+def test_cache_write_errors(lib):
+    a = good_write()
+    a[4] = T([4], pa.PA_F32)
+    expect(lib, call_write(lib, a), -2, "slot_mapping")
+    expect(lib, call_write(lib, good_write(kin=pa.PA_BF16)), -2)  # bf16 into an f16 cache
+    a = good_write()
+    a[4] = T([5], pa.PA_I64)
+    expect(lib, call_write(lib, a), -3)
+    a = good_write()
+    a[2] = T([64, 16, 4, 128], pa.PA_F16)
+    expect(lib, call_write(lib, a), -3)
+    a = good_write()
+    a[0] = T([4, 2, 128], pa.PA_F16, data=0)
+    expect(lib, call_write(lib, a), -1)
+    o = pa.PaOpts()
+    o.k_scale = -1.0
+    expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), o), -7, "scale")
+    expect(lib, call_write(lib, good_write(D=8, kin=pa.PA_F16, kc=pa.PA_FP8_E4M3)), -4)  # 8-byte rows

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every expected value comes from the oracle or from the generator's own bytes,
+never from the HIP path.  Run on an MI355X with ``pytest -m gpu``.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_447_amd as pa
+from pa_workloads import get_config, make_inputs, make_layout, scaled
+from pa_workloads.configs import CONFIG_ORDER
+from tests.gpu_common import (TOL_F32, TOL_OUT, gpu_cache_write, gpu_decode, host_inputs, log, max_abs_err,
+                              oracle_step, setup)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bytes(t):
+    return t.detach().cpu().contiguous().view(torch.uint8)
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_full_size_step_matches_oracle(name):
+    """One decode step of each workload at full size: cache write (bit-exact over the
+    whole pool) then decode (q-dtype and fp32 outputs) against the oracle."""
+    cfg = get_config(name)
+    log(f"[{name}] generating")
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    log(f"[{name}] gpu step")
+    gpu_cache_write(cfg, inp)
+    out = gpu_decode(cfg, inp)
+    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    log(f"[{name}] oracle")
+    ref, kc, vc = oracle_step(cfg, host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8)), "k_cache differs from the oracle's write"
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8)), "v_cache differs from the oracle's write"
+    err = max_abs_err(out, ref)
+    err32 = max_abs_err(out32, ref)
+    log(f"[{name}] max|err| out={err:.3e} (tol {TOL_OUT[cfg.kv_dtype]})  fp32-out={err32:.3e} "
+        f"(tol {TOL_F32[cfg.kv_dtype]})  max|ref|={np.abs(ref).max():.3f}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
+
+
+SMALL = {
+    # ragged lengths around block and partition edges, a full table row, GQA groups
+    "mha_f16_edges": scaled(get_config("llama7b"), num_seqs=12, num_blocks=600, max_blocks_per_seq=40,
+                            ctx_kind="fixed", ctx_fixed=(1, 2, 15, 16, 17, 255, 256, 257, 511, 512, 513, 640)),
+    "mha_bf16_d64": scaled(get_config("llama13b_prefix"), num_seqs=16, num_heads=6, num_kv_heads=6, head_dim=64,
+                           num_blocks=900, max_blocks_per_seq=64, ctx_lo=512, ctx_hi=1024, share_group=4),
+    "gqa2_f16": scaled(get_config("gqa70b"), num_seqs=9, num_heads=8, num_kv_heads=4, num_blocks=2000,
+                       max_blocks_per_seq=48, ctx_hi=1536),
+    "gqa4_bf16_bs16": scaled(get_config("gqa70b"), num_seqs=7, num_heads=16, num_kv_heads=4, block_size=16,
+                             kv_dtype="bf16", q_dtype="bf16", num_blocks=3000, max_blocks_per_seq=96, ctx_hi=1536),
+    "gqa8_f16": scaled(get_config("gqa70b"), num_seqs=10, num_blocks=2000, max_blocks_per_seq=64, ctx_hi=2048),
+    "fp8_bf16q": scaled(get_config("fp8_long"), num_seqs=4, num_heads=8, num_kv_heads=8, q_dtype="bf16",
+                        num_blocks=1200, max_blocks_per_seq=256, ctx_lo=1, ctx_hi=4096, partition_size=256),
+    "fp8_gqa4_d64": scaled(get_config("fp8_long"), num_seqs=5, num_heads=16, num_kv_heads=4, head_dim=64,
+                           num_blocks=800, max_blocks_per_seq=128, ctx_lo=100, ctx_hi=2048, partition_size=0),
+    "f32_d128_bs32": scaled(get_config("tiny"), num_seqs=6, num_heads=4, num_kv_heads=2, head_dim=128,
+                            block_size=32, num_blocks=100, max_blocks_per_seq=10, ctx_kind="uniform", ctx_lo=1,
+                            ctx_hi=320, scale=None),
+    "full_row": scaled(get_config("llama7b"), num_seqs=3, num_blocks=200, max_blocks_per_seq=20,
+                       ctx_kind="fixed", ctx_fixed=(320, 319, 1)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("partition", [0, 64, 256])
+def test_small_cases_match_oracle(case, partition):
+    cfg = SMALL[case]
+    part = partition if partition % cfg.block_size == 0 else 0
+    log(f"[{case} p={part}]")
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    gpu_cache_write(cfg, inp)
+    out = gpu_decode(cfg, inp, partition_size=part)
+    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=part)
+    torch.cuda.synchronize()
+    ref, kc, vc = oracle_step(cfg, host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8))
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8))
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    log(f"    err={err:.3e} err32={err32:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
+
+
+@pytest.mark.parametrize("name", ["llama7b", "gqa70b", "fp8_long"])
+def test_partition_sizes_agree(name):
+    """Split-context is a re-association of the same softmax: every partition size
+    gives the oracle's answer (fp32 output), and they agree with each other."""
+    cfg = get_config(name)
+    if name != "fp8_long":
+        cfg = scaled(cfg, num_seqs=16)
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    gpu_cache_write(cfg, inp)
+    ref, _, _ = oracle_step(cfg, host)
+    outs = {}
+    for p in (cfg.block_size, 128, 256, 512, 1024, cfg.max_blocks_per_seq * cfg.block_size):
+        outs[p] = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=p)
+    torch.cuda.synchronize()
+    for p, o in outs.items():
+        e = max_abs_err(o, ref)
+        log(f"[{name}] partition {p}: err32={e:.3e}")
+        assert e <= TOL_F32[cfg.kv_dtype]
+    first = next(iter(outs.values())).double()
+    for o in outs.values():
+        assert float((o.double() - first).abs().max()) <= 2 * TOL_F32[cfg.kv_dtype]
+
+
+@pytest.mark.parametrize("kv_dtype,G,bs", [("f32", 1, 16), ("f16", 1, 16), ("bf16", 1, 32), ("f16", 8, 32),
+                                           ("bf16", 4, 16), ("fp8", 1, 16)])
+def test_needle_block_resolution_is_bit_exact(kv_dtype, G, bs):
+    """Plant one key per sequence that dominates every other score by > 200 nats: the
+    output must then be that token's V row, bit for bit -- for every needle position,
+    with and without split partitions."""
+    Hkv = 2
+    base = get_config("fp8_long" if kv_dtype == "fp8" else "llama7b")
+    cfg = scaled(base, num_seqs=6, num_heads=Hkv * G, num_kv_heads=Hkv, block_size=bs,
+                 kv_dtype=kv_dtype, q_dtype="f16" if kv_dtype == "fp8" else kv_dtype,
+                 num_blocks=1200, max_blocks_per_seq=2048 // bs, ctx_kind="fixed",
+                 ctx_fixed=(1, bs, bs + 1, 300, 1025, 2048), partition_size=0)
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    # every stored token, the new ones included, as the oracle's cache write leaves the pool
+    kc_h, vc_h = oracle.cache_write(host["k_new"], host["v_new"], host["k_cache"], host["v_cache"],
+                                    host["slot_mapping"], host["k_scale"], host["v_scale"], inplace=True)
+    inp["k_cache"], inp["v_cache"] = kc_h.cuda(), vc_h.cuda()
+    q = inp["q"]
+    for s in range(cfg.num_seqs):  # one query direction per group, so one key can dominate for all G heads
+        for kvh in range(Hkv):
+            q[s, kvh * G:(kvh + 1) * G] = q[s, kvh * G]
+    bt = layout.block_tables
+    ctx = layout.context_lens
+    k_scale = 1.0 if kv_dtype == "fp8" else inp["k_scale"]
+    rng = np.random.default_rng(3)
+    for rnd in range(5):
+        kc = inp["k_cache"].clone()
+        expected = torch.empty(q.shape, dtype=torch.float32)
+        for s in range(cfg.num_seqs):
+            L = int(ctx[s])
+            choices = [0, L - 1, min(L - 1, bs - 1), min(L - 1, bs), min(L - 1, 255), min(L - 1, 256),
+                       int(rng.integers(L))]
+            t = choices[rnd % len(choices)] if rnd < 4 else choices[-1]
+            phys, off = int(bt[s, t // bs]), t % bs
+            for kvh in range(Hkv):
+                qv = q[s, kvh * G].float()
+                if kv_dtype == "fp8":
+                    codes = torch.where(qv >= 0, 0x7E, 0xFE).to(torch.uint8)
+                    kc.view(torch.uint8)[phys, off, kvh] = codes
+                    vrow = vc_h[phys, off, kvh].float() * torch.tensor(inp["v_scale"], dtype=torch.float32)
+                else:
+                    c = 300.0 / (cfg.softmax_scale * float(qv.norm()))
+                    kc[phys, off, kvh] = (c * qv / qv.norm()).to(kc.dtype)
+                    vrow = vc_h[phys, off, kvh].float()
+                expected[s, kvh * G:(kvh + 1) * G] = vrow
+        for part in (0, bs, 256):
+            out = torch.empty_like(q)
+            pa.decode(out, q, kc, inp["v_cache"], inp["block_tables"], inp["context_lens"], bs, cfg.softmax_scale,
+                      Hkv, k_scale=k_scale, v_scale=inp["v_scale"], partition_size=part)
+            torch.cuda.synchronize()
+            want = expected.to(q.dtype)
+            got = out.cpu()
+            assert torch.equal(got.view(torch.int16) if got.dtype != torch.float32 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype != torch.float32 else want.view(torch.int32)), \
+                f"round {rnd} partition {part}"
+
+
+def test_fp8_hardware_decode_matches_ocp_table():
+    """ctx = 1 makes out = V exactly: put all 256 codes in V rows and read them back in fp32."""
+    D, bs = 128, 16
+    dev = "cuda"
+    kc = torch.zeros((4, bs, 1, D), dtype=torch.uint8, device=dev)
+    vc = torch.zeros((4, bs, 1, D), dtype=torch.uint8, device=dev)
+    vc[0, 0, 0] = torch.arange(0, 128, dtype=torch.int32).to(torch.uint8).to(dev)
+    vc[1, 0, 0] = torch.arange(128, 256, dtype=torch.int32).to(torch.uint8).to(dev)
+    bt = torch.tensor([[0], [1]], dtype=torch.int32, device=dev)
+    cl = torch.tensor([1, 1], dtype=torch.int32, device=dev)
+    q = torch.randn((2, 1, D), device=dev).half()
+    out = torch.empty((2, 1, D), dtype=torch.float32, device=dev)
+    pa.decode(out, q, kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn), bt, cl, bs, 0.1, 1)
+    got = out.cpu().view(-1).numpy()
+    for code in range(256):
+        want = oracle.fp8_to_double(code)
+        if math.isnan(want):
+            assert math.isnan(got[code])
+        else:
+            assert got[code] == np.float32(want), (code, got[code], want)
+
+
+def test_repeated_runs_are_bit_identical():
+    cfg = scaled(get_config("gqa70b"), num_seqs=24)
+    layout, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)
+    a = gpu_decode(cfg, inp)
+    b = gpu_decode(cfg, inp)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_tiny_round_trip_before_and_after_the_write():
+    """Decode the tiny workload over ctx-1 tokens (the new slots still hold NaN and
+    must not be read), write the 4 new tokens, decode over ctx."""
+    cfg = get_config("tiny")
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    before = torch.clamp(inp["context_lens"] - 1, min=0)
+    out0 = gpu_decode(cfg, inp, context_lens=before)
+    torch.cuda.synchronize()
+    ref0 = oracle.paged_decode(host["q"], host["k_cache"], host["v_cache"], host["block_tables"], before.cpu(),
+                               cfg.softmax_scale, cfg.num_kv_heads)
+    assert max_abs_err(out0, ref0) <= TOL_F32["f32"]
+    assert (out0[0] == 0).all()  # ctx 1 -> 0 before the write
+    gpu_cache_write(cfg, inp)
+    out1 = gpu_decode(cfg, inp)
+    torch.cuda.synchronize()
+    ref1, _, _ = oracle_step(cfg, host)
+    assert max_abs_err(out1, ref1) <= TOL_F32["f32"]
+
+
+def test_empty_batch_and_zero_length_sequences():
+    cfg = scaled(get_config("llama7b"), num_seqs=4, num_blocks=300)
+    layout, inp = setup(cfg)
+    out = torch.full_like(inp["q"], 7.0)
+    cl = inp["context_lens"].clone()
+    cl[1] = 0
+    cl[3] = 0
+    gpu_decode(cfg, inp, context_lens=cl, out=out)
+    torch.cuda.synchronize()
+    assert (out[1] == 0).all() and (out[3] == 0).all()
+    assert torch.isfinite(out).all()
+    empty = inp["q"][:0]
+    pa.decode(torch.empty_like(empty), empty, inp["k_cache"], inp["v_cache"], inp["block_tables"][:0],
+              inp["context_lens"][:0], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads)
+
+
+def test_side_stream_and_strided_query():
+    cfg = scaled(get_config("llama7b"), num_seqs=8, num_blocks=800)
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    gpu_cache_write(cfg, inp)
+    S, H, D = inp["q"].shape
+    big = torch.zeros((S, 3 * H, D), dtype=inp["q"].dtype, device="cuda")
+    big[:, H:2 * H] = inp["q"]
+    inp["q"] = big[:, H:2 * H]  # a view: sequence stride 3*H*D
+    out_big = torch.zeros((S, 2, H, D), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpu_decode(cfg, inp, out=out_big[:, 1])
+    side.synchronize()
+    ref, _, _ = oracle_step(cfg, host)
+    assert max_abs_err(out_big[:, 1], ref) <= TOL_F32["f16"]
+    assert (out_big[:, 0] == 0).all()
+
+
+def test_cache_write_skip_rules_and_int32_slots():
+    NB, bs, Hkv, D = 8, 16, 2, 128
+    g = torch.Generator(device="cuda").manual_seed(5)
+    kc = torch.randn((NB, bs, Hkv, D), generator=g, device="cuda").half()
+    vc = torch.randn((NB, bs, Hkv, D), generator=g, device="cuda").half()
+    k = torch.randn((5, Hkv, D), generator=g, device="cuda").half()
+    v = torch.randn((5, Hkv, D), generator=g, device="cuda").half()
+    slots = torch.tensor([3, -1, NB * bs, 127, 17], dtype=torch.int32, device="cuda")
+    hk, hv = kc.cpu(), vc.cpu()
+    pa.cache_write(k, v, kc, vc, slots)
+    torch.cuda.synchronize()
+    keep = torch.tensor([0, 3, 4])
+    ek, ev = oracle.cache_write(k.cpu()[keep], v.cpu()[keep], hk, hv, slots.cpu().long()[keep])
+    assert torch.equal(kc.cpu().view(torch.int16), ek.view(torch.int16))
+    assert torch.equal(vc.cpu().view(torch.int16), ev.view(torch.int16))
+
+
+@pytest.mark.parametrize("in_dtype", [torch.float16, torch.bfloat16, torch.float32])
+def test_fp8_cache_write_rounding_edges(in_dtype):
+    """Ties, subnormals, saturation and NaN through the kernel's quantiser, bit for bit."""
+    NB, bs, Hkv, D = 4, 16, 1, 128
+    scale = 0.5
+    grid = [oracle.fp8_to_double(c) for c in range(0x7F)]
+    vals = []
+    for c in range(0x7E):
+        vals.append((grid[c] + grid[c + 1]) / 2)  # exact midpoints -> ties to even
+        vals.append(grid[c] * 1.0001)
+    vals += [448.0, 460.0, 470.0, 1e4, float("inf"), float("nan"), 0.0, -0.0, 2.0**-12, 2.0**-10, 3 * 2.0**-11]
+    x = torch.tensor(vals, dtype=torch.float64)
+    x = torch.cat([x, -x])
+    n = x.numel()
+    rows = (n + D - 1) // D
+    xs = torch.zeros(rows * D, dtype=torch.float64)
+    xs[:n] = x
+    k = (xs.view(rows, 1, D) * scale).to(in_dtype)
+    kc = torch.zeros((NB, bs, Hkv, D), dtype=torch.uint8)
+    slots = torch.arange(rows, dtype=torch.int64) * 3
+    ek, ev = oracle.cache_write(k, k, kc.view(torch.float8_e4m3fn), kc.view(torch.float8_e4m3fn), slots, scale, scale)
+    dk = kc.clone().cuda()
+    dv = kc.clone().cuda()
+    pa.cache_write(k.cuda(), k.cuda(), dk.view(torch.float8_e4m3fn), dv.view(torch.float8_e4m3fn), slots.cuda(),
+                   k_scale=scale, v_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dk.cpu(), ek.view(torch.uint8))
+    assert torch.equal(dv.cpu(), ev.view(torch.uint8))
