@@ -27,7 +27,12 @@ template <> struct Elem<f32_t> {
   static constexpr int kPer16 = 4;
   __device__ static void unpack(u32x4 w, float *f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f[i] = __builtin_bit_cast(float, w[i]);
+    for (int i = 0; i < 4; ++i) {
+      // copy the lane out first: a bit cast applied directly to a vector
+      // element is lowered as a read of element 0
+      const uint32_t x = w[i];
+      f[i] = __builtin_bit_cast(float, x);
+    }
   }
   __device__ static float load(const void *p, int64_t i) { return reinterpret_cast<const float *>(p)[i]; }
   __device__ static void store(void *p, int64_t i, float x) { reinterpret_cast<float *>(p)[i] = x; }

@@ -230,6 +230,7 @@ def test_tiny_round_trip_before_and_after_the_write():
 def test_empty_batch_and_zero_length_sequences():
     cfg = scaled(get_config("llama7b"), num_seqs=4, num_blocks=300)
     layout, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)  # each sequence's last slot holds poison until its token is written
     out = torch.full_like(inp["q"], 7.0)
     cl = inp["context_lens"].clone()
     cl[1] = 0
