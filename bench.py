@@ -34,6 +34,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="llama7b")
     ap.add_argument("--partition-size", type=int, default=-1, help="-1: the workload's own setting")
+    ap.add_argument("--num-workers", type=int, default=0, help="0: the library's choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target wall time of the oracle sample")
     return ap.parse_args()
@@ -74,7 +75,7 @@ def main():
     for i in range(nsets):
         inp = make_inputs(cfg, layout, dev, seed_offset=i)
         inp["out"] = torch.empty_like(inp["q"])
-        inp["ws"] = pa.new_workspace(inp["q"], inp["block_tables"], cfg.block_size, cfg.num_kv_heads, part)
+        inp["ws"] = pa.new_workspace(inp["q"], cfg.num_kv_heads, args.num_workers)
         sets.append(inp)
     host0 = None
     if not args.no_cpu_baseline:  # generator bytes of set 0, before any kernel touches them
@@ -83,12 +84,19 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def step(inp, mark=None):
+    def write(inp):
         pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
                        k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
+
+    def decode(inp):
         pa.decode(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
                   cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
-                  v_scale=inp["v_scale"], partition_size=part, workspace=inp["ws"], stream=sptr, mark_event=mark)
+                  v_scale=inp["v_scale"], partition_size=part, num_workers=args.num_workers, workspace=inp["ws"],
+                  stream=sptr)
+
+    def step(inp):
+        write(inp)
+        decode(inp)
 
     for i in range(args.warmup):
         step(sets[i % nsets])
@@ -105,7 +113,8 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
-    # timed region 2: the same steps with events around the partition kernel
+    # timed region 2: the same steps with HIP events around the decode kernel,
+    # recorded on the stream the kernels run on
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b in evs:  # materialise the underlying hipEvents
         a.record(stream)
@@ -113,13 +122,10 @@ def main():
     torch.cuda.synchronize()
     for i in range(args.steps):
         inp = sets[i % nsets]
-        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
-                       k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
+        write(inp)
         evs[i][0].record(stream)
-        pa.decode(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-                  cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
-                  v_scale=inp["v_scale"], partition_size=part, workspace=inp["ws"], stream=sptr,
-                  mark_event=evs[i][1])
+        decode(inp)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     part_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     for inp in sets:
@@ -150,15 +156,15 @@ def main():
             "block_size": cfg.block_size,
             "kv_dtype": cfg.kv_dtype,
             "mean_context": float(np.mean(ctx)),
-            "partition_size": part or pa.partition_size(cfg.num_seqs, cfg.num_kv_heads, cfg.max_blocks_per_seq,
-                                                        cfg.block_size),
+            "partition_size": part,
+            "num_workers": pa.num_workers(args.num_workers),
             "input_sets": nsets,
             "kv_bytes_per_step": step_kv,
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
         "roofline": {
-            "kernel": "decode_partition (paged K/V gather + QK + online softmax + PV)",
+            "kernel": "decode (paged K/V gather + QK + online softmax + PV + in-kernel log-sum-exp merge)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -71,7 +71,7 @@ typedef enum pa_status {
   PA_ERR_SHAPE = -3,       /* ranks or sizes disagree */
   PA_ERR_LAYOUT = -4,      /* inner dimension not contiguous, or misaligned */
   PA_ERR_UNSUPPORTED = -5, /* head_dim / block_size / group size outside the built set */
-  PA_ERR_WORKSPACE = -6,   /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_WORKSPACE = -6,   /* workspace missing, misaligned or smaller than pa_decode_workspace_size() */
   PA_ERR_ARG = -7,         /* a scalar argument out of range (scale, partition size, ...) */
   PA_ERR_HIP = -8,         /* the HIP runtime reported an error while enqueuing */
 } pa_status;
@@ -80,29 +80,31 @@ typedef enum pa_status {
 typedef struct pa_opts {
   float k_scale;          /* fp8 caches: stored value = code * k_scale; ignored otherwise.  0 = 1.0 */
   float v_scale;          /* likewise for the value cache.  0 = 1.0 */
-  int32_t partition_size; /* decode: tokens per context partition, a multiple of block_size;
-                             0 = library choice (pa_decode_partition_size) */
+  int32_t partition_size; /* decode: tokens per split-context work unit, a multiple of block_size;
+                             0 = library choice (a few dozen tokens) */
+  int32_t num_workers;    /* decode: wavefronts that share the work (rounded up to a multiple of 4);
+                             0 = library choice for the current device */
   uint32_t flags;         /* reserved, must be 0 */
+  uint32_t reserved;      /* must be 0 */
   void *workspace;        /* decode: device scratch of >= pa_decode_workspace_size() bytes */
   size_t workspace_bytes;
   void *stream;           /* hipStream_t the work is enqueued on; NULL = null stream */
-  void *mark_event;       /* decode, optional hipEvent_t recorded on the stream between the
-                             partition kernel and the log-sum-exp merge (for timing); NULL = none */
 } pa_opts;
 
-/* Partition size pa_decode uses when opts->partition_size is 0.  Depends on the
- * shapes only (never on device-resident context lengths). */
-PA_API int32_t pa_decode_partition_size(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq,
-                                 int32_t block_size);
+/* Number of workers pa_decode launches for this request (0 = the library's
+ * choice for the current device).  Always a positive multiple of 4. */
+PA_API int32_t pa_decode_num_workers(int32_t requested);
 
-/* Bytes of workspace pa_decode needs for these shapes and partition size
- * (0 = library choice).  Returns 0 when a single partition covers every
- * sequence: then no workspace is needed.  Layout, all fp32: per (sequence,
- * query head, partition) a running max and a running sum, then the
- * unnormalised head_dim-long output of that partition. */
+/* Bytes of workspace pa_decode needs: one int32 counter per (sequence, kv
+ * head), then two partial-result slots per worker, each holding for every
+ * query head of a group a running max, a running sum and an unnormalised
+ * head_dim-long output (fp32).  num_workers as in pa_opts (0 = default).
+ * The workspace belongs to the caller: it must be zero-filled once before its
+ * first use; every pa_decode call leaves the counters at zero again.  One
+ * workspace serves one pa_decode at a time (calls that overlap on different
+ * streams need separate workspaces). */
 PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
-                                       int64_t head_dim, int64_t max_blocks_per_seq, int32_t block_size,
-                                       int32_t partition_size);
+                                       int64_t head_dim, int32_t num_workers);
 
 /*
  * pa_decode -- paged attention decode.
@@ -125,9 +127,12 @@ PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int6
  *   scale        softmax scale (finite, > 0).
  *   num_kv_heads must equal k_cache.shape[2] and divide num_heads.
  *   head_dim     (q.shape[2]) 64 or 128.
- * Work: one workgroup per (sequence, kv head, context partition); with more
- * than one partition a second kernel merges partitions by log-sum-exp, using
- * opts->workspace.
+ *   opts         workspace (required), stream, fp8 scales, work split.
+ * Work: one launch of num_workers persistent wavefronts.  The contexts of all
+ * (sequence, kv head) pairs are cut into work units of partition_size tokens
+ * and every worker takes an equal contiguous share of the units; a context
+ * that two or more workers share is merged by log-sum-exp in the same launch
+ * by whichever of them finishes last.
  */
 PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
                            pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,

@@ -19,7 +19,7 @@ __all__ = [
     "decode",
     "cache_write",
     "workspace_size",
-    "partition_size",
+    "num_workers",
     "new_workspace",
     "version",
 ]
@@ -56,11 +56,12 @@ class PaOpts(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("partition_size", ctypes.c_int32),
+        ("num_workers", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
-        ("mark_event", ctypes.c_void_p),
     ]
 
 
@@ -78,14 +79,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch carries its own HIP runtime; loading it first makes libpa bind to
+    # that same runtime, so torch's device pointers and streams are valid here
+    import torch  # noqa: F401
+
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m paged_kv_cache_447_amd.build`")
     lib = ctypes.CDLL(path)
     i64, i32 = ctypes.c_int64, ctypes.c_int32
-    lib.pa_decode_partition_size.restype = i32
-    lib.pa_decode_partition_size.argtypes = [i64, i64, i64, i32]
+    lib.pa_decode_num_workers.restype = i32
+    lib.pa_decode_num_workers.argtypes = [i32]
     lib.pa_decode_workspace_size.restype = ctypes.c_size_t
-    lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_cache_write.restype = i32
@@ -150,49 +155,47 @@ def _raise(lib, status: int):
     raise PaError(status, lib.pa_last_error().decode(errors="replace"))
 
 
-def partition_size(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int, block_size: int) -> int:
-    return int(load_library().pa_decode_partition_size(num_seqs, num_kv_heads, max_blocks_per_seq, block_size))
+def num_workers(requested: int = 0) -> int:
+    """Workers pa_decode launches for this request (0 = the library's choice for the current device)."""
+    return int(load_library().pa_decode_num_workers(requested))
 
 
-def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, max_blocks_per_seq: int,
-                   block_size: int, partition_size: int = 0) -> int:
-    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                       max_blocks_per_seq, block_size, partition_size))
+def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int, num_workers: int = 0) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, num_workers))
 
 
-def new_workspace(q, block_tables, block_size: int, num_kv_heads: int, partition_size: int = 0):
-    """A caller-owned workspace tensor sized for this decode shape (None if not needed)."""
+def new_workspace(q, num_kv_heads: int, num_workers: int = 0):
+    """A zero-filled, caller-owned decode workspace for queries shaped like ``q``.
+
+    pa_decode leaves its counters at zero, so one workspace can serve any
+    number of calls of this shape, one at a time."""
     import torch
 
     S, H, D = q.shape
-    n = workspace_size(S, H, num_kv_heads, D, block_tables.shape[1], block_size, partition_size)
-    if n == 0:
-        return None
-    return torch.empty(n // 4 + 4, dtype=torch.float32, device=q.device)
+    n = workspace_size(max(S, 1), H, num_kv_heads, D, num_workers)
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float, num_kv_heads: int,
-           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0, workspace=None, stream=None,
-           mark_event=None):
+           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0, num_workers: int = 0, workspace=None,
+           stream=None):
     """pa_decode: fill ``out`` [S, H, D] with paged attention over the cache; returns ``out``.
 
-    ``workspace`` is a device tensor of at least workspace_size() bytes when more
-    than one partition is possible; it is allocated here if not given.
+    ``workspace`` is a zero-filled device tensor from new_workspace() (made
+    here, once per call, if not given; pass one to avoid that allocation).
     """
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
     if workspace is None:
-        workspace = new_workspace(q, block_tables, block_size, num_kv_heads, partition_size)
+        workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
     o.k_scale = k_scale
     o.v_scale = v_scale
     o.partition_size = partition_size
-    o.flags = 0
-    if workspace is not None:
-        o.workspace = workspace.data_ptr()
-        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.num_workers = num_workers
+    o.workspace = workspace.data_ptr()
+    o.workspace_bytes = workspace.numel() * workspace.element_size()
     o.stream = stream if stream is not None else _current_stream(q)
-    o.mark_event = mark_event.cuda_event if mark_event is not None else None
     st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                        describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
     if st != 0:

@@ -1,224 +1,341 @@
-// Paged decode, split-context partition kernel, vector-ALU path.
+// Paged decode on the vector ALUs: persistent, balanced split-context workers.
 //
-// One workgroup (4 wave64s) per (context partition, kv head, sequence).  The
-// table lookup follows the logical-to-physical translation of the page
+// The table lookup follows the logical-to-physical translation of the page
 // "vLLM框架中的KV cache优化与PagedAttention机制详解" (section 5.1: find the KV range,
-// map logical block numbers to physical ones, handle reads that cross blocks),
-// with the address rule physical = block * block_size + offset of page
+// map logical block numbers to physical ones, handle reads that cross blocks;
+// section 5.2: translate many block numbers at once, prefetch ahead), with
+// the address rule physical = block * block_size + offset of page
 // "Paged KVCache：大模型推理显存管理优化方案" (section 2.3).  The per-block score /
 // cross-block accumulation split is the one page
 // "vLLM推理引擎架构：PagedAttention机制与高吞吐推理" (section 2.3) describes.
 //
-// Data movement (the whole cost of this kernel):
-//   A token's K row for one kv head is head_dim * elem bytes, contiguous.  LPR
-//   lanes cover it with 16-byte loads, so one wave-wide load instruction reads
-//   TPW = 64 / LPR consecutive tokens of one block.  A wave takes chunks of
-//   CH = TPW * NL tokens (chunks of a partition are dealt round-robin to the 4
-//   waves), issuing all NL K loads and NL V loads of a chunk before using any,
-//   so 2 * NL * 1 KiB per wave are in flight.  The block id of each load is
-//   wave-uniform and comes through the scalar cache.
+// Work distribution is in pa_sched.h: every wavefront is one worker that
+// streams an equal share of all (sequence, kv head) contexts.
 //
-// Arithmetic per chunk (fp32): score = (q * scale * log2 e) . K via per-lane
-// FMAs and a DPP sum over the LPR lanes of a token; a running max m and sum l
-// per wave with the usual rescale by exp2(m_old - m_new); acc += p * V.  Waves
-// merge their (m, l, acc) through LDS at the end.  A partition that is its
-// sequence's only one writes the normalised output; otherwise it writes
-// (m, l, acc) to the workspace for the log-sum-exp merge kernel.
-#include "pa_device.h"
-#include "pa_internal.h"
+// Data movement (the whole cost of this kernel): a token's K row for one kv
+// head is head_dim * elem bytes, contiguous.  LPR lanes cover it with 16-byte
+// loads, so one wave-wide load reads TPW = 64 / LPR consecutive tokens of one
+// block.  A chunk is NL such loads (CH = TPW * NL tokens) of K and the same of
+// V.  The loop is a rolling pipeline: the next chunk's K loads are issued as
+// soon as this chunk's scores are computed, its V loads as soon as this
+// chunk's V rows are accumulated, so a wave always has a chunk's worth of K or
+// V in flight.  Block-table entries come through the scalar unit one chunk
+// ahead.  Loads past the end of a segment are redirected to its last token
+// (already in cache), never to another worker's tokens.
+//
+// Arithmetic (fp32): score = (q . K) * scale * log2(e), the dot product per lane
+// with v_dot2 (16-bit KV) or FMAs (fp32 / fp8 KV), then a DPP sum over the LPR
+// lanes of a token; running max m and sum l with the rescale by
+// exp2(m_old - m_new) per chunk; acc += p * V.  Masked tokens get p = 0 and a
+// finite (duplicated) V row, so nothing poisons the sum.
+#include "pa_sched.h"
 
 namespace pa {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesPerWG = 4;
 
-template <typename QT>
-__device__ __forceinline__ void store_out(const DecodeArgs &a, int64_t idx, float x) {
-  if (a.out_f32)
-    reinterpret_cast<float *>(a.out)[idx] = x;
-  else
-    Elem<QT>::store(a.out, idx, x);
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+
+// Block tables and context lengths are never written during a launch: reading
+// them through the constant address space lets uniform reads use the scalar unit.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+__device__ __forceinline__ const_i32 *as_const(const int32_t *p) { return (const_i32 *)(uintptr_t)p; }
+
+// One lane's slice of a query row and its dot product with a 16-byte K slice.
+template <typename KVT, typename QT> struct QSlice;
+
+template <> struct QSlice<f16_t, f16_t> {
+  u32x4 w;
+  __device__ void load(const void *q, int64_t off) { w = ld16(reinterpret_cast<const _Float16 *>(q) + off); }
+  __device__ float dot(u32x4 k) const {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qa = w[i], ka = k[i];
+      d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, qa), __builtin_bit_cast(h2_t, ka), d, false);
+    }
+    return d;
+  }
+};
+
+template <> struct QSlice<bf16_t, bf16_t> {
+  u32x4 w;
+  __device__ void load(const void *q, int64_t off) { w = ld16(reinterpret_cast<const uint16_t *>(q) + off); }
+  __device__ float dot(u32x4 k) const {
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qa = w[i], ka = k[i];
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, qa), __builtin_bit_cast(b2_t, ka), d, false);
+    }
+    return d;
+  }
+};
+
+template <> struct QSlice<f32_t, f32_t> {
+  float f[4];
+  __device__ void load(const void *q, int64_t off) { Elem<f32_t>::unpack(ld16(reinterpret_cast<const float *>(q) + off), f); }
+  __device__ float dot(u32x4 k) const {
+    float kf[4];
+    Elem<f32_t>::unpack(k, kf);
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d = __builtin_fmaf(f[i], kf[i], d);
+    return d;
+  }
+};
+
+// fp8 K with a 16-bit query: 16 codes per slice, the query slice kept in fp32
+template <typename QT> struct QSliceFp8 {
+  float f[16];
+  __device__ void load(const void *q, int64_t off) {
+    const char *p = reinterpret_cast<const char *>(q) + off * 2;
+    Elem<QT>::unpack(ld16(p), f);
+    Elem<QT>::unpack(ld16(p + 16), f + 8);
+  }
+  __device__ float dot(u32x4 k) const {
+    float kf[16];
+    Elem<fp8_t>::unpack(k, kf);
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) d = __builtin_fmaf(f[i], kf[i], d);
+    return d;
+  }
+};
+template <> struct QSlice<fp8_t, f16_t> : QSliceFp8<f16_t> {};
+template <> struct QSlice<fp8_t, bf16_t> : QSliceFp8<bf16_t> {};
+
+// VEC consecutive output values of one lane, rounded to the output dtype.
+template <typename OT, int VEC>
+__device__ __forceinline__ void store_vec(void *base, int64_t off, const float *x) {
+  if constexpr (sizeof(typename OT::storage) == 4) {
+#pragma unroll
+    for (int j = 0; j < VEC; j += 4) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, x[j + i]);
+      st16(reinterpret_cast<float *>(base) + off + j, w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < VEC; j += 8) {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t lo, hi;
+        if constexpr (__is_same(OT, f16_t)) {
+          lo = __builtin_bit_cast(uint16_t, (_Float16)x[j + 2 * i]);
+          hi = __builtin_bit_cast(uint16_t, (_Float16)x[j + 2 * i + 1]);
+        } else {
+          lo = f32_to_bf16_rne(x[j + 2 * i]);
+          hi = f32_to_bf16_rne(x[j + 2 * i + 1]);
+        }
+        w[i] = lo | (hi << 16);
+      }
+      st16(reinterpret_cast<uint16_t *>(base) + off + j, w);
+    }
+  }
 }
 
-template <typename KVT, typename QT, int D, int G, int NL>
-__global__ void __launch_bounds__(kThreads) decode_partition_valu(const DecodeArgs a) {
-  constexpr int VEC = Elem<KVT>::kPer16;  // KV elements per 16-byte load
-  constexpr int LPR = D / VEC;            // lanes per token row
-  constexpr int TPW = 64 / LPR;           // tokens per wave-wide load
-  constexpr int CH = TPW * NL;            // tokens per wave chunk
-  static_assert(LPR >= 4 && LPR <= 32, "row must span 4..32 lanes");
+template <typename KVT, typename QT, int D, int G, int BS, int NL>
+struct ValuSeg {
+  static constexpr int VEC = Elem<KVT>::kPer16;  // KV elements per 16-byte load
+  static constexpr int LPR = D / VEC;            // lanes per token row
+  static constexpr int TPW = 64 / LPR;           // tokens per wave-wide load
+  static constexpr int CH = TPW * NL;            // tokens per chunk
+  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
+  static constexpr int EB = Elem<KVT>::kBytes;
+  static_assert(LPR >= 4 && LPR <= 32, "a row must span 4..32 lanes");
+  static_assert(BS % TPW == 0, "a wave-wide load must stay inside one block");
 
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-  __shared__ float sm_acc[kWaves][G][D];
-
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_ctx ? a.max_ctx : ctx);
-  const int t0 = part * a.partition_size;
-  if (t0 >= ctx) {
-    if (part == 0) {  // empty context: the output is zero
-      for (int i = threadIdx.x; i < G * D; i += kThreads) {
-        const int h = kvh * G + i / D;
-        store_out<QT>(a, (int64_t)seq * a.o_ss + (int64_t)h * a.o_sh + i % D, 0.0f);
-      }
-    }
-    return;
-  }
-  const int t1 = min(ctx, t0 + a.partition_size);
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane % LPR;  // which 16-byte slice of the row
-  const int g = lane / LPR;  // which token of a wave-wide load
-
-  // query slice, pre-scaled into the log2 domain
-  float qf[G][VEC];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const int64_t base = (int64_t)seq * a.q_ss + (int64_t)(kvh * G + h) * a.q_sh + r * VEC;
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) qf[h][v] = Elem<QT>::load(a.q, base + v) * a.qk_scale_log2;
-  }
-
+  const DecodeArgs &a;
+  const int lane, r, g;  // lane, 16-byte slice of the row, token of a wave-wide load
   float m[G], l[G], acc[G][VEC];
+
+  __device__ ValuSeg(const DecodeArgs &args, int ln) : a(args), lane(ln), r(ln % LPR), g(ln / LPR) {}
+
+  // Block ids of the chunk starting at cs: the chunk spans NBC blocks (one
+  // when it is shorter than a block), and wave-wide load i reads block
+  // (i * TPW) / BS of them.  A load past `last` reads last's block, which is
+  // always one of the chunk's own.
+  static constexpr int NBC = CH >= BS ? CH / BS : 1;
+  __device__ __forceinline__ void fetch_blocks(const_i32 *bt, int cs, int last, int *blk) const {
+    int e[NBC];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.0f;
+    for (int j = 0; j < NBC; ++j) e[j] = bt[min(cs + j * BS, last) >> LOG2BS];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[h][v] = 0.0f;
+    for (int j = 0; j < NBC; ++j) e[j] = e[j] < 0 ? 0 : (e[j] >= a.num_blocks ? a.num_blocks - 1 : e[j]);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) blk[i] = e[NBC == 1 ? 0 : (i * TPW) / BS];
   }
 
-  const int32_t *bt = a.block_tables + (int64_t)seq * a.bt_ss;
-  const char *kb = reinterpret_cast<const char *>(a.k_cache) +
-                   ((int64_t)kvh * a.k_sh + r * VEC) * Elem<KVT>::kBytes;
-  const char *vb = reinterpret_cast<const char *>(a.v_cache) +
-                   ((int64_t)kvh * a.v_sh + r * VEC) * Elem<KVT>::kBytes;
-  const int bmask = a.block_size - 1;
-  const int nchunks = (t1 - t0 + CH - 1) / CH;
+  __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
+                                        u32x4 *dst) const {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int t = min(cs + i * TPW + g, last);
+      dst[i] = ld16(base + ((int64_t)blk[i] * sb + (int64_t)(t & (BS - 1)) * st) * EB);
+    }
+  }
 
-  for (int c = wave; c < nchunks; c += kWaves) {
-    const int cb = t0 + c * CH;
+  __device__ void run(int s, int kvh, int t_lo, int t_hi) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[h][v] = 0.0f;
+    }
+    if (t_hi <= t_lo) return;
+    const int last = t_hi - 1;
+    const_i32 *bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
+    const char *kb = reinterpret_cast<const char *>(a.k_cache) + ((int64_t)kvh * a.k_sh + r * VEC) * EB;
+    const char *vb = reinterpret_cast<const char *>(a.v_cache) + ((int64_t)kvh * a.v_sh + r * VEC) * EB;
+
+    QSlice<KVT, QT> q[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) q[h].load(a.q, (int64_t)s * a.q_ss + (int64_t)(kvh * G + h) * a.q_sh + r * VEC);
+    int blk[NL];
     u32x4 kr[NL], vr[NL];
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int tu = cb + i * TPW;  // wave-uniform first token of this load
-      if (tu < t1) {
-        int blk = bt[tu >> a.log2_block_size];
-        blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-        const int tok = (tu & bmask) + g;
-        kr[i] = ld16(kb + ((int64_t)blk * a.k_sb + (int64_t)tok * a.k_st) * Elem<KVT>::kBytes);
-        vr[i] = ld16(vb + ((int64_t)blk * a.v_sb + (int64_t)tok * a.v_st) * Elem<KVT>::kBytes);
-      } else {
-        kr[i] = u32x4{0u, 0u, 0u, 0u};
-        vr[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    fetch_blocks(bt, t_lo, last, blk);
+    // q first, then K, then V: the loop's first wait is then for K alone
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb, a.k_sb, a.k_st, t_lo, last, blk, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(vb, a.v_sb, a.v_st, t_lo, last, blk, vr);
+    __builtin_amdgcn_sched_barrier(0);
 
-    float s[G][NL];
+    const int nch = (t_hi - t_lo + CH - 1) / CH;
+    int cs = t_lo;
+    for (int c = 0; c < nch; ++c) {
+      // the next chunk (the last one again at the end: a cache hit, never used)
+      const int cn = c + 1 < nch ? cs + CH : cs;
+      int nblk[NL];
+      fetch_blocks(bt, cn, last, nblk);
+      // the scheduler would otherwise sink table reads and loads down to their
+      // uses and drain the pipeline: keep the program order at these points
+      __builtin_amdgcn_sched_barrier(0);
+
+      float sc[G][NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float kf[VEC];
-      Elem<KVT>::unpack(kr[i], kf);
-      const bool valid = cb + i * TPW + g < t1;
+      for (int i = 0; i < NL; ++i) {
+        const bool valid = cs + i * TPW + g <= last;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float d = group_sum<LPR>(q[h].dot(kr[i])) * a.qk_scale_log2;
+          sc[h][i] = valid ? d : -INFINITY;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb, a.k_sb, a.k_st, cn, last, nblk, kr);
+      __builtin_amdgcn_sched_barrier(0);
+
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float d = 0.0f;
+        float cm = sc[h][0];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) d = __builtin_fmaf(qf[h][v], kf[v], d);
-        d = group_sum<LPR>(d);
-        s[h][i] = valid ? d : -INFINITY;
+        for (int i = 1; i < NL; ++i) cm = fmaxf(cm, sc[h][i]);
+        cm = across_groups_max<LPR>(cm);
+        const float mn = fmaxf(m[h], cm);
+        const float alpha = fast_exp2(m[h] - mn);
+        l[h] *= alpha;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[h][v] *= alpha;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) sc[h][i] = fast_exp2(sc[h][i] - mn);
+        m[h] = mn;
       }
-      // masked rows may hold anything (NaN included): keep them out of p * V
-      if (!valid) vr[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        float vf[VEC];
+        Elem<KVT>::unpack(vr[i], vf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          l[h] += sc[h][i];
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[h][v] = __builtin_fmaf(sc[h][i], vf[v], acc[h][v]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(vb, a.v_sb, a.v_st, cn, last, nblk, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      cs = cn;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) blk[i] = nblk[i];
     }
 
+    // every lane ends with the totals of its row slice over all tokens of the segment
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float cm = s[h][0];
+      l[h] = across_groups_sum<LPR>(l[h]);
 #pragma unroll
-      for (int i = 1; i < NL; ++i) cm = fmaxf(cm, s[h][i]);
-      cm = across_groups_max<LPR>(cm);
-      const float mn = fmaxf(m[h], cm);
-      const float alpha = fast_exp2(m[h] - mn);
-      l[h] *= alpha;
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[h][v] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NL; ++i) s[h][i] = fast_exp2(s[h][i] - mn);
-      m[h] = mn;
+      for (int v = 0; v < VEC; ++v) acc[h][v] = across_groups_sum<LPR>(acc[h][v]);
     }
+  }
+
+  __device__ void write_out(int s, int kvh) const {
+    if (g != 0) return;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      float vf[VEC];
-      Elem<KVT>::unpack(vr[i], vf);
+    for (int h = 0; h < G; ++h) {
+      float o[VEC];
+      const float inv = a.v_scale / l[h];
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) o[v] = acc[h][v] * inv;
+      const int64_t off = (int64_t)s * a.o_ss + (int64_t)(kvh * G + h) * a.o_sh + r * VEC;
+      if (a.out_f32)
+        store_vec<f32_t, VEC>(a.out, off, o);
+      else
+        store_vec<QT, VEC>(a.out, off, o);
+    }
+  }
+
+  __device__ void write_partial(int64_t slot) const {
+    if (g == 0) {
+      float *pacc = slot_acc<G, D>(a, slot);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) store_shared(pacc + h * D + r * VEC + v, acc[h][v]);
+    }
+    if (lane == 0) {
+      float *pml = slot_ml<G>(a, slot);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        l[h] += s[h][i];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[h][v] = __builtin_fmaf(s[h][i], vf[v], acc[h][v]);
+        store_shared(pml + 2 * h, m[h]);
+        store_shared(pml + 2 * h + 1, l[h]);
       }
     }
   }
+};
 
-  // combine the TPW token groups of the wave, then the waves through LDS
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = across_groups_sum<LPR>(l[h]);
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[h][v] = across_groups_sum<LPR>(acc[h][v]);
-  }
-  if (lane < LPR) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) sm_acc[wave][h][r * VEC + v] = acc[h][v];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sm_m[wave][h] = m[h];
-      sm_l[wave][h] = l[h];
-    }
-  }
-  __syncthreads();
-
-  const bool single = ctx <= a.partition_size;
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D, d = i % D;
-    float M = sm_m[0][h];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float e = fast_exp2(sm_m[w][h] - M);
-      L = __builtin_fmaf(e, sm_l[w][h], L);
-      O = __builtin_fmaf(e, sm_acc[w][h][d], O);
-    }
-    const int head = kvh * G + h;
-    if (single) {
-      store_out<QT>(a, (int64_t)seq * a.o_ss + (int64_t)head * a.o_sh + d, O / L * a.v_scale);
-    } else {
-      const int64_t row = ((int64_t)seq * a.num_heads + head) * a.num_partitions + part;
-      a.ws_acc[row * D + d] = O;
-      if (d == 0) {
-        a.ws_ml[row * 2] = M;
-        a.ws_ml[row * 2 + 1] = L;
-      }
-    }
-  }
+template <typename KVT, typename QT, int D, int G, int BS, int NL>
+__global__ void __launch_bounds__(64 * kWavesPerWG) decode_valu(const DecodeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  // workgroups are dealt to the 8 XCDs round-robin; number them so that each
+  // XCD's workers hold one contiguous stretch of the work order
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  ValuSeg<KVT, QT, D, G, BS, NL> seg(a, lane);
+  run_worker<QT, G, D>(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
+
+// loads per chunk: fewer for larger groups, whose query, score and accumulator
+// registers grow with G
+template <int G> constexpr int nl_for() { return G == 1 ? 8 : (G == 2 ? 4 : (G == 4 ? 2 : 1)); }
 
 template <typename KVT, typename QT, int D, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
-  constexpr int NL = 8;
-  dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_partition_valu<KVT, QT, D, G, NL>), grid, dim3(kThreads), 0, stream, a);
+  constexpr int NL = nl_for<G>();
+  const dim3 grid(a.num_workers / kWavesPerWG), block(64 * kWavesPerWG);
+  if (a.block_size == 16)
+    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -244,13 +361,20 @@ hipError_t dispatch_dim(const DecodeArgs &a, hipStream_t stream) {
 
 }  // namespace
 
+int decode_chunk_tokens(int kv_kind, int head_dim, int group) {
+  const int vec = kv_kind == KV_F32 ? 4 : (kv_kind == KV_FP8 ? 16 : 8);
+  const int tpw = 64 / (head_dim / vec);
+  const int nl = group == 1 ? 8 : (group == 2 ? 4 : (group == 4 ? 2 : 1));
+  return tpw * nl;
+}
+
 bool decode_supported(int kv_kind, int q_kind, int head_dim, int group) {
   const bool pair = (kv_kind == q_kind && kv_kind != KV_FP8) ||
                     (kv_kind == KV_FP8 && (q_kind == KV_F16 || q_kind == KV_BF16));
   return pair && (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
 }
 
-hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   switch (a.kv_kind) {
     case KV_F32: return dispatch_dim<f32_t, f32_t>(a, stream);
     case KV_F16: return dispatch_dim<f16_t, f16_t>(a, stream);

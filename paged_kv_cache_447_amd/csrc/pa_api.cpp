@@ -1,5 +1,5 @@
 // Host side of the C ABI declared in include/pa.h: argument validation, the
-// partition-size choice, workspace carving and kernel dispatch.  Nothing here
+// work-split choice, workspace carving and kernel dispatch.  Nothing here
 // allocates device memory or waits for the device.
 #include "pa.h"
 
@@ -72,38 +72,55 @@ pa_status check_tensor(const pa_tensor &t, const char *name, int ndim, bool need
   return PA_OK;
 }
 
-int32_t choose_partition(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks, int32_t block_size) {
-  // Split long contexts until (sequence, kv head, partition) work items
-  // comfortably outnumber the 256 compute units, but never below 256 tokens.
-  const int64_t max_ctx = max_blocks * block_size;
-  const int64_t pairs = num_seqs * num_kv_heads > 0 ? num_seqs * num_kv_heads : 1;
-  int64_t p = 256;
-  while (p < 4096 && pairs * ((max_ctx + p - 1) / p) > 16384) p *= 2;
-  if (p < block_size) p = block_size;
-  return (int32_t)p;
+constexpr int kWavesPerWG = 4;
+constexpr int64_t kMaxWorkers = 1 << 20;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Workers per compute unit when the caller leaves the choice to the library:
+// one wavefront per SIMD.  Each keeps a chunk of K or V in flight; more
+// workers only add segment starts and partials to merge.
+constexpr int kDefaultWorkersPerCU = 4;
+
+int32_t device_default_workers() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  // a multiple of 8 workgroups, so that every XCD gets the same number
+  return (int32_t)round_up((int64_t)cus * kDefaultWorkersPerCU, 8 * kWavesPerWG);
+}
+
+int32_t effective_workers(int32_t requested) {
+  if (requested <= 0) return device_default_workers();
+  int64_t w = round_up(requested, kWavesPerWG);
+  return (int32_t)(w > kMaxWorkers ? kMaxWorkers : w);
+}
+
+struct WsLayout {
+  size_t counters, ml, acc, total;  // byte offsets and total size
+};
+
+WsLayout workspace_layout(int64_t S, int64_t H, int64_t Hkv, int64_t D, int64_t W) {
+  WsLayout l;
+  const int64_t G = H / Hkv;
+  l.counters = 0;
+  l.ml = (size_t)round_up(S * Hkv * 4, 256);
+  l.acc = l.ml + (size_t)round_up(2 * W * G * 2 * 4, 256);
+  l.total = l.acc + (size_t)round_up(2 * W * G * D * 4, 256);
+  return l;
 }
 
 }  // namespace
 
 extern "C" {
 
-int32_t pa_decode_partition_size(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq,
-                                 int32_t block_size) {
-  if (block_size <= 0 || max_blocks_per_seq < 0) return 0;
-  return choose_partition(num_seqs, num_kv_heads, max_blocks_per_seq, block_size);
-}
+int32_t pa_decode_num_workers(int32_t requested) { return effective_workers(requested); }
 
 size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads, int64_t head_dim,
-                                int64_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
-  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
-      block_size <= 0)
-    return 0;
-  const int64_t p =
-      partition_size > 0 ? partition_size : choose_partition(num_seqs, num_kv_heads, max_blocks_per_seq, block_size);
-  const int64_t np = (max_blocks_per_seq * block_size + p - 1) / p;
-  if (np <= 1) return 0;
-  const int64_t rows = num_seqs * num_heads * np;
-  return (size_t)(rows * 2 + rows * head_dim) * sizeof(float);
+                                int32_t num_workers) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_heads % num_kv_heads) return 0;
+  return workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, effective_workers(num_workers)).total;
 }
 
 pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
@@ -158,7 +175,7 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   if (kvk != pa::KV_FP8) ks = vs = 1.0f;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
-  if (o.flags != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
   const int64_t W = block_tables.shape[1];
   if (S > 65535 || num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 sequences or kv heads");
   if (W * block_size > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "table width too large");
@@ -166,13 +183,24 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   if (S == 0 || H == 0) return PA_OK;
   if (NB == 0 || W == 0) return fail(PA_ERR_SHAPE, "empty cache or block table");
 
-  int64_t part = o.partition_size ? o.partition_size : choose_partition(S, num_kv_heads, W, block_size);
-  if (part <= 0 || part % block_size) return fail(PA_ERR_ARG, "partition_size %lld must be a positive multiple of "
-                                                  "block_size", (long long)part);
+  const int G = (int)(H / num_kv_heads);
   const int64_t max_ctx = W * block_size;
-  if (part > max_ctx) part = ((max_ctx + block_size - 1) / block_size) * block_size;
-  const int64_t np = (max_ctx + part - 1) / part;
-  if (np > 65535 * 32) return fail(PA_ERR_ARG, "partition_size too small for this table width");
+  int64_t part = o.partition_size;
+  if (part == 0) part = pa::decode_chunk_tokens(kvk, (int)D, G);
+  if (part <= 0 || (o.partition_size && part % block_size))
+    return fail(PA_ERR_ARG, "partition_size %lld must be a positive multiple of block_size", (long long)part);
+  if ((max_ctx + part - 1) / part > ((int64_t)1 << 24))
+    return fail(PA_ERR_ARG, "partition_size %lld too small for a table of %lld tokens", (long long)part,
+                (long long)max_ctx);
+  if (o.num_workers < 0) return fail(PA_ERR_ARG, "num_workers must be >= 0");
+  if (S * num_kv_heads * ((max_ctx + part - 1) / part) > ((int64_t)1 << 40))
+    return fail(PA_ERR_UNSUPPORTED, "too many work units");
+  const int32_t nw = effective_workers(o.num_workers);
+  const WsLayout ws = workspace_layout(S, H, num_kv_heads, D, nw);
+  if (!o.workspace || o.workspace_bytes < ws.total)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
+                o.workspace ? o.workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
 
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
@@ -182,16 +210,10 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   a.v_cache = v_cache.data;
   a.block_tables = static_cast<const int32_t *>(block_tables.data);
   a.context_lens = static_cast<const int32_t *>(context_lens.data);
-  if (np > 1) {
-    const size_t need = pa_decode_workspace_size(S, H, num_kv_heads, D, W, block_size, (int32_t)part);
-    if (!o.workspace || o.workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                  o.workspace ? o.workspace_bytes : (size_t)0);
-    if (reinterpret_cast<uintptr_t>(o.workspace) % 16) return fail(PA_ERR_LAYOUT, "workspace not 16-byte aligned");
-    const int64_t rows = S * H * np;
-    a.ws_ml = static_cast<float *>(o.workspace);
-    a.ws_acc = a.ws_ml + rows * 2;
-  }
+  char *wsb = static_cast<char *>(o.workspace);
+  a.counters = reinterpret_cast<int32_t *>(wsb + ws.counters);
+  a.part_ml = reinterpret_cast<float *>(wsb + ws.ml);
+  a.part_acc = reinterpret_cast<float *>(wsb + ws.acc);
   a.q_ss = q.stride[0];
   a.q_sh = q.stride[1];
   a.o_ss = out.stride[0];
@@ -209,28 +231,18 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   a.head_dim = (int32_t)D;
   a.num_blocks = (int32_t)NB;
   a.block_size = block_size;
-  a.log2_block_size = block_size == 16 ? 4 : 5;
   a.max_blocks_per_seq = (int32_t)W;
   a.max_ctx = (int32_t)max_ctx;
-  a.partition_size = (int32_t)part;
-  a.num_partitions = (int32_t)np;
+  a.part_tokens = (int32_t)part;
+  a.num_workers = nw;
   a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)ks);
   a.v_scale = vs;
   a.kv_kind = kvk;
   a.q_kind = kv_kind(q.dtype);
   a.out_f32 = out.dtype == PA_F32 && q.dtype != PA_F32;
 
-  hipStream_t stream = static_cast<hipStream_t>(o.stream);
-  hipError_t e = pa::launch_decode_partitions(a, stream);
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "partition kernel launch: %s", hipGetErrorString(e));
-  if (o.mark_event) {
-    e = hipEventRecord(static_cast<hipEvent_t>(o.mark_event), stream);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  }
-  if (np > 1) {
-    e = pa::launch_decode_reduce(a, stream);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "reduce kernel launch: %s", hipGetErrorString(e));
-  }
+  hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(o.stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 
@@ -268,7 +280,7 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
-  if (o.flags != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
   if (N == 0 || Hkv == 0 || D == 0) return PA_OK;
 
   pa::CacheWriteArgs a;
@@ -321,6 +333,6 @@ const char *pa_status_string(pa_status s) {
 
 const char *pa_last_error(void) { return g_last_error; }
 
-const char *pa_version(void) { return "0.1.0"; }
+const char *pa_version(void) { return "0.2.0"; }
 
 }  // extern "C"

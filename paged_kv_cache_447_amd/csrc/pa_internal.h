@@ -9,6 +9,15 @@ namespace pa {
 enum KvKind : int { KV_F32 = 0, KV_F16 = 1, KV_BF16 = 2, KV_FP8 = 3 };
 
 // Everything a decode launch needs, already validated; strides in elements.
+//
+// Work decomposition (shared by every decode kernel): the context of each
+// (sequence, kv head) pair -- an "item" -- is cut into units of part_tokens
+// tokens.  Items are ordered sequence-major, then kv head, then unit, and the
+// num_workers wavefronts of the launch each take one contiguous, equally sized
+// range of that order.  A worker whose range covers a whole item writes the
+// item's output; a range that cuts an item leaves a partial result (running
+// max, running sum, unnormalised output) in one of its two workspace slots,
+// and the last worker to finish an item merges the partials by log-sum-exp.
 struct DecodeArgs {
   void *out;
   const void *q;
@@ -16,17 +25,19 @@ struct DecodeArgs {
   const void *v_cache;
   const int32_t *block_tables;
   const int32_t *context_lens;
-  float *ws_ml;   // [S, H, NP, 2] running max (log2 units) and sum per partition
-  float *ws_acc;  // [S, H, NP, D] unnormalised partition outputs
+  int32_t *counters;   // [S * Hkv] finished-partial counters; zero between calls
+  float *part_ml;      // [2 * num_workers, G, 2] partial (max in log2 units, sum)
+  float *part_acc;     // [2 * num_workers, G, D] partial unnormalised outputs
   int64_t q_ss, q_sh;           // q strides: sequence, head
   int64_t o_ss, o_sh;           // out strides
   int64_t k_sb, k_st, k_sh;     // k_cache strides: block, token, kv head
   int64_t v_sb, v_st, v_sh;     // v_cache strides
   int64_t bt_ss;                // block-table row stride
   int32_t num_seqs, num_heads, num_kv_heads, head_dim;
-  int32_t num_blocks, block_size, log2_block_size, max_blocks_per_seq;
+  int32_t num_blocks, block_size, max_blocks_per_seq;
   int32_t max_ctx;              // max_blocks_per_seq * block_size
-  int32_t partition_size, num_partitions;
+  int32_t part_tokens;          // tokens per work unit
+  int32_t num_workers;          // wavefronts in the launch
   float qk_scale_log2;          // scale * log2(e) (* k_scale for fp8)
   float v_scale;                // 1, or the fp8 value-cache scale
   int32_t kv_kind;              // KvKind
@@ -51,9 +62,12 @@ struct CacheWriteArgs {
   float k_scale, v_scale;          // fp8 caches only
 };
 
+// Tokens per chunk (the unit of one pipelined load batch) of the decode kernel
+// that serves this configuration; work units are multiples of it by default.
+int decode_chunk_tokens(int kv_kind, int head_dim, int group);
+
 // Launchers (defined in the .hip files).  They return the launch's hipError_t.
-hipError_t launch_decode_partitions(const DecodeArgs &a, hipStream_t stream);
-hipError_t launch_decode_reduce(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 
 // Which (kv dtype, q dtype, head_dim, group size) the decode kernels were built for.

@@ -1,0 +1,254 @@
+// Work distribution shared by the decode kernels: a persistent, balanced split
+// of every (sequence, kv head) context over the wavefronts of one launch, and
+// the in-kernel log-sum-exp merge of contexts that the split cuts.
+//
+// Items are (sequence, kv head) pairs, ordered sequence-major.  The context of
+// an item with L tokens is cut into ceil(L / P) units of P tokens (the last one
+// shorter).  With T units in all and W workers, worker w takes units
+// [w*T/W, (w+1)*T/W) in that order, so every worker streams the same amount
+// of cache (up to one unit) whatever the mix of context lengths.  A maximal run
+// of a worker's units inside one item is a segment.  A segment that is the
+// whole item is written straight to the output; otherwise the segment's
+// running max m, running sum l and unnormalised output acc go to a workspace
+// slot and the item's counter is incremented.  The worker that brings the
+// counter to the number of segments of the item merges them:
+//   M = max m_i,  out = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i,
+// which is the softmax over the whole context summed in another order, then
+// resets the counter to zero for the next call.
+//
+// Each worker has two slots: slot 2w for its first segment and 2w+1 for its
+// last.  Only a worker's first and last segments can be cut, so two suffice,
+// and the merging worker finds every slot from the same arithmetic.
+//
+// Publication without cache-wide fences.  The 8 XCDs of the chip each have
+// their own L2, and a device-scope fence writes back (release) or
+// invalidates (acquire) a whole L2 -- thousands of those per launch cost more
+// than the decode itself.  Partials are therefore written with device-scope
+// atomic stores, which write through to the coherent level, and read with
+// device-scope atomic loads, which read from it; the writer waits for its
+// stores to complete (s_waitcnt) before it increments the counter, and the
+// merger issues its loads only after the counter increment has returned.
+// No other data crosses between workers.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+__device__ __forceinline__ int clamp_ctx(int c, int max_ctx) { return c < 0 ? 0 : (c > max_ctx ? max_ctx : c); }
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// First unit of worker w's range, and the worker whose range holds unit x
+// (all ranges are non-empty because the launch never uses more workers than
+// units).
+__device__ __forceinline__ int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+__device__ __forceinline__ int64_t unit_owner(int64_t x, int64_t T, int64_t W) { return ((x + 1) * W - 1) / T; }
+
+// A window of 64 consecutive sequences: units per sequence and their prefix sums.
+struct SeqWindow {
+  int s0;        // first sequence of the window
+  int L;         // this lane's sequence: clamped context length (0 past the last sequence)
+  int n;         // this lane's sequence: number of units
+  int incl;      // inclusive prefix of n inside the window
+  int total;     // units of the whole window (uniform)
+};
+
+__device__ __forceinline__ SeqWindow load_window(const DecodeArgs &a, int s0, int lane) {
+  SeqWindow win;
+  win.s0 = s0;
+  const int s = s0 + lane;
+  win.L = s < a.num_seqs ? clamp_ctx(a.context_lens[s], a.max_ctx) : 0;
+  win.n = (win.L + a.part_tokens - 1) / a.part_tokens;
+  win.incl = wave_incl_scan(win.n, lane);
+  win.total = uniform(__shfl(win.incl, 63));
+  return win;
+}
+
+// Per-segment partial result layout in the workspace.
+template <int G, int D>
+__device__ __forceinline__ float *slot_acc(const DecodeArgs &a, int64_t slot) {
+  return a.part_acc + slot * (int64_t)(G * D);
+}
+template <int G>
+__device__ __forceinline__ float *slot_ml(const DecodeArgs &a, int64_t slot) {
+  return a.part_ml + slot * (int64_t)(G * 2);
+}
+
+// Partials cross between wavefronts of different XCDs: device-scope atomic
+// stores and loads reach the coherent level past every XCD's own L2.
+__device__ __forceinline__ float load_shared(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_shared(float *p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename QT>
+__device__ __forceinline__ void store_elem(const DecodeArgs &a, int64_t idx, float x) {
+  if (a.out_f32)
+    reinterpret_cast<float *>(a.out)[idx] = x;
+  else
+    Elem<QT>::store(a.out, idx, x);
+}
+
+// Merge the segments of item (s, kvh) whose units start at a0 (n units): the
+// caller is the last of its workers to finish.
+template <typename QT, int G, int D>
+__device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, int64_t T, int64_t W,
+                           int lane) {
+  const int64_t w0 = unit_owner(a0, T, W), w1 = unit_owner(a0 + n - 1, T, W);
+  const bool first_is_last = range_begin(w0, T, W) < a0;  // w0 began in an earlier item
+  const int cnt = (int)(w1 - w0 + 1);
+  for (int e = lane; e < G * D; e += 64) {
+    const int g = e / D, d = e % D;
+    float M = -INFINITY;
+    for (int i = 0; i < cnt; ++i) {
+      const int64_t wi = w0 + i;
+      const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
+      M = fmaxf(M, load_shared(slot_ml<G>(a, slot) + 2 * g));
+    }
+    float L = 0.0f, O = 0.0f;
+    for (int i = 0; i < cnt; ++i) {
+      const int64_t wi = w0 + i;
+      const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
+      const float *ml = slot_ml<G>(a, slot);
+      const float f = fast_exp2(load_shared(ml + 2 * g) - M);
+      L = __builtin_fmaf(f, load_shared(ml + 2 * g + 1), L);
+      O = __builtin_fmaf(f, load_shared(slot_acc<G, D>(a, slot) + g * D + d), O);
+    }
+    const int head = kvh * G + g;
+    store_elem<QT>(a, (int64_t)s * a.o_ss + (int64_t)head * a.o_sh + d, O / L * a.v_scale);
+  }
+}
+
+// Publish a segment's partial (already stored by the caller to `slot`) and,
+// if this worker is the item's last, merge.  Returns nothing; all lanes call.
+template <typename QT, int G, int D>
+__device__ __forceinline__ void finish_partial(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, int64_t T,
+                                               int64_t W, int lane) {
+  const int64_t w0 = unit_owner(a0, T, W), w1 = unit_owner(a0 + n - 1, T, W);
+  const int cnt = (int)(w1 - w0 + 1);
+  int32_t *ctr = a.counters + (int64_t)s * a.num_kv_heads + kvh;
+  // the partial's write-through stores are complete before the count goes up
+  // (the signal fences keep the compiler from moving memory operations across)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  int old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = uniform(__shfl(old, 0));
+  if (old == cnt - 1) {
+    // every other segment's count, hence its stores, came before ours
+    merge_item<QT, G, D>(a, s, kvh, a0, n, T, W, lane);
+    if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Zero the output rows of sequences with an empty context (sequence s is
+// handled by worker s mod W).
+template <typename QT>
+__device__ __forceinline__ void zero_empty_sequences(const DecodeArgs &a, const SeqWindow &win, int w, int W,
+                                                     int lane) {
+  const int s = win.s0 + lane;
+  const bool mine = s < a.num_seqs && win.n == 0 && (s % W) == w;
+  uint64_t mask = __ballot(mine);
+  while (mask) {
+    const int l = __builtin_ctzll(mask);
+    mask &= mask - 1;
+    const int sz = win.s0 + l;
+    for (int e = lane; e < a.num_heads * a.head_dim; e += 64)
+      store_elem<QT>(a, (int64_t)sz * a.o_ss + (int64_t)(e / a.head_dim) * a.o_sh + e % a.head_dim, 0.0f);
+  }
+}
+
+// Drive one worker through its range.  Seg must provide
+//   void run(int s, int kvh, int t_lo, int t_hi)      -- attend over tokens [t_lo, t_hi)
+//   void write_out(int s, int kvh)                    -- normalised output of a whole item
+//   void write_partial(int64_t slot)                  -- partial (m, l, acc) to a slot
+// All lanes of the wave call every function; all control flow is uniform.
+template <typename QT, int G, int D, class Seg>
+__device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+  // pass 1: total units T; zero empty sequences
+  int64_t T = 0;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+    const SeqWindow win = load_window(a, s0, lane);
+    zero_empty_sequences<QT>(a, win, w, W, lane);
+    T += (int64_t)win.total;
+  }
+  T *= a.num_kv_heads;
+  const int64_t Wn = T < (int64_t)W ? T : (int64_t)W;  // never more workers than units
+  if (w >= Wn) return;
+  const int64_t b = range_begin(w, T, Wn), e = range_begin(w + 1, T, Wn);
+
+  // pass 2: find the window and sequence holding unit b
+  int64_t base = 0;  // units (all kv heads) of the sequences before the window
+  SeqWindow win = load_window(a, 0, lane);
+  while (b >= base + (int64_t)win.total * a.num_kv_heads) {
+    if (win.s0 + 64 >= a.num_seqs) return;  // only if context_lens changed under the launch
+    base += (int64_t)win.total * a.num_kv_heads;
+    win = load_window(a, win.s0 + 64, lane);
+  }
+  int ls;  // lane (sequence) in the window
+  {
+    const int64_t lo = base + (int64_t)(win.incl - win.n) * a.num_kv_heads;
+    const int64_t hi = base + (int64_t)win.incl * a.num_kv_heads;
+    const uint64_t hit = __ballot(win.n > 0 && lo <= b && b < hi);
+    if (hit == 0) return;
+    ls = __builtin_ctzll(hit);
+  }
+  int n_s = uniform(__shfl(win.n, ls));
+  int64_t item0 = base + (int64_t)uniform(__shfl(win.incl - win.n, ls)) * a.num_kv_heads;  // first unit of (s, 0)
+  int kvh = (int)((b - item0) / n_s);
+  int u = (int)((b - item0) % n_s);
+
+  int64_t x = b;
+  bool first = true;
+  while (true) {
+    const int s = win.s0 + ls;
+    const int L = uniform(__shfl(win.L, ls));
+    const int64_t a0 = item0 + (int64_t)kvh * n_s;     // first unit of this item
+    const int64_t u_end = (e - a0) < n_s ? (e - a0) : n_s;  // units of this item in range
+    const int t_lo = u * a.part_tokens;
+    const int t_hi = (int)(u_end * a.part_tokens < L ? u_end * a.part_tokens : L);
+    seg.run(s, kvh, t_lo, t_hi);
+    if (u == 0 && u_end == n_s) {
+      seg.write_out(s, kvh);
+    } else {
+      const int64_t slot = first ? 2 * (int64_t)w : 2 * (int64_t)w + 1;
+      seg.write_partial(slot);
+      finish_partial<QT, G, D>(a, s, kvh, a0, n_s, T, Wn, lane);
+    }
+    x = a0 + u_end;
+    first = false;
+    if (x >= e) break;
+    // next item: next kv head, else the next sequence with a non-empty context
+    u = 0;
+    if (++kvh == a.num_kv_heads) {
+      kvh = 0;
+      item0 += (int64_t)n_s * a.num_kv_heads;
+      do {
+        if (++ls == 64) {
+          if (win.s0 + 64 >= a.num_seqs) return;  // only if context_lens changed under the launch
+          win = load_window(a, win.s0 + 64, lane);
+          ls = 0;
+        }
+        if (win.s0 + ls >= a.num_seqs) return;
+        n_s = uniform(__shfl(win.n, ls));
+      } while (n_s == 0);
+    }
+  }
+}
+
+}  // namespace pa

@@ -37,7 +37,8 @@ def gpu_cache_write(cfg, inp):
                    k_scale=inp["k_scale"], v_scale=inp["v_scale"])
 
 
-def gpu_decode(cfg, inp, out_dtype=None, partition_size=None, context_lens=None, stream=None, out=None):
+def gpu_decode(cfg, inp, out_dtype=None, partition_size=None, context_lens=None, stream=None, out=None,
+               num_workers=0, workspace=None):
     q = inp["q"]
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
@@ -45,7 +46,7 @@ def gpu_decode(cfg, inp, out_dtype=None, partition_size=None, context_lens=None,
     pa.decode(out, q, inp["k_cache"], inp["v_cache"], inp["block_tables"],
               inp["context_lens"] if context_lens is None else context_lens, cfg.block_size, cfg.softmax_scale,
               cfg.num_kv_heads, k_scale=inp["k_scale"], v_scale=inp["v_scale"], partition_size=part,
-              stream=stream)
+              num_workers=num_workers, workspace=workspace, stream=stream)
     return out
 
 

@@ -72,17 +72,26 @@ SMALL = {
 }
 
 
+# (partition_size, num_workers): the unit of work and how many wavefronts share
+# it decide where contexts are cut and merged.  One worker cuts nothing; a
+# handful of workers cut long contexts into a few big segments; many workers
+# (more than there are units, for the small cases) give one unit each.
+SPLITS = [(0, 0), (64, 0), (256, 0), (0, 4), (0, 36), (16, 100), (0, 65536)]
+
+
 @pytest.mark.parametrize("case", sorted(SMALL))
-@pytest.mark.parametrize("partition", [0, 64, 256])
-def test_small_cases_match_oracle(case, partition):
+@pytest.mark.parametrize("split", SPLITS, ids=[f"p{p}w{w}" for p, w in SPLITS])
+def test_small_cases_match_oracle(case, split):
     cfg = SMALL[case]
+    partition, workers = split
     part = partition if partition % cfg.block_size == 0 else 0
-    log(f"[{case} p={part}]")
+    log(f"[{case} p={part} w={workers}]")
     layout, inp = setup(cfg)
     host = host_inputs(inp)
     gpu_cache_write(cfg, inp)
-    out = gpu_decode(cfg, inp, partition_size=part)
-    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=part)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads, workers)
+    out = gpu_decode(cfg, inp, partition_size=part, num_workers=workers, workspace=ws)
+    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=part, num_workers=workers, workspace=ws)
     torch.cuda.synchronize()
     ref, kc, vc = oracle_step(cfg, host)
     assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8))
@@ -91,12 +100,16 @@ def test_small_cases_match_oracle(case, partition):
     log(f"    err={err:.3e} err32={err32:.3e}")
     assert err <= TOL_OUT[cfg.kv_dtype]
     assert err32 <= TOL_F32[cfg.kv_dtype]
+    # every call leaves the merge counters at zero for the next one
+    S, Hkv = cfg.num_seqs, cfg.num_kv_heads
+    assert int(ws[: 4 * S * Hkv].view(torch.int32).abs().sum()) == 0
 
 
 @pytest.mark.parametrize("name", ["llama7b", "gqa70b", "fp8_long"])
-def test_partition_sizes_agree(name):
-    """Split-context is a re-association of the same softmax: every partition size
-    gives the oracle's answer (fp32 output), and they agree with each other."""
+def test_split_choices_agree(name):
+    """Split-context is a re-association of the same softmax: every work unit and
+    worker count gives the oracle's answer (fp32 output), and they agree with
+    each other."""
     cfg = get_config(name)
     if name != "fp8_long":
         cfg = scaled(cfg, num_seqs=16)
@@ -105,12 +118,13 @@ def test_partition_sizes_agree(name):
     gpu_cache_write(cfg, inp)
     ref, _, _ = oracle_step(cfg, host)
     outs = {}
-    for p in (cfg.block_size, 128, 256, 512, 1024, cfg.max_blocks_per_seq * cfg.block_size):
-        outs[p] = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=p)
+    for p, w in ((0, 0), (cfg.block_size, 0), (256, 0), (1024, 0), (0, 1), (0, 52), (512, 1000),
+                 (cfg.max_blocks_per_seq * cfg.block_size, 0)):
+        outs[(p, w)] = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=p, num_workers=w)
     torch.cuda.synchronize()
-    for p, o in outs.items():
+    for (p, w), o in outs.items():
         e = max_abs_err(o, ref)
-        log(f"[{name}] partition {p}: err32={e:.3e}")
+        log(f"[{name}] partition {p} workers {w}: err32={e:.3e}")
         assert e <= TOL_F32[cfg.kv_dtype]
     first = next(iter(outs.values())).double()
     for o in outs.values():
@@ -163,16 +177,16 @@ def test_needle_block_resolution_is_bit_exact(kv_dtype, G, bs):
                     kc[phys, off, kvh] = (c * qv / qv.norm()).to(kc.dtype)
                     vrow = vc_h[phys, off, kvh].float()
                 expected[s, kvh * G:(kvh + 1) * G] = vrow
-        for part in (0, bs, 256):
+        for part, workers in ((0, 0), (bs, 0), (256, 0), (0, 1), (bs, 24)):
             out = torch.empty_like(q)
             pa.decode(out, q, kc, inp["v_cache"], inp["block_tables"], inp["context_lens"], bs, cfg.softmax_scale,
-                      Hkv, k_scale=k_scale, v_scale=inp["v_scale"], partition_size=part)
+                      Hkv, k_scale=k_scale, v_scale=inp["v_scale"], partition_size=part, num_workers=workers)
             torch.cuda.synchronize()
             want = expected.to(q.dtype)
             got = out.cpu()
             assert torch.equal(got.view(torch.int16) if got.dtype != torch.float32 else got.view(torch.int32),
                                want.view(torch.int16) if want.dtype != torch.float32 else want.view(torch.int32)), \
-                f"round {rnd} partition {part}"
+                f"round {rnd} partition {part} workers {workers}"
 
 
 def test_fp8_hardware_decode_matches_ocp_table():
