@@ -1,0 +1,368 @@
+// Paged decode for grouped-query heads on the matrix cores (MFMA).
+//
+// When G = num_heads / num_kv_heads query heads read one KV head, the scores
+// of a chunk of tokens and the output update are small dense contractions:
+//   S^T[t][h] = sum_d K[t][d] q[h][d]        (tokens x heads, over head_dim)
+//   O^T[d][h] += sum_t V[t][d] P[h][t]       (head_dim x heads, over tokens)
+// Both run as v_mfma_f32_16x16x32 (f16 or bf16 operands, fp32 accumulation),
+// with the G heads padded to the 16 columns of the instruction.  Everything
+// else -- the block-table walk, the per-wavefront balanced split and the
+// log-sum-exp merge -- is the same as on the vector-ALU path (pa_sched.h), and
+// follows the same pages: logical-to-physical translation of page
+// "vLLM框架中的KV cache优化与PagedAttention机制详解" (section 5.1), address rule of
+// page "Paged KVCache：大模型推理显存管理优化方案" (section 2.3), per-block scores
+// accumulated across blocks as page "vLLM推理引擎架构：PagedAttention机制与高吞吐推理"
+// (section 2.3) describes.
+//
+// Lane layouts (v_mfma_f32_16x16x32: lane l holds row l % 16 and the 8
+// consecutive k-indices 8 * (l / 16) .. +7 of A; column l % 16 and the same
+// k-indices of B; rows 4 * (l / 16) + i, i < 4, column l % 16 of C):
+//   QK  A = K tile (16 tokens x 32 dims): lane (t, j) loads 16 bytes of token
+//       t's row at dims 32 kb + 8 j -- for each k-step kb the 16 rows are read
+//       in 64-byte pieces, so every instruction is coalesced;
+//       B = q^T: lane (h, j) holds q[h][32 kb + 8 j ..]; zero for h >= G.
+//       The output gives lane (h, j) the scores of head h for tokens 4 j + i.
+//   PV  A = V^T tile (16 dims x 32 tokens), B = P^T (32 tokens x 16 heads).
+//       The chunk's 32 tokens enter the contraction in the order
+//       tau(j, i) = 4 j + i (i < 4), 16 + 4 j + i - 4 (i >= 4), which is
+//       exactly the 8 scores lane (h, j) already holds from the two QK tiles,
+//       so P needs no exchange between lanes.  V rows are staged through LDS
+//       (one 32-row buffer per wavefront) and read back transposed.
+//       The output gives lane (h, j) dims 16 n + 4 j + i of head h -- the same
+//       head as its softmax state, so the rescale by exp2(m_old - m_new) is
+//       per lane.
+//   P is split as P = hi + lo in the operand type (f16 or bf16) and both parts
+//   are multiplied in, so the weights carry ~16 more bits than one rounding
+//   would give (a single bf16 rounding of the weights alone would cost more
+//   than the fp32-output error budget).
+// K and V loads follow the rolling pipeline of the vector path: the next
+// chunk's K loads go out after this chunk's scores, its V loads as soon as
+// this chunk's V rows sit in LDS.  fp8 caches are decoded exactly into the
+// query's 16-bit type on the way (every e4m3fn value is representable).
+#include "pa_sched.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kWavesPerWG = 4;
+constexpr int CT = 32;  // tokens per chunk: two 16-token QK tiles, one 32-token PV step
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+__device__ __forceinline__ const_i32 *as_const(const int32_t *p) { return (const_i32 *)(uintptr_t)p; }
+
+// MFMA operand type (the query's 16-bit type)
+template <typename MT> struct Op;
+template <> struct Op<f16_t> {
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  __device__ static uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+  __device__ static float value(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
+};
+template <> struct Op<bf16_t> {
+  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  }
+  __device__ static uint32_t bits(float x) { return f32_to_bf16_rne(x); }
+  __device__ static float value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+};
+
+// Raw K/V storage of one operand slice (8 elements) and its conversion to MT.
+template <typename KVT, typename MT> struct Slice {
+  typedef u32x4 raw;  // 16-bit cache: the slice is already in the operand type
+  __device__ static raw load(const char *p) { return ld16(p); }
+  __device__ static u32x4 to_op(raw r) { return r; }
+};
+template <typename MT> struct Slice<fp8_t, MT> {
+  typedef u32x2 raw;  // 8 e4m3fn codes
+  __device__ static raw load(const char *p) { return *reinterpret_cast<const u32x2 *>(p); }
+  __device__ static u32x4 to_op(raw r) {
+    float f[8];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], true);
+      f[4 * w] = lo[0];
+      f[4 * w + 1] = lo[1];
+      f[4 * w + 2] = hi[0];
+      f[4 * w + 3] = hi[1];
+    }
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = Op<MT>::bits(f[2 * i]) | (Op<MT>::bits(f[2 * i + 1]) << 16);  // exact
+    return o;
+  }
+};
+
+template <typename OT>
+__device__ __forceinline__ void store4(void *base, int64_t off, const float *x) {
+  if constexpr (__is_same(OT, f32_t)) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, x[i]);
+    st16(reinterpret_cast<float *>(base) + off, w);
+  } else {
+    u32x2 w;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) w[i] = Op<OT>::bits(x[2 * i]) | (Op<OT>::bits(x[2 * i + 1]) << 16);
+    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(base) + off) = w;
+  }
+}
+
+template <typename KVT, typename MT, int D, int G, int BS>
+struct MfmaSeg {
+  static constexpr int KS = D / 32;        // k-steps of the QK contraction
+  static constexpr int NT = D / 16;        // 16-dim output tiles
+  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
+  static constexpr int EB = Elem<KVT>::kBytes;
+  static constexpr int LDS_STRIDE = D + 8;  // halves per staged V row (padding spreads the banks)
+  static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
+
+  const DecodeArgs &a;
+  const int lane, c16, j;  // lane, column / row within 16, quarter of the wave
+  uint16_t *vs;            // this wavefront's LDS V stage [CT][LDS_STRIDE]
+  float m, l;              // softmax state of head c16 (lane-local, combined over j at the end)
+  f32x4 acc[NT];           // O^T tiles: dims 16 n + 4 j + i of head c16
+
+  __device__ MfmaSeg(const DecodeArgs &args, int ln, uint16_t *stage)
+      : a(args), lane(ln), c16(ln & 15), j(ln >> 4), vs(stage) {}
+
+  // block ids of the chunk's two 16-token tiles (loads past `last` read its block)
+  __device__ __forceinline__ void fetch_blocks(const_i32 *bt, int cs, int last, int *blk) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      int b = bt[min(cs + 16 * tt, last) >> LOG2BS];
+      blk[tt] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+    }
+  }
+
+  __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
+                                        typename Slice<KVT, MT>::raw (*dst)[KS]) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = min(cs + 16 * tt + c16, last);
+      const char *row = base + ((int64_t)blk[tt] * sb + (int64_t)(t & (BS - 1)) * st) * EB;
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) dst[tt][kb] = Slice<KVT, MT>::load(row + (32 * kb + 8 * j) * EB);
+    }
+  }
+
+  // V rows of the chunk into LDS, as the operand type
+  __device__ __forceinline__ void stage_v(typename Slice<KVT, MT>::raw (*vr)[KS]) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb)
+        st16(vs + (16 * tt + c16) * LDS_STRIDE + 32 * kb + 8 * j, Slice<KVT, MT>::to_op(vr[tt][kb]));
+  }
+
+  // A operand of PV for output tile n: V[tau(j, i)][16 n + c16], i < 8
+  __device__ __forceinline__ u32x4 vt_operand(int n) const {
+    const uint16_t *col = vs + 16 * n + c16;
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r0 = 2 * i < 4 ? 4 * j + 2 * i : 16 + 4 * j + 2 * i - 4;
+      o[i] = (uint32_t)col[r0 * LDS_STRIDE] | ((uint32_t)col[(r0 + 1) * LDS_STRIDE] << 16);
+    }
+    return o;
+  }
+
+  __device__ void run(int s, int kvh, int t_lo, int t_hi) {
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (t_hi <= t_lo) return;
+    const int last = t_hi - 1;
+    const_i32 *bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
+    const char *kb_ = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * EB;
+    const char *vb_ = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * EB;
+
+    // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
+    u32x4 qop[KS];
+    {
+      const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)s * a.q_ss +
+                             (int64_t)(kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) {
+        qop[kb] = ld16(qrow + 32 * kb + 8 * j);
+        if (c16 >= G) qop[kb] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    int blk[2];
+    typename Slice<KVT, MT>::raw kr[2][KS], vr[2][KS];
+    fetch_blocks(bt, t_lo, last, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb_, a.k_sb, a.k_st, t_lo, last, blk, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(vb_, a.v_sb, a.v_st, t_lo, last, blk, vr);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int nch = (t_hi - t_lo + CT - 1) / CT;
+    int cs = t_lo;
+    for (int c = 0; c < nch; ++c) {
+      const int cn = c + 1 < nch ? cs + CT : cs;  // the last chunk again at the end: a cache hit, unused
+      int nblk[2];
+      fetch_blocks(bt, cn, last, nblk);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // scores of both 16-token tiles
+      f32x4 sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        sc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(Slice<KVT, MT>::to_op(kr[tt][kb]), qop[kb], sc[tt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kb_, a.k_sb, a.k_st, cn, last, nblk, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_v(vr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(vb_, a.v_sb, a.v_st, cn, last, nblk, vr);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // online softmax for head c16 over the lane's 8 tokens, then across the 4 quarters
+      float p[8];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
+        const float x = sc[i >> 2][i & 3] * a.qk_scale_log2;
+        p[i] = cs + tok <= last ? x : -INFINITY;
+        cm = fmaxf(cm, p[i]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 16));
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float mn = fmaxf(m, cm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      u32x4 phi, plo;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = fast_exp2(p[i] - mn), e1 = fast_exp2(p[i + 1] - mn);
+        l += e0 + e1;
+        const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
+        phi[i >> 1] = h0 | (h1 << 16);
+        plo[i >> 1] = Op<MT>::bits(e0 - Op<MT>::value(h0)) | (Op<MT>::bits(e1 - Op<MT>::value(h1)) << 16);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u32x4 vt = vt_operand(n);
+        acc[n] = Op<MT>::mma(vt, phi, acc[n]);
+        acc[n] = Op<MT>::mma(vt, plo, acc[n]);
+      }
+      cs = cn;
+      blk[0] = nblk[0];
+      blk[1] = nblk[1];
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+  }
+
+  __device__ void write_out(int s, int kvh) const {
+    if (c16 >= G) return;
+    const float inv = a.v_scale / l;
+    const int64_t row = (int64_t)s * a.o_ss + (int64_t)(kvh * G + c16) * a.o_sh;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = acc[n][i] * inv;
+      if (a.out_f32)
+        store4<f32_t>(a.out, row + 16 * n + 4 * j, o);
+      else
+        store4<MT>(a.out, row + 16 * n + 4 * j, o);
+    }
+  }
+
+  __device__ void write_partial(int64_t slot) const {
+    if (c16 >= G) return;
+    float *pacc = slot_acc<G, D>(a, slot) + c16 * D;
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_shared(pacc + 16 * n + 4 * j + i, acc[n][i]);
+    if (j == 0) {
+      float *pml = slot_ml<G>(a, slot);
+      store_shared(pml + 2 * c16, m);
+      store_shared(pml + 2 * c16 + 1, l);
+    }
+  }
+};
+
+template <typename KVT, typename MT, int D, int G, int BS>
+__global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
+  __shared__ uint16_t stage[kWavesPerWG][CT * (D + 8)];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  // workgroups are dealt to the 8 XCDs round-robin; number them so that each
+  // XCD's workers hold one contiguous stretch of the work order
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  MfmaSeg<KVT, MT, D, G, BS> seg(a, lane, stage[wave]);
+  run_worker<MT, G, D>(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
+}
+
+template <typename KVT, typename MT, int D, int G>
+hipError_t launch_g(const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid(a.num_workers / kWavesPerWG), block(64 * kWavesPerWG);
+  if (a.block_size == 16)
+    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename KVT, typename MT, int D>
+hipError_t launch_d(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.num_heads / a.num_kv_heads) {
+    case 4: return launch_g<KVT, MT, D, 4>(a, stream);
+    case 8: return launch_g<KVT, MT, D, 8>(a, stream);
+    case 16: return launch_g<KVT, MT, D, 16>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename KVT, typename MT>
+hipError_t launch_kv(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_d<KVT, MT, 64>(a, stream);
+    case 128: return launch_d<KVT, MT, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_uses_mfma(int kv_kind, int head_dim, int group) {
+  return kv_kind != KV_F32 && (head_dim == 64 || head_dim == 128) && (group == 4 || group == 8 || group == 16);
+}
+
+int decode_mfma_chunk_tokens() { return CT; }
+
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream) {
+  switch (a.kv_kind) {
+    case KV_F16: return launch_kv<f16_t, f16_t>(a, stream);
+    case KV_BF16: return launch_kv<bf16_t, bf16_t>(a, stream);
+    case KV_FP8:
+      if (a.q_kind == KV_F16) return launch_kv<fp8_t, f16_t>(a, stream);
+      if (a.q_kind == KV_BF16) return launch_kv<fp8_t, bf16_t>(a, stream);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

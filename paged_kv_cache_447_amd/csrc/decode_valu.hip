@@ -339,13 +339,18 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// groups of 4 and more go to the matrix cores, except for fp32 caches
 template <typename KVT, typename QT, int D>
 hipError_t dispatch_group(const DecodeArgs &a, hipStream_t stream) {
   switch (a.num_heads / a.num_kv_heads) {
     case 1: return launch_one<KVT, QT, D, 1>(a, stream);
     case 2: return launch_one<KVT, QT, D, 2>(a, stream);
-    case 4: return launch_one<KVT, QT, D, 4>(a, stream);
-    case 8: return launch_one<KVT, QT, D, 8>(a, stream);
+  }
+  if constexpr (__is_same(KVT, f32_t)) {
+    switch (a.num_heads / a.num_kv_heads) {
+      case 4: return launch_one<KVT, QT, D, 4>(a, stream);
+      case 8: return launch_one<KVT, QT, D, 8>(a, stream);
+    }
   }
   return hipErrorInvalidValue;
 }
@@ -362,6 +367,7 @@ hipError_t dispatch_dim(const DecodeArgs &a, hipStream_t stream) {
 }  // namespace
 
 int decode_chunk_tokens(int kv_kind, int head_dim, int group) {
+  if (decode_uses_mfma(kv_kind, head_dim, group)) return decode_mfma_chunk_tokens();
   const int vec = kv_kind == KV_F32 ? 4 : (kv_kind == KV_FP8 ? 16 : 8);
   const int tpw = 64 / (head_dim / vec);
   const int nl = group == 1 ? 8 : (group == 2 ? 4 : (group == 4 ? 2 : 1));
@@ -371,10 +377,14 @@ int decode_chunk_tokens(int kv_kind, int head_dim, int group) {
 bool decode_supported(int kv_kind, int q_kind, int head_dim, int group) {
   const bool pair = (kv_kind == q_kind && kv_kind != KV_FP8) ||
                     (kv_kind == KV_FP8 && (q_kind == KV_F16 || q_kind == KV_BF16));
-  return pair && (head_dim == 64 || head_dim == 128) && (group == 1 || group == 2 || group == 4 || group == 8);
+  if (!pair || (head_dim != 64 && head_dim != 128)) return false;
+  if (group == 1 || group == 2) return true;
+  if (kv_kind == KV_F32) return group == 4 || group == 8;
+  return decode_uses_mfma(kv_kind, head_dim, group);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+  if (decode_uses_mfma(a.kv_kind, a.head_dim, a.num_heads / a.num_kv_heads)) return launch_decode_mfma(a, stream);
   switch (a.kv_kind) {
     case KV_F32: return dispatch_dim<f32_t, f32_t>(a, stream);
     case KV_F16: return dispatch_dim<f16_t, f16_t>(a, stream);

@@ -169,7 +169,7 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   if (block_size != 16 && block_size != 32) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 16, 32)", block_size);
   if (!pa::decode_supported(kvk, kv_kind(q.dtype), (int)D, (int)(H / num_kv_heads)))
     return fail(PA_ERR_UNSUPPORTED, "no kernel for head_dim %lld, group size %lld with these dtypes "
-                "(built: head_dim 64/128, group 1/2/4/8)", (long long)D, (long long)(H / num_kv_heads));
+                "(built: head_dim 64/128, group 1/2/4/8, 16 for 16-bit or fp8 caches)", (long long)D, (long long)(H / num_kv_heads));
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (kvk != pa::KV_FP8) ks = vs = 1.0f;

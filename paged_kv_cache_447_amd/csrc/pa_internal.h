@@ -68,6 +68,10 @@ int decode_chunk_tokens(int kv_kind, int head_dim, int group);
 
 // Launchers (defined in the .hip files).  They return the launch's hipError_t.
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+// grouped-query heads on the matrix cores (decode_mfma.hip)
+bool decode_uses_mfma(int kv_kind, int head_dim, int group);
+int decode_mfma_chunk_tokens();
+hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 
 // Which (kv dtype, q dtype, head_dim, group size) the decode kernels were built for.

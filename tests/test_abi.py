@@ -154,7 +154,8 @@ def test_decode_layout_errors(lib):
 def test_decode_unsupported(lib):
     expect(lib, call_decode(lib, good_decode(D=96)), -5, "head_dim")
     expect(lib, call_decode(lib, good_decode(bs=8)), -5, "block_size")
-    expect(lib, call_decode(lib, good_decode(H=32, Hkv=2)), -5, "group")
+    expect(lib, call_decode(lib, good_decode(H=64, Hkv=2)), -5, "group")
+    expect(lib, call_decode(lib, good_decode(H=32, Hkv=2, kv=pa.PA_F32, q=pa.PA_F32)), -5, "group")
 
 
 def test_decode_argument_errors(lib):

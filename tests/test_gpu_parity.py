@@ -69,6 +69,12 @@ SMALL = {
                             ctx_hi=320, scale=None),
     "full_row": scaled(get_config("llama7b"), num_seqs=3, num_blocks=200, max_blocks_per_seq=20,
                        ctx_kind="fixed", ctx_fixed=(320, 319, 1)),
+    "gqa16_f16": scaled(get_config("gqa70b"), num_seqs=6, num_heads=32, num_kv_heads=2, num_blocks=600,
+                        max_blocks_per_seq=48, ctx_hi=1536),
+    "gqa8_bf16_d64": scaled(get_config("gqa70b"), num_seqs=8, num_heads=32, num_kv_heads=4, head_dim=64,
+                            kv_dtype="bf16", q_dtype="bf16", num_blocks=800, max_blocks_per_seq=40, ctx_hi=1280),
+    "gqa16_fp8_bf16q": scaled(get_config("fp8_long"), num_seqs=5, num_heads=32, num_kv_heads=2, q_dtype="bf16",
+                              num_blocks=1000, max_blocks_per_seq=160, ctx_lo=1, ctx_hi=2560, partition_size=0),
 }
 
 
@@ -132,7 +138,8 @@ def test_split_choices_agree(name):
 
 
 @pytest.mark.parametrize("kv_dtype,G,bs", [("f32", 1, 16), ("f16", 1, 16), ("bf16", 1, 32), ("f16", 8, 32),
-                                           ("bf16", 4, 16), ("fp8", 1, 16)])
+                                           ("bf16", 4, 16), ("fp8", 1, 16), ("f16", 2, 16), ("fp8", 16, 32),
+                                           ("f32", 8, 16)])
 def test_needle_block_resolution_is_bit_exact(kv_dtype, G, bs):
     """Plant one key per sequence that dominates every other score by > 200 nats: the
     output must then be that token's V row, bit for bit -- for every needle position,
