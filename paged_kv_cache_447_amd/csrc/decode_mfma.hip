@@ -78,6 +78,8 @@ template <> struct Op<bf16_t> {
 // Raw K/V storage of one operand slice (8 elements) and its conversion to MT.
 template <typename KVT, typename MT> struct Slice {
   typedef u32x4 raw;  // 16-bit cache: the slice is already in the operand type
+  // plain loads: each instruction reads half of each 128-byte line it touches,
+  // and the other half must still be in L2 for the next k-step's instruction
   __device__ static raw load(const char *p) { return ld16(p); }
   __device__ static u32x4 to_op(raw r) { return r; }
 };

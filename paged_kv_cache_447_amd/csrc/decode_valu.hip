@@ -178,7 +178,7 @@ struct ValuSeg {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int t = min(cs + i * TPW + g, last);
-      dst[i] = ld16(base + ((int64_t)blk[i] * sb + (int64_t)(t & (BS - 1)) * st) * EB);
+      dst[i] = ld16_stream(base + ((int64_t)blk[i] * sb + (int64_t)(t & (BS - 1)) * st) * EB);
     }
   }
 

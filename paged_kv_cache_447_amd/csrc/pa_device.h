@@ -10,6 +10,12 @@ namespace pa {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// K/V rows are read once per launch: nontemporal loads mark them as streaming
+// data, which on gfx950 keeps them from displacing reusable lines and lets
+// the memory system stream at a markedly higher rate than plain loads.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 // ---------------------------------------------------------------------------------

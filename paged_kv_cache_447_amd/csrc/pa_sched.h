@@ -104,32 +104,63 @@ __device__ __forceinline__ void store_elem(const DecodeArgs &a, int64_t idx, flo
 }
 
 // Merge the segments of item (s, kvh) whose units start at a0 (n units): the
-// caller is the last of its workers to finish.
+// caller is the last of its workers to finish.  One pass over the partials,
+// folding each into a running (M, L, O) per output element; the loads of
+// partial i+1 are in flight while partial i is folded in, so a merge costs
+// about one memory round trip per partial.  Lane l owns elements l + 64 k of
+// the [G][D] block, whose head (64 k) / D is the same for the whole wave.
 template <typename QT, int G, int D>
 __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, int64_t T, int64_t W,
                            int lane) {
+  constexpr int EPL = G * D / 64;
+  static_assert((G * D) % 64 == 0 && D % 64 == 0, "a wave covers whole heads");
   const int64_t w0 = unit_owner(a0, T, W), w1 = unit_owner(a0 + n - 1, T, W);
   const bool first_is_last = range_begin(w0, T, W) < a0;  // w0 began in an earlier item
   const int cnt = (int)(w1 - w0 + 1);
-  for (int e = lane; e < G * D; e += 64) {
-    const int g = e / D, d = e % D;
-    float M = -INFINITY;
-    for (int i = 0; i < cnt; ++i) {
-      const int64_t wi = w0 + i;
-      const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
-      M = fmaxf(M, load_shared(slot_ml<G>(a, slot) + 2 * g));
+  float M[EPL], L[EPL], O[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    M[k] = -INFINITY;
+    L[k] = 0.0f;
+    O[k] = 0.0f;
+  }
+  float cm = 0.0f, cl = 0.0f, cacc[EPL];
+  auto load = [&](int i, float &m_, float &l_, float *acc_) {
+    const int64_t wi = w0 + i;
+    const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
+    const float *ml = slot_ml<G>(a, slot);
+    const int g = lane < G ? lane : 0;
+    m_ = load_shared(ml + 2 * g);
+    l_ = load_shared(ml + 2 * g + 1);
+    const float *pacc = slot_acc<G, D>(a, slot);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) acc_[k] = load_shared(pacc + lane + 64 * k);
+  };
+  load(0, cm, cl, cacc);
+  for (int i = 0; i < cnt; ++i) {
+    float nm = 0.0f, nl = 0.0f, nacc[EPL];
+    if (i + 1 < cnt) load(i + 1, nm, nl, nacc);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      const int g = (64 * k) / D;
+      const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cm), g));
+      const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cl), g));
+      const float mn = fmaxf(M[k], mi);
+      const float f0 = fast_exp2(M[k] - mn), f1 = fast_exp2(mi - mn);
+      L[k] = L[k] * f0 + li * f1;
+      O[k] = O[k] * f0 + cacc[k] * f1;
+      M[k] = mn;
     }
-    float L = 0.0f, O = 0.0f;
-    for (int i = 0; i < cnt; ++i) {
-      const int64_t wi = w0 + i;
-      const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
-      const float *ml = slot_ml<G>(a, slot);
-      const float f = fast_exp2(load_shared(ml + 2 * g) - M);
-      L = __builtin_fmaf(f, load_shared(ml + 2 * g + 1), L);
-      O = __builtin_fmaf(f, load_shared(slot_acc<G, D>(a, slot) + g * D + d), O);
-    }
-    const int head = kvh * G + g;
-    store_elem<QT>(a, (int64_t)s * a.o_ss + (int64_t)head * a.o_sh + d, O / L * a.v_scale);
+    cm = nm;
+    cl = nl;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) cacc[k] = nacc[k];
+  }
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    const int e = lane + 64 * k;
+    const int head = kvh * G + e / D;
+    store_elem<QT>(a, (int64_t)s * a.o_ss + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * a.v_scale);
   }
 }
 
@@ -173,81 +204,126 @@ __device__ __forceinline__ void zero_empty_sequences(const DecodeArgs &a, const 
   }
 }
 
+// Where unit x sits: its sequence, the first unit of that sequence's kv head
+// 0, the sequence's units per kv head and its context length (all uniform).
+struct UnitPos {
+  int s;
+  int n;
+  int L;
+  int64_t item0;
+};
+
+// Find unit x (x < T) scanning the windows from the first one (`first` is the
+// already loaded window of sequences 0..63).  Returns false only if the
+// context lengths changed under the launch.
+__device__ __forceinline__ bool locate(const DecodeArgs &a, const SeqWindow &first, int64_t x, int lane,
+                                       UnitPos &p) {
+  int64_t base = 0;  // units (all kv heads) of the sequences before the window
+  SeqWindow win = first;
+  while (x >= base + (int64_t)win.total * a.num_kv_heads) {
+    if (win.s0 + 64 >= a.num_seqs) return false;
+    base += (int64_t)win.total * a.num_kv_heads;
+    win = load_window(a, win.s0 + 64, lane);
+  }
+  const int64_t lo = base + (int64_t)(win.incl - win.n) * a.num_kv_heads;
+  const int64_t hi = base + (int64_t)win.incl * a.num_kv_heads;
+  const uint64_t hit = __ballot(win.n > 0 && lo <= x && x < hi);
+  if (hit == 0) return false;
+  const int ls = __builtin_ctzll(hit);
+  p.s = win.s0 + ls;
+  p.n = uniform(__shfl(win.n, ls));
+  p.L = uniform(__shfl(win.L, ls));
+  p.item0 = base + (int64_t)uniform(__shfl(win.incl - win.n, ls)) * a.num_kv_heads;
+  return true;
+}
+
 // Drive one worker through its range.  Seg must provide
 //   void run(int s, int kvh, int t_lo, int t_hi)      -- attend over tokens [t_lo, t_hi)
 //   void write_out(int s, int kvh)                    -- normalised output of a whole item
 //   void write_partial(int64_t slot)                  -- partial (m, l, acc) to a slot
 // All lanes of the wave call every function; all control flow is uniform.
+//
+// Order of work: the range's last segment, then its first, then the whole
+// items between them.  A context cut between workers w and w+1 is then the
+// first or second thing both of them do, so its merge happens early in the
+// launch instead of in its tail.
 template <typename QT, int G, int D, class Seg>
 __device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
-  // pass 1: total units T; zero empty sequences
+  // total units T; zero the outputs of empty sequences
   int64_t T = 0;
-  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
-    const SeqWindow win = load_window(a, s0, lane);
+  const SeqWindow first = load_window(a, 0, lane);
+  for (SeqWindow win = first;;) {
     zero_empty_sequences<QT>(a, win, w, W, lane);
     T += (int64_t)win.total;
+    if (win.s0 + 64 >= a.num_seqs) break;
+    win = load_window(a, win.s0 + 64, lane);
   }
   T *= a.num_kv_heads;
   const int64_t Wn = T < (int64_t)W ? T : (int64_t)W;  // never more workers than units
   if (w >= Wn) return;
   const int64_t b = range_begin(w, T, Wn), e = range_begin(w + 1, T, Wn);
 
-  // pass 2: find the window and sequence holding unit b
-  int64_t base = 0;  // units (all kv heads) of the sequences before the window
-  SeqWindow win = load_window(a, 0, lane);
-  while (b >= base + (int64_t)win.total * a.num_kv_heads) {
-    if (win.s0 + 64 >= a.num_seqs) return;  // only if context_lens changed under the launch
-    base += (int64_t)win.total * a.num_kv_heads;
-    win = load_window(a, win.s0 + 64, lane);
+  UnitPos pb, pe;
+  if (!locate(a, first, b, lane, pb)) return;
+  const int kvh_b = (int)((b - pb.item0) / pb.n);
+  const int64_t a0_b = pb.item0 + (int64_t)kvh_b * pb.n, end_b = a0_b + pb.n;
+  int kvh_e = 0;
+  int64_t a0_e = 0;
+  const bool one_item = e <= end_b;
+  if (!one_item) {
+    if (!locate(a, first, e - 1, lane, pe)) return;
+    kvh_e = (int)((e - 1 - pe.item0) / pe.n);
+    a0_e = pe.item0 + (int64_t)kvh_e * pe.n;
   }
-  int ls;  // lane (sequence) in the window
-  {
-    const int64_t lo = base + (int64_t)(win.incl - win.n) * a.num_kv_heads;
-    const int64_t hi = base + (int64_t)win.incl * a.num_kv_heads;
-    const uint64_t hit = __ballot(win.n > 0 && lo <= b && b < hi);
-    if (hit == 0) return;
-    ls = __builtin_ctzll(hit);
-  }
-  int n_s = uniform(__shfl(win.n, ls));
-  int64_t item0 = base + (int64_t)uniform(__shfl(win.incl - win.n, ls)) * a.num_kv_heads;  // first unit of (s, 0)
-  int kvh = (int)((b - item0) / n_s);
-  int u = (int)((b - item0) % n_s);
 
-  int64_t x = b;
-  bool first = true;
+  // stage 0: the last segment (units [a0_e, e)); stage 1: the first (from b);
+  // stage 2: whole items in [end_b, a0_e).  One call site for the segment work.
+  int stage = one_item ? 1 : 0;
+  UnitPos p = one_item ? pb : pe;
+  int kvh = one_item ? kvh_b : kvh_e;
+  int u_lo = one_item ? (int)(b - a0_b) : 0;
+  int u_hi = one_item ? (int)(e - a0_b) : (int)(e - a0_e);
+  int64_t x = end_b;  // next unit of stage 2
   while (true) {
-    const int s = win.s0 + ls;
-    const int L = uniform(__shfl(win.L, ls));
-    const int64_t a0 = item0 + (int64_t)kvh * n_s;     // first unit of this item
-    const int64_t u_end = (e - a0) < n_s ? (e - a0) : n_s;  // units of this item in range
-    const int t_lo = u * a.part_tokens;
-    const int t_hi = (int)(u_end * a.part_tokens < L ? u_end * a.part_tokens : L);
-    seg.run(s, kvh, t_lo, t_hi);
-    if (u == 0 && u_end == n_s) {
-      seg.write_out(s, kvh);
+    const int64_t a0 = p.item0 + (int64_t)kvh * p.n;
+    const int t_lo = u_lo * a.part_tokens;
+    const int t_hi = (int)((int64_t)u_hi * a.part_tokens < p.L ? (int64_t)u_hi * a.part_tokens : p.L);
+    seg.run(p.s, kvh, t_lo, t_hi);
+    if (u_lo == 0 && u_hi == p.n) {
+      seg.write_out(p.s, kvh);
     } else {
-      const int64_t slot = first ? 2 * (int64_t)w : 2 * (int64_t)w + 1;
-      seg.write_partial(slot);
-      finish_partial<QT, G, D>(a, s, kvh, a0, n_s, T, Wn, lane);
+      seg.write_partial(stage == 1 ? 2 * (int64_t)w : 2 * (int64_t)w + 1);
+      finish_partial<QT, G, D>(a, p.s, kvh, a0, p.n, T, Wn, lane);
     }
-    x = a0 + u_end;
-    first = false;
-    if (x >= e) break;
-    // next item: next kv head, else the next sequence with a non-empty context
-    u = 0;
+    if (one_item) return;
+    if (stage == 0) {
+      stage = 1;
+      p = pb;
+      kvh = kvh_b;
+      u_lo = (int)(b - a0_b);
+      u_hi = pb.n;
+      continue;
+    }
+    if (stage == 1) {
+      stage = 2;
+      p = pb;
+      kvh = kvh_b;
+    } else {
+      x += p.n;
+    }
+    if (x >= a0_e) return;
+    // next item after (p, kvh): the next kv head, else the next sequence with a non-empty context
     if (++kvh == a.num_kv_heads) {
       kvh = 0;
-      item0 += (int64_t)n_s * a.num_kv_heads;
+      p.item0 += (int64_t)p.n * a.num_kv_heads;
       do {
-        if (++ls == 64) {
-          if (win.s0 + 64 >= a.num_seqs) return;  // only if context_lens changed under the launch
-          win = load_window(a, win.s0 + 64, lane);
-          ls = 0;
-        }
-        if (win.s0 + ls >= a.num_seqs) return;
-        n_s = uniform(__shfl(win.n, ls));
-      } while (n_s == 0);
+        if (++p.s >= a.num_seqs) return;  // only if context_lens changed under the launch
+        p.L = clamp_ctx(uniform(a.context_lens[p.s]), a.max_ctx);
+        p.n = (p.L + a.part_tokens - 1) / a.part_tokens;
+      } while (p.n == 0);
     }
+    u_lo = 0;
+    u_hi = p.n;
   }
 }
 
