@@ -178,43 +178,74 @@ struct MfmaSeg {
     return o;
   }
 
-  __device__ void run(int s, int kvh, int t_lo, int t_hi) {
+  // where a segment's rows live
+  struct Ptrs {
+    const_i32 *bt;
+    const char *kb, *vb;
+    int last;
+  };
+  __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
+    Ptrs p;
+    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
+    p.last = g.t_hi - 1;
+    return p;
+  }
+  // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
+  __device__ __forceinline__ void load_q(const SegInfo &g, u32x4 *dst) const {
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)g.s * a.q_ss +
+                           (int64_t)(g.kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+      dst[kb] = ld16(qrow + 32 * kb + 8 * j);
+      if (c16 >= G) dst[kb] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // pipeline state carried from one segment into the next
+  u32x4 qop[KS];
+  int blk[2];
+  typename Slice<KVT, MT>::raw kr[2][KS], vr[2][KS];
+
+  __device__ void begin(const SegInfo &g) {
+    const Ptrs p = ptrs(g);
+    load_q(g, qop);
+    fetch_blocks(p.bt, g.t_lo, p.last, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ void run(const SegInfo &g, const SegInfo &nx, bool has) {
     m = -INFINITY;
     l = 0.0f;
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (t_hi <= t_lo) return;
-    const int last = t_hi - 1;
-    const_i32 *bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
-    const char *kb_ = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * EB;
-    const char *vb_ = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * EB;
-
-    // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
-    u32x4 qop[KS];
-    {
-      const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)s * a.q_ss +
-                             (int64_t)(kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
-#pragma unroll
-      for (int kb = 0; kb < KS; ++kb) {
-        qop[kb] = ld16(qrow + 32 * kb + 8 * j);
-        if (c16 >= G) qop[kb] = u32x4{0u, 0u, 0u, 0u};
-      }
+    if (g.t_hi <= g.t_lo) {  // only if context_lens changed under the launch
+      if (has) begin(nx);
+      return;
     }
-    int blk[2];
-    typename Slice<KVT, MT>::raw kr[2][KS], vr[2][KS];
-    fetch_blocks(bt, t_lo, last, blk);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kb_, a.k_sb, a.k_st, t_lo, last, blk, kr);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(vb_, a.v_sb, a.v_st, t_lo, last, blk, vr);
-    __builtin_amdgcn_sched_barrier(0);
+    const Ptrs p = ptrs(g);
+    // the chunk after this segment's last one: the next segment's first (or,
+    // for the range's last segment, this last chunk again -- a cache hit, unused)
+    const Ptrs pn = has ? ptrs(nx) : p;
+    u32x4 qn[KS];
+    load_q(has ? nx : g, qn);
 
-    const int nch = (t_hi - t_lo + CT - 1) / CT;
-    int cs = t_lo;
+    const int nch = (g.t_hi - g.t_lo + CT - 1) / CT;
+    int cs = g.t_lo;
     for (int c = 0; c < nch; ++c) {
-      const int cn = c + 1 < nch ? cs + CT : cs;  // the last chunk again at the end: a cache hit, unused
+      const bool lastc = c + 1 == nch;
+      const int cn = lastc ? (has ? nx.t_lo : cs) : cs + CT;
+      const_i32 *btn = lastc ? pn.bt : p.bt;
+      const char *kbn = lastc ? pn.kb : p.kb;
+      const char *vbn = lastc ? pn.vb : p.vb;
+      const int lastn = lastc ? pn.last : p.last;
       int nblk[2];
-      fetch_blocks(bt, cn, last, nblk);
+      fetch_blocks(btn, cn, lastn, nblk);
       __builtin_amdgcn_sched_barrier(0);
 
       // scores of both 16-token tiles
@@ -226,22 +257,22 @@ struct MfmaSeg {
         for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(Slice<KVT, MT>::to_op(kr[tt][kb]), qop[kb], sc[tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(kb_, a.k_sb, a.k_st, cn, last, nblk, kr);
+      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
       __builtin_amdgcn_sched_barrier(0);
       stage_v(vr);
       __builtin_amdgcn_sched_barrier(0);
-      issue(vb_, a.v_sb, a.v_st, cn, last, nblk, vr);
+      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
 
       // online softmax for head c16 over the lane's 8 tokens, then across the 4 quarters
-      float p[8];
+      float p8[8];
       float cm = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
         const float x = sc[i >> 2][i & 3] * a.qk_scale_log2;
-        p[i] = cs + tok <= last ? x : -INFINITY;
-        cm = fmaxf(cm, p[i]);
+        p8[i] = cs + tok <= p.last ? x : -INFINITY;
+        cm = fmaxf(cm, p8[i]);
       }
       cm = fmaxf(cm, __shfl_xor(cm, 16));
       cm = fmaxf(cm, __shfl_xor(cm, 32));
@@ -254,7 +285,7 @@ struct MfmaSeg {
       u32x4 phi, plo;
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const float e0 = fast_exp2(p[i] - mn), e1 = fast_exp2(p[i + 1] - mn);
+        const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
         l += e0 + e1;
         const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
         phi[i >> 1] = h0 | (h1 << 16);
@@ -270,6 +301,8 @@ struct MfmaSeg {
       blk[0] = nblk[0];
       blk[1] = nblk[1];
     }
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) qop[kb] = qn[kb];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
   }

@@ -153,10 +153,10 @@ struct ValuSeg {
   static_assert(BS % TPW == 0, "a wave-wide load must stay inside one block");
 
   const DecodeArgs &a;
-  const int lane, r, g;  // lane, 16-byte slice of the row, token of a wave-wide load
+  const int lane, r, tg;  // lane, 16-byte slice of the row, token of a wave-wide load
   float m[G], l[G], acc[G][VEC];
 
-  __device__ ValuSeg(const DecodeArgs &args, int ln) : a(args), lane(ln), r(ln % LPR), g(ln / LPR) {}
+  __device__ ValuSeg(const DecodeArgs &args, int ln) : a(args), lane(ln), r(ln % LPR), tg(ln / LPR) {}
 
   // Block ids of the chunk starting at cs: the chunk spans NBC blocks (one
   // when it is shorter than a block), and wave-wide load i reads block
@@ -177,12 +177,49 @@ struct ValuSeg {
                                         u32x4 *dst) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      const int t = min(cs + i * TPW + g, last);
+      const int t = min(cs + i * TPW + tg, last);
       dst[i] = ld16_stream(base + ((int64_t)blk[i] * sb + (int64_t)(t & (BS - 1)) * st) * EB);
     }
   }
 
-  __device__ void run(int s, int kvh, int t_lo, int t_hi) {
+  // where a segment's rows live
+  struct Ptrs {
+    const_i32 *bt;
+    const char *kb, *vb;
+    int last;
+  };
+  __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
+    Ptrs p;
+    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + ((int64_t)g.kvh * a.k_sh + r * VEC) * EB;
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + ((int64_t)g.kvh * a.v_sh + r * VEC) * EB;
+    p.last = g.t_hi - 1;
+    return p;
+  }
+  __device__ __forceinline__ void load_q(const SegInfo &g, QSlice<KVT, QT> *dst) const {
+#pragma unroll
+    for (int h = 0; h < G; ++h) dst[h].load(a.q, (int64_t)g.s * a.q_ss + (int64_t)(g.kvh * G + h) * a.q_sh + r * VEC);
+  }
+
+  // pipeline state carried from one segment into the next
+  QSlice<KVT, QT> q[G];
+  int blk[NL];
+  u32x4 kr[NL], vr[NL];
+
+  // q, block ids and the K / V loads of g's first chunk; K before V, so that
+  // the first wait of the chunk loop is for K alone
+  __device__ void begin(const SegInfo &g) {
+    const Ptrs p = ptrs(g);
+    load_q(g, q);
+    fetch_blocks(p.bt, g.t_lo, p.last, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ void run(const SegInfo &g, const SegInfo &nx, bool has) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       m[h] = -INFINITY;
@@ -190,32 +227,28 @@ struct ValuSeg {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[h][v] = 0.0f;
     }
-    if (t_hi <= t_lo) return;
-    const int last = t_hi - 1;
-    const_i32 *bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
-    const char *kb = reinterpret_cast<const char *>(a.k_cache) + ((int64_t)kvh * a.k_sh + r * VEC) * EB;
-    const char *vb = reinterpret_cast<const char *>(a.v_cache) + ((int64_t)kvh * a.v_sh + r * VEC) * EB;
+    if (g.t_hi <= g.t_lo) {  // only if context_lens changed under the launch
+      if (has) begin(nx);
+      return;
+    }
+    const Ptrs p = ptrs(g);
+    // the chunk after this segment's last one: the next segment's first (or,
+    // for the range's last segment, this last chunk again -- a cache hit, unused)
+    const Ptrs pn = has ? ptrs(nx) : p;
+    QSlice<KVT, QT> qn[G];
+    load_q(has ? nx : g, qn);
 
-    QSlice<KVT, QT> q[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) q[h].load(a.q, (int64_t)s * a.q_ss + (int64_t)(kvh * G + h) * a.q_sh + r * VEC);
-    int blk[NL];
-    u32x4 kr[NL], vr[NL];
-    fetch_blocks(bt, t_lo, last, blk);
-    // q first, then K, then V: the loop's first wait is then for K alone
-    __builtin_amdgcn_sched_barrier(0);
-    issue(kb, a.k_sb, a.k_st, t_lo, last, blk, kr);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(vb, a.v_sb, a.v_st, t_lo, last, blk, vr);
-    __builtin_amdgcn_sched_barrier(0);
-
-    const int nch = (t_hi - t_lo + CH - 1) / CH;
-    int cs = t_lo;
+    const int nch = (g.t_hi - g.t_lo + CH - 1) / CH;
+    int cs = g.t_lo;
     for (int c = 0; c < nch; ++c) {
-      // the next chunk (the last one again at the end: a cache hit, never used)
-      const int cn = c + 1 < nch ? cs + CH : cs;
+      const bool lastc = c + 1 == nch;
+      const int cn = lastc ? (has ? nx.t_lo : cs) : cs + CH;
+      const_i32 *btn = lastc ? pn.bt : p.bt;
+      const char *kbn = lastc ? pn.kb : p.kb;
+      const char *vbn = lastc ? pn.vb : p.vb;
+      const int lastn = lastc ? pn.last : p.last;
       int nblk[NL];
-      fetch_blocks(bt, cn, last, nblk);
+      fetch_blocks(btn, cn, lastn, nblk);
       // the scheduler would otherwise sink table reads and loads down to their
       // uses and drain the pipeline: keep the program order at these points
       __builtin_amdgcn_sched_barrier(0);
@@ -223,7 +256,7 @@ struct ValuSeg {
       float sc[G][NL];
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const bool valid = cs + i * TPW + g <= last;
+        const bool valid = cs + i * TPW + tg <= p.last;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           const float d = group_sum<LPR>(q[h].dot(kr[i])) * a.qk_scale_log2;
@@ -231,7 +264,7 @@ struct ValuSeg {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(kb, a.k_sb, a.k_st, cn, last, nblk, kr);
+      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
       __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -261,12 +294,14 @@ struct ValuSeg {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(vb, a.v_sb, a.v_st, cn, last, nblk, vr);
+      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
       cs = cn;
 #pragma unroll
       for (int i = 0; i < NL; ++i) blk[i] = nblk[i];
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) q[h] = qn[h];
 
     // every lane ends with the totals of its row slice over all tokens of the segment
 #pragma unroll
@@ -278,7 +313,7 @@ struct ValuSeg {
   }
 
   __device__ void write_out(int s, int kvh) const {
-    if (g != 0) return;
+    if (tg != 0) return;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float o[VEC];
@@ -294,7 +329,7 @@ struct ValuSeg {
   }
 
   __device__ void write_partial(int64_t slot) const {
-    if (g == 0) {
+    if (tg == 0) {
       float *pacc = slot_acc<G, D>(a, slot);
 #pragma unroll
       for (int h = 0; h < G; ++h)

@@ -237,16 +237,105 @@ __device__ __forceinline__ bool locate(const DecodeArgs &a, const SeqWindow &fir
   return true;
 }
 
+// One segment of a worker's range: units [u_lo, u_hi) of item (s, kvh), as
+// tokens [t_lo, t_hi), plus what finishing it needs.
+struct SegInfo {
+  int s, kvh;
+  int t_lo, t_hi;
+  int u_lo, u_hi, n;  // units of the segment; units per kv head of the sequence
+  int64_t a0;         // first unit of the item
+  bool first;         // the first segment of the range (slot 2w) rather than a later one (2w+1)
+};
+
+// Yields a worker's segments in the order: the range's last segment, its
+// first, then the whole items between them.  A context cut between workers w
+// and w+1 is then the first or second thing both of them do, so its merge
+// happens early in the launch instead of in its tail.
+struct Walker {
+  const DecodeArgs &a;
+  int64_t b, e, a0_b, end_b, a0_e;
+  UnitPos pb, pe, p;
+  int kvh_b, kvh_e, kvh;
+  int stage;  // 0: last segment next, 1: first segment next, 2: whole items, 3: done
+  int64_t x;  // next unit of stage 2
+
+  __device__ Walker(const DecodeArgs &args) : a(args) {}
+
+  // false if there is nothing to do (or context_lens changed under the launch)
+  __device__ bool init(const SeqWindow &first, int64_t b_, int64_t e_, int lane) {
+    b = b_;
+    e = e_;
+    if (!locate(a, first, b, lane, pb)) return false;
+    kvh_b = (int)((b - pb.item0) / pb.n);
+    a0_b = pb.item0 + (int64_t)kvh_b * pb.n;
+    end_b = a0_b + pb.n;
+    stage = 1;
+    if (e > end_b) {
+      if (!locate(a, first, e - 1, lane, pe)) return false;
+      kvh_e = (int)((e - 1 - pe.item0) / pe.n);
+      a0_e = pe.item0 + (int64_t)kvh_e * pe.n;
+      stage = 0;
+    }
+    return true;
+  }
+
+  __device__ void fill(SegInfo &g, const UnitPos &q, int kv, int u_lo, int u_hi, bool is_first) const {
+    g.s = q.s;
+    g.kvh = kv;
+    g.u_lo = u_lo;
+    g.u_hi = u_hi;
+    g.n = q.n;
+    g.a0 = q.item0 + (int64_t)kv * q.n;
+    g.t_lo = u_lo * a.part_tokens;
+    g.t_hi = (int)((int64_t)u_hi * a.part_tokens < q.L ? (int64_t)u_hi * a.part_tokens : q.L);
+    g.first = is_first;
+  }
+
+  __device__ bool next(SegInfo &g) {
+    if (stage == 0) {
+      fill(g, pe, kvh_e, 0, (int)(e - a0_e), false);
+      stage = 1;
+      return true;
+    }
+    if (stage == 1) {
+      fill(g, pb, kvh_b, (int)(b - a0_b), (int)((e < end_b ? e : end_b) - a0_b), true);
+      stage = e > end_b ? 2 : 3;
+      p = pb;
+      kvh = kvh_b;
+      x = end_b;
+      return true;
+    }
+    if (stage == 3 || x >= a0_e) {
+      stage = 3;
+      return false;
+    }
+    // the item after (p, kvh): the next kv head, else the next sequence with a non-empty context
+    if (++kvh == a.num_kv_heads) {
+      kvh = 0;
+      p.item0 += (int64_t)p.n * a.num_kv_heads;
+      do {
+        if (++p.s >= a.num_seqs) {  // only if context_lens changed under the launch
+          stage = 3;
+          return false;
+        }
+        p.L = clamp_ctx(uniform(a.context_lens[p.s]), a.max_ctx);
+        p.n = (p.L + a.part_tokens - 1) / a.part_tokens;
+      } while (p.n == 0);
+    }
+    fill(g, p, kvh, 0, p.n, false);
+    x += p.n;
+    return true;
+  }
+};
+
 // Drive one worker through its range.  Seg must provide
-//   void run(int s, int kvh, int t_lo, int t_hi)      -- attend over tokens [t_lo, t_hi)
-//   void write_out(int s, int kvh)                    -- normalised output of a whole item
-//   void write_partial(int64_t slot)                  -- partial (m, l, acc) to a slot
+//   void begin(const SegInfo &g)                            -- issue the loads of g's first chunk
+//   void run(const SegInfo &g, const SegInfo &nx, bool has) -- attend over g's tokens (its first chunk
+//       already in flight); while on g's last chunk, issue nx's first chunk if `has`
+//   void write_out(int s, int kvh)                          -- normalised output of a whole item
+//   void write_partial(int64_t slot)                        -- partial (m, l, acc) to a slot
 // All lanes of the wave call every function; all control flow is uniform.
-//
-// Order of work: the range's last segment, then its first, then the whole
-// items between them.  A context cut between workers w and w+1 is then the
-// first or second thing both of them do, so its merge happens early in the
-// launch instead of in its tail.
+// The load pipeline thus runs on from one segment into the next.
 template <typename QT, int G, int D, class Seg>
 __device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
   // total units T; zero the outputs of empty sequences
@@ -261,69 +350,24 @@ __device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg
   T *= a.num_kv_heads;
   const int64_t Wn = T < (int64_t)W ? T : (int64_t)W;  // never more workers than units
   if (w >= Wn) return;
-  const int64_t b = range_begin(w, T, Wn), e = range_begin(w + 1, T, Wn);
 
-  UnitPos pb, pe;
-  if (!locate(a, first, b, lane, pb)) return;
-  const int kvh_b = (int)((b - pb.item0) / pb.n);
-  const int64_t a0_b = pb.item0 + (int64_t)kvh_b * pb.n, end_b = a0_b + pb.n;
-  int kvh_e = 0;
-  int64_t a0_e = 0;
-  const bool one_item = e <= end_b;
-  if (!one_item) {
-    if (!locate(a, first, e - 1, lane, pe)) return;
-    kvh_e = (int)((e - 1 - pe.item0) / pe.n);
-    a0_e = pe.item0 + (int64_t)kvh_e * pe.n;
-  }
-
-  // stage 0: the last segment (units [a0_e, e)); stage 1: the first (from b);
-  // stage 2: whole items in [end_b, a0_e).  One call site for the segment work.
-  int stage = one_item ? 1 : 0;
-  UnitPos p = one_item ? pb : pe;
-  int kvh = one_item ? kvh_b : kvh_e;
-  int u_lo = one_item ? (int)(b - a0_b) : 0;
-  int u_hi = one_item ? (int)(e - a0_b) : (int)(e - a0_e);
-  int64_t x = end_b;  // next unit of stage 2
+  Walker walk(a);
+  if (!walk.init(first, range_begin(w, T, Wn), range_begin(w + 1, T, Wn), lane)) return;
+  SegInfo cur, nx;
+  if (!walk.next(cur)) return;
+  bool has = walk.next(nx);
+  seg.begin(cur);
   while (true) {
-    const int64_t a0 = p.item0 + (int64_t)kvh * p.n;
-    const int t_lo = u_lo * a.part_tokens;
-    const int t_hi = (int)((int64_t)u_hi * a.part_tokens < p.L ? (int64_t)u_hi * a.part_tokens : p.L);
-    seg.run(p.s, kvh, t_lo, t_hi);
-    if (u_lo == 0 && u_hi == p.n) {
-      seg.write_out(p.s, kvh);
+    seg.run(cur, nx, has);
+    if (cur.u_lo == 0 && cur.u_hi == cur.n) {
+      seg.write_out(cur.s, cur.kvh);
     } else {
-      seg.write_partial(stage == 1 ? 2 * (int64_t)w : 2 * (int64_t)w + 1);
-      finish_partial<QT, G, D>(a, p.s, kvh, a0, p.n, T, Wn, lane);
+      seg.write_partial(cur.first ? 2 * (int64_t)w : 2 * (int64_t)w + 1);
+      finish_partial<QT, G, D>(a, cur.s, cur.kvh, cur.a0, cur.n, T, Wn, lane);
     }
-    if (one_item) return;
-    if (stage == 0) {
-      stage = 1;
-      p = pb;
-      kvh = kvh_b;
-      u_lo = (int)(b - a0_b);
-      u_hi = pb.n;
-      continue;
-    }
-    if (stage == 1) {
-      stage = 2;
-      p = pb;
-      kvh = kvh_b;
-    } else {
-      x += p.n;
-    }
-    if (x >= a0_e) return;
-    // next item after (p, kvh): the next kv head, else the next sequence with a non-empty context
-    if (++kvh == a.num_kv_heads) {
-      kvh = 0;
-      p.item0 += (int64_t)p.n * a.num_kv_heads;
-      do {
-        if (++p.s >= a.num_seqs) return;  // only if context_lens changed under the launch
-        p.L = clamp_ctx(uniform(a.context_lens[p.s]), a.max_ctx);
-        p.n = (p.L + a.part_tokens - 1) / a.part_tokens;
-      } while (p.n == 0);
-    }
-    u_lo = 0;
-    u_hi = p.n;
+    if (!has) return;
+    cur = nx;
+    has = walk.next(nx);
   }
 }
 
