@@ -75,32 +75,23 @@ template <> struct Op<bf16_t> {
   __device__ static float value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
 };
 
-// Raw K/V storage of one operand slice (8 elements) and its conversion to MT.
-template <typename KVT, typename MT> struct Slice {
-  typedef u32x4 raw;  // 16-bit cache: the slice is already in the operand type
-  // plain loads: each instruction reads half of each 128-byte line it touches,
-  // and the other half must still be in L2 for the next k-step's instruction
-  __device__ static raw load(const char *p) { return ld16(p); }
-  __device__ static u32x4 to_op(raw r) { return r; }
+// A 16-byte piece of a cache row (8 16-bit elements or 16 fp8 codes) and its
+// conversion to the operand type.
+template <typename KVT, typename MT> struct Piece {
+  static constexpr int kElems = 8;
+  __device__ static void to_op(u32x4 r, u32x4 *o) { o[0] = r; }
 };
-template <typename MT> struct Slice<fp8_t, MT> {
-  typedef u32x2 raw;  // 8 e4m3fn codes
-  __device__ static raw load(const char *p) { return *reinterpret_cast<const u32x2 *>(p); }
-  __device__ static u32x4 to_op(raw r) {
-    float f[8];
+template <typename MT> struct Piece<fp8_t, MT> {
+  static constexpr int kElems = 16;
+  __device__ static void to_op(u32x4 r, u32x4 *o) {
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
+    for (int w = 0; w < 4; ++w) {
       const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], false);
       const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], true);
-      f[4 * w] = lo[0];
-      f[4 * w + 1] = lo[1];
-      f[4 * w + 2] = hi[0];
-      f[4 * w + 3] = hi[1];
+      // every e4m3fn value is exact in f16 and in bf16
+      o[w >> 1][2 * (w & 1)] = Op<MT>::bits(lo[0]) | (Op<MT>::bits(lo[1]) << 16);
+      o[w >> 1][2 * (w & 1) + 1] = Op<MT>::bits(hi[0]) | (Op<MT>::bits(hi[1]) << 16);
     }
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = Op<MT>::bits(f[2 * i]) | (Op<MT>::bits(f[2 * i + 1]) << 16);  // exact
-    return o;
   }
 };
 
@@ -125,17 +116,23 @@ struct MfmaSeg {
   static constexpr int NT = D / 16;        // 16-dim output tiles
   static constexpr int LOG2BS = BS == 16 ? 4 : 5;
   static constexpr int EB = Elem<KVT>::kBytes;
-  static constexpr int LDS_STRIDE = D + 8;  // halves per staged V row (padding spreads the banks)
+  static constexpr int PE = Piece<KVT, MT>::kElems;  // elements per 16-byte piece
+  static constexpr int LPR = D / PE;                  // lanes per cache row
+  static constexpr int RPI = 64 / LPR;                // rows per load instruction
+  static constexpr int NLD = CT / RPI;                // load instructions per chunk (K or V)
+  static constexpr int LDS_STRIDE = D + 8;  // halves per staged row (padding spreads the banks)
   static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
+  static_assert(RPI <= 16 && 16 % RPI == 0, "a load instruction stays inside one 16-token tile");
 
   const DecodeArgs &a;
-  const int lane, c16, j;  // lane, column / row within 16, quarter of the wave
-  uint16_t *vs;            // this wavefront's LDS V stage [CT][LDS_STRIDE]
-  float m, l;              // softmax state of head c16 (lane-local, combined over j at the end)
-  f32x4 acc[NT];           // O^T tiles: dims 16 n + 4 j + i of head c16
+  const int lane, c16, j;   // lane, column / row within 16, quarter of the wave
+  const int lrow, lpiece;   // row of a load instruction and 16-byte piece of the row this lane loads
+  uint16_t *ks, *vs;        // this wavefront's LDS stages [CT][LDS_STRIDE], operand type
+  float m, l;               // softmax state of head c16 (lane-local, combined over j at the end)
+  f32x4 acc[NT];            // O^T tiles: dims 16 n + 4 j + i of head c16
 
-  __device__ MfmaSeg(const DecodeArgs &args, int ln, uint16_t *stage)
-      : a(args), lane(ln), c16(ln & 15), j(ln >> 4), vs(stage) {}
+  __device__ MfmaSeg(const DecodeArgs &args, int ln, uint16_t *kstage, uint16_t *vstage)
+      : a(args), lane(ln), c16(ln & 15), j(ln >> 4), lrow(ln / LPR), lpiece(ln % LPR), ks(kstage), vs(vstage) {}
 
   // block ids of the chunk's two 16-token tiles (loads past `last` read its block)
   __device__ __forceinline__ void fetch_blocks(const_i32 *bt, int cs, int last, int *blk) const {
@@ -146,24 +143,33 @@ struct MfmaSeg {
     }
   }
 
+  // Whole cache rows: instruction i reads rows RPI i .. RPI i + RPI - 1 of the
+  // chunk, LPR lanes per row, 16 bytes each -- every row a contiguous run.
   __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
-                                        typename Slice<KVT, MT>::raw (*dst)[KS]) const {
+                                        u32x4 *dst) const {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = min(cs + 16 * tt + c16, last);
-      const char *row = base + ((int64_t)blk[tt] * sb + (int64_t)(t & (BS - 1)) * st) * EB;
-#pragma unroll
-      for (int kb = 0; kb < KS; ++kb) dst[tt][kb] = Slice<KVT, MT>::load(row + (32 * kb + 8 * j) * EB);
+    for (int i = 0; i < NLD; ++i) {
+      const int row = RPI * i + lrow;
+      const int t = min(cs + row, last);
+      const int tile_blk = blk[(RPI * i) / 16];
+      dst[i] = ld16_stream(base + ((int64_t)tile_blk * sb + (int64_t)(t & (BS - 1)) * st + lpiece * PE) * EB);
     }
   }
 
-  // V rows of the chunk into LDS, as the operand type
-  __device__ __forceinline__ void stage_v(typename Slice<KVT, MT>::raw (*vr)[KS]) const {
+  // the chunk's rows into an LDS stage, as the operand type
+  __device__ __forceinline__ void stage(uint16_t *dst, const u32x4 *r) const {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int i = 0; i < NLD; ++i) {
+      u32x4 o[PE / 8];
+      Piece<KVT, MT>::to_op(r[i], o);
 #pragma unroll
-      for (int kb = 0; kb < KS; ++kb)
-        st16(vs + (16 * tt + c16) * LDS_STRIDE + 32 * kb + 8 * j, Slice<KVT, MT>::to_op(vr[tt][kb]));
+      for (int h = 0; h < PE / 8; ++h) st16(dst + (RPI * i + lrow) * LDS_STRIDE + lpiece * PE + 8 * h, o[h]);
+    }
+  }
+
+  // A operand of QK for tile tt, k-step kb: K[16 tt + c16][32 kb + 8 j ..]
+  __device__ __forceinline__ u32x4 k_operand(int tt, int kb) const {
+    return *reinterpret_cast<const u32x4 *>(ks + (16 * tt + c16) * LDS_STRIDE + 32 * kb + 8 * j);
   }
 
   // A operand of PV for output tile n: V[tau(j, i)][16 n + c16], i < 8
@@ -206,7 +212,7 @@ struct MfmaSeg {
   // pipeline state carried from one segment into the next
   u32x4 qop[KS];
   int blk[2];
-  typename Slice<KVT, MT>::raw kr[2][KS], vr[2][KS];
+  u32x4 kr[NLD], vr[NLD];
 
   __device__ void begin(const SegInfo &g) {
     const Ptrs p = ptrs(g);
@@ -248,18 +254,21 @@ struct MfmaSeg {
       fetch_blocks(btn, cn, lastn, nblk);
       __builtin_amdgcn_sched_barrier(0);
 
+      // K rows to LDS, then the next chunk's K loads into the freed registers
+      stage(ks, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
+      __builtin_amdgcn_sched_barrier(0);
       // scores of both 16-token tiles
       f32x4 sc[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         sc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(Slice<KVT, MT>::to_op(kr[tt][kb]), qop[kb], sc[tt]);
+        for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(k_operand(tt, kb), qop[kb], sc[tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
-      __builtin_amdgcn_sched_barrier(0);
-      stage_v(vr);
+      stage(vs, vr);
       __builtin_amdgcn_sched_barrier(0);
       issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
@@ -340,14 +349,15 @@ struct MfmaSeg {
 
 template <typename KVT, typename MT, int D, int G, int BS>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
-  __shared__ uint16_t stage[kWavesPerWG][CT * (D + 8)];
+  __shared__ uint16_t kstage[kWavesPerWG][CT * (D + 8)];
+  __shared__ uint16_t vstage[kWavesPerWG][CT * (D + 8)];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   // workgroups are dealt to the 8 XCDs round-robin; number them so that each
   // XCD's workers hold one contiguous stretch of the work order
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  MfmaSeg<KVT, MT, D, G, BS> seg(a, lane, stage[wave]);
+  MfmaSeg<KVT, MT, D, G, BS> seg(a, lane, kstage[wave], vstage[wave]);
   run_worker<MT, G, D>(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
