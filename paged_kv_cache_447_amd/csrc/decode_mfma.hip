@@ -86,11 +86,11 @@ template <typename MT> struct Piece<fp8_t, MT> {
   __device__ static void to_op(u32x4 r, u32x4 *o) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)r[w], true);
-      // every e4m3fn value is exact in f16 and in bf16
-      o[w >> 1][2 * (w & 1)] = Op<MT>::bits(lo[0]) | (Op<MT>::bits(lo[1]) << 16);
-      o[w >> 1][2 * (w & 1) + 1] = Op<MT>::bits(hi[0]) | (Op<MT>::bits(hi[1]) << 16);
+      // codes 4w .. 4w+3 become operand elements 4w .. 4w+3 (exact conversions)
+      const uint32_t lo = __is_same(MT, f16_t) ? fp8x2_to_f16x2<false>(r[w]) : fp8x2_to_bf16x2<false>(r[w]);
+      const uint32_t hi = __is_same(MT, f16_t) ? fp8x2_to_f16x2<true>(r[w]) : fp8x2_to_bf16x2<true>(r[w]);
+      o[w >> 1][2 * (w & 1)] = lo;
+      o[w >> 1][2 * (w & 1) + 1] = hi;
     }
   }
 };
@@ -120,14 +120,19 @@ struct MfmaSeg {
   static constexpr int LPR = D / PE;                  // lanes per cache row
   static constexpr int RPI = 64 / LPR;                // rows per load instruction
   static constexpr int NLD = CT / RPI;                // load instructions per chunk (K or V)
-  static constexpr int LDS_STRIDE = D + 8;  // halves per staged row (padding spreads the banks)
+  // halves per staged row; the paddings put the rows that one LDS access
+  // touches on distinct banks: 16 consecutive rows for the 16-byte K operand
+  // reads (a 4-bank shift per row), 4 consecutive rows for the transposed V
+  // reads (an 8-bank shift per row)
+  static constexpr int KSTRIDE = D + 8;
+  static constexpr int VSTRIDE = D + 16;
   static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
   static_assert(RPI <= 16 && 16 % RPI == 0, "a load instruction stays inside one 16-token tile");
 
   const DecodeArgs &a;
   const int lane, c16, j;   // lane, column / row within 16, quarter of the wave
   const int lrow, lpiece;   // row of a load instruction and 16-byte piece of the row this lane loads
-  uint16_t *ks, *vs;        // this wavefront's LDS stages [CT][LDS_STRIDE], operand type
+  uint16_t *ks, *vs;        // this wavefront's LDS stages [CT][KSTRIDE], [CT][VSTRIDE], operand type
   float m, l;               // softmax state of head c16 (lane-local, combined over j at the end)
   f32x4 acc[NT];            // O^T tiles: dims 16 n + 4 j + i of head c16
 
@@ -151,37 +156,44 @@ struct MfmaSeg {
     for (int i = 0; i < NLD; ++i) {
       const int row = RPI * i + lrow;
       const int t = min(cs + row, last);
-      const int tile_blk = blk[(RPI * i) / 16];
-      dst[i] = ld16_stream(base + ((int64_t)tile_blk * sb + (int64_t)(t & (BS - 1)) * st + lpiece * PE) * EB);
+      const char *bb = base + (int64_t)blk[(RPI * i) / 16] * sb * EB;  // uniform block base
+      dst[i] = ld16_stream(bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + lpiece * PE) * EB));
     }
   }
 
   // the chunk's rows into an LDS stage, as the operand type
+  template <int STRIDE>
   __device__ __forceinline__ void stage(uint16_t *dst, const u32x4 *r) const {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       u32x4 o[PE / 8];
       Piece<KVT, MT>::to_op(r[i], o);
 #pragma unroll
-      for (int h = 0; h < PE / 8; ++h) st16(dst + (RPI * i + lrow) * LDS_STRIDE + lpiece * PE + 8 * h, o[h]);
+      for (int h = 0; h < PE / 8; ++h) st16(dst + (RPI * i + lrow) * STRIDE + lpiece * PE + 8 * h, o[h]);
     }
   }
 
   // A operand of QK for tile tt, k-step kb: K[16 tt + c16][32 kb + 8 j ..]
   __device__ __forceinline__ u32x4 k_operand(int tt, int kb) const {
-    return *reinterpret_cast<const u32x4 *>(ks + (16 * tt + c16) * LDS_STRIDE + 32 * kb + 8 * j);
+    return *reinterpret_cast<const u32x4 *>(ks + (16 * tt + c16) * KSTRIDE + 32 * kb + 8 * j);
   }
 
-  // A operand of PV for output tile n: V[tau(j, i)][16 n + c16], i < 8
+  // A operand of PV for output tile n: V[tau(j, i)][16 n + c16], i < 8.
+  // ds_read_b64_tr_b16 hands lane i of a 16-lane group the elements
+  // M[4 r + i / 4][i % 4], r < 4, where M[k] are the four 16-bit values at lane
+  // k's address.  Lane k of quarter j therefore points at row tau(j, 4 h + k / 4)
+  // (h = which half of the operand), columns 16 n + 4 (k % 4) .. +3: lane i
+  // receives column 16 n + i of the four rows, in the contraction's order.
   __device__ __forceinline__ u32x4 vt_operand(int n) const {
-    const uint16_t *col = vs + 16 * n + c16;
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r0 = 2 * i < 4 ? 4 * j + 2 * i : 16 + 4 * j + 2 * i - 4;
-      o[i] = (uint32_t)col[r0 * LDS_STRIDE] | ((uint32_t)col[(r0 + 1) * LDS_STRIDE] << 16);
-    }
-    return o;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int col = 16 * n + 4 * (c16 & 3);
+    const uint16_t *r0 = vs + (4 * j + (c16 >> 2)) * VSTRIDE + col;       // tokens 4 j .. 4 j + 3
+    const uint16_t *r1 = vs + (16 + 4 * j + (c16 >> 2)) * VSTRIDE + col;  // tokens 16 + 4 j ..
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)r0);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)r1);
+    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+    return u32x4{w0[0], w0[1], w1[0], w1[1]};
   }
 
   // where a segment's rows live
@@ -255,7 +267,7 @@ struct MfmaSeg {
       __builtin_amdgcn_sched_barrier(0);
 
       // K rows to LDS, then the next chunk's K loads into the freed registers
-      stage(ks, kr);
+      stage<KSTRIDE>(ks, kr);
       __builtin_amdgcn_sched_barrier(0);
       issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
       __builtin_amdgcn_sched_barrier(0);
@@ -268,7 +280,7 @@ struct MfmaSeg {
         for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(k_operand(tt, kb), qop[kb], sc[tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      stage(vs, vr);
+      stage<VSTRIDE>(vs, vr);
       __builtin_amdgcn_sched_barrier(0);
       issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
@@ -350,7 +362,7 @@ struct MfmaSeg {
 template <typename KVT, typename MT, int D, int G, int BS>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
   __shared__ uint16_t kstage[kWavesPerWG][CT * (D + 8)];
-  __shared__ uint16_t vstage[kWavesPerWG][CT * (D + 8)];
+  __shared__ uint16_t vstage[kWavesPerWG][CT * (D + 16)];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   // workgroups are dealt to the 8 XCDs round-robin; number them so that each

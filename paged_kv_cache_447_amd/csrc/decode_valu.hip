@@ -24,7 +24,8 @@
 // (already in cache), never to another worker's tokens.
 //
 // Arithmetic (fp32): score = (q . K) * scale * log2(e), the dot product per lane
-// with v_dot2 (16-bit KV) or FMAs (fp32 / fp8 KV), then a DPP sum over the LPR
+// with v_dot2 (16-bit and fp8 KV, fp8 converted exactly to the query's type)
+// or FMAs (fp32 KV), then a DPP sum over the LPR
 // lanes of a token; running max m and sum l with the rescale by
 // exp2(m_old - m_new) per chunk; acc += p * V.  Masked tokens get p = 0 and a
 // finite (duplicated) V row, so nothing poisons the sum.
@@ -89,20 +90,30 @@ template <> struct QSlice<f32_t, f32_t> {
   }
 };
 
-// fp8 K with a 16-bit query: 16 codes per slice, the query slice kept in fp32
+// fp8 K with a 16-bit query: 16 codes per slice, converted exactly to the
+// query's type in pairs, then v_dot2 against the packed query slice
 template <typename QT> struct QSliceFp8 {
-  float f[16];
+  u32x4 w[2];  // 16 query elements
   __device__ void load(const void *q, int64_t off) {
     const char *p = reinterpret_cast<const char *>(q) + off * 2;
-    Elem<QT>::unpack(ld16(p), f);
-    Elem<QT>::unpack(ld16(p + 16), f + 8);
+    w[0] = ld16(p);
+    w[1] = ld16(p + 16);
   }
   __device__ float dot(u32x4 k) const {
-    float kf[16];
-    Elem<fp8_t>::unpack(k, kf);
     float d = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d = __builtin_fmaf(f[i], kf[i], d);
+    for (int i = 0; i < 4; ++i) {  // codes 4i .. 4i+3 against query elements 4i .. 4i+3
+      const uint32_t k01 = __is_same(QT, f16_t) ? fp8x2_to_f16x2<false>(k[i]) : fp8x2_to_bf16x2<false>(k[i]);
+      const uint32_t k23 = __is_same(QT, f16_t) ? fp8x2_to_f16x2<true>(k[i]) : fp8x2_to_bf16x2<true>(k[i]);
+      const uint32_t q01 = w[i >> 1][2 * (i & 1)], q23 = w[i >> 1][2 * (i & 1) + 1];
+      if constexpr (__is_same(QT, f16_t)) {
+        d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q01), __builtin_bit_cast(h2_t, k01), d, false);
+        d = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, q23), __builtin_bit_cast(h2_t, k23), d, false);
+      } else {
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q01), __builtin_bit_cast(b2_t, k01), d, false);
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, q23), __builtin_bit_cast(b2_t, k23), d, false);
+      }
+    }
     return d;
   }
 };
@@ -173,12 +184,15 @@ struct ValuSeg {
     for (int i = 0; i < NL; ++i) blk[i] = e[NBC == 1 ? 0 : (i * TPW) / BS];
   }
 
+  // the block's base address is uniform (scalar registers); each lane adds a
+  // 32-bit offset inside the block
   __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
                                         u32x4 *dst) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int t = min(cs + i * TPW + tg, last);
-      dst[i] = ld16_stream(base + ((int64_t)blk[i] * sb + (int64_t)(t & (BS - 1)) * st) * EB);
+      const char *bb = base + (int64_t)blk[i] * sb * EB;
+      dst[i] = ld16_stream(bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + r * VEC) * EB));
     }
   }
 
@@ -191,8 +205,8 @@ struct ValuSeg {
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
     p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
-    p.kb = reinterpret_cast<const char *>(a.k_cache) + ((int64_t)g.kvh * a.k_sh + r * VEC) * EB;
-    p.vb = reinterpret_cast<const char *>(a.v_cache) + ((int64_t)g.kvh * a.v_sh + r * VEC) * EB;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;  // uniform
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
     p.last = g.t_hi - 1;
     return p;
   }
@@ -255,13 +269,15 @@ struct ValuSeg {
 
       float sc[G][NL];
 #pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int h = 0; h < G; ++h) sc[h][i] = q[h].dot(kr[i]);
+      group_sum_n<LPR, G * NL>(&sc[0][0]);
+#pragma unroll
       for (int i = 0; i < NL; ++i) {
         const bool valid = cs + i * TPW + tg <= p.last;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float d = group_sum<LPR>(q[h].dot(kr[i])) * a.qk_scale_log2;
-          sc[h][i] = valid ? d : -INFINITY;
-        }
+        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * a.qk_scale_log2 : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);

@@ -100,6 +100,18 @@ template <> struct Elem<fp8_t> {
   }
 };
 
+// Two e4m3fn codes of a 32-bit word (bytes 0-1, or 2-3 with `hi`) to a packed
+// pair of f16 or bf16 values.  Exact: every e4m3fn value is representable in
+// both 16-bit formats (gfx950 converts with a unit scale).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // ---------------------------------------------------------------------------------
 // wave64 lane exchange
 
@@ -127,6 +139,32 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (N >= 16) v += dpp<DPP_ROW_MIRROR>(v);
   if constexpr (N >= 32) v += __shfl_xor(v, 16);
   return v;
+}
+
+// The same for M independent values, one DPP step across all of them at a
+// time, so that no step waits on the one before it for the same value.
+template <int N, int M>
+__device__ __forceinline__ void group_sum_n(float *v) {
+  if constexpr (N >= 2) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] += dpp<DPP_QUAD_XOR1>(v[i]);
+  }
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] += dpp<DPP_QUAD_XOR2>(v[i]);
+  }
+  if constexpr (N >= 8) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] += dpp<DPP_ROW_HALF_MIRROR>(v[i]);
+  }
+  if constexpr (N >= 16) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] += dpp<DPP_ROW_MIRROR>(v[i]);
+  }
+  if constexpr (N >= 32) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) v[i] += __shfl_xor(v[i], 16);
+  }
 }
 
 // Combine across the 64/N groups of N lanes (lanes at the same position in every

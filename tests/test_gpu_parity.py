@@ -196,8 +196,11 @@ def test_needle_block_resolution_is_bit_exact(kv_dtype, G, bs):
                 f"round {rnd} partition {part} workers {workers}"
 
 
-def test_fp8_hardware_decode_matches_ocp_table():
-    """ctx = 1 makes out = V exactly: put all 256 codes in V rows and read them back in fp32."""
+@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("G", [1, 4])
+def test_fp8_hardware_decode_matches_ocp_table(q_dtype, G):
+    """ctx = 1 makes out = V exactly: put all 256 codes in V rows and read them back in fp32,
+    through the vector path (G = 1) and the matrix-core path (G = 4), for both query types."""
     D, bs = 128, 16
     dev = "cuda"
     kc = torch.zeros((4, bs, 1, D), dtype=torch.uint8, device=dev)
@@ -206,10 +209,12 @@ def test_fp8_hardware_decode_matches_ocp_table():
     vc[1, 0, 0] = torch.arange(128, 256, dtype=torch.int32).to(torch.uint8).to(dev)
     bt = torch.tensor([[0], [1]], dtype=torch.int32, device=dev)
     cl = torch.tensor([1, 1], dtype=torch.int32, device=dev)
-    q = torch.randn((2, 1, D), device=dev).half()
-    out = torch.empty((2, 1, D), dtype=torch.float32, device=dev)
+    q = torch.randn((2, G, D), device=dev).to(q_dtype)
+    out = torch.empty((2, G, D), dtype=torch.float32, device=dev)
     pa.decode(out, q, kc.view(torch.float8_e4m3fn), vc.view(torch.float8_e4m3fn), bt, cl, bs, 0.1, 1)
-    got = out.cpu().view(-1).numpy()
+    got = out.cpu()[:, 0].reshape(-1).numpy()
+    for g in range(1, G):
+        assert torch.equal(out[:, g].cpu().view(torch.int32), out[:, 0].cpu().view(torch.int32))
     for code in range(256):
         want = oracle.fp8_to_double(code)
         if math.isnan(want):
