@@ -35,9 +35,8 @@
 //   are multiplied in, so the weights carry ~16 more bits than one rounding
 //   would give (a single bf16 rounding of the weights alone would cost more
 //   than the fp32-output error budget).
-// K and V loads follow the rolling pipeline of the vector path: the next
-// chunk's K loads go out after this chunk's scores, its V loads as soon as
-// this chunk's V rows sit in LDS.  fp8 caches are decoded exactly into the
+// K and V rows pass through LDS, so the next chunk's loads go out as soon as
+// this chunk's rows are staged, before any of its arithmetic.  fp8 caches are decoded exactly into the
 // query's 16-bit type on the way (every e4m3fn value is representable).
 #include "pa_sched.h"
 
@@ -47,6 +46,7 @@ namespace {
 
 constexpr int kWavesPerWG = 4;
 constexpr int CT = 32;  // tokens per chunk: two 16-token QK tiles, one 32-token PV step
+constexpr float kSlack = 8.0f;  // how far (log2 units) scores may exceed the running reference max
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -266,10 +266,15 @@ struct MfmaSeg {
       fetch_blocks(btn, cn, lastn, nblk);
       __builtin_amdgcn_sched_barrier(0);
 
-      // K rows to LDS, then the next chunk's K loads into the freed registers
+      // this chunk's K and V rows to LDS, then the next chunk's loads into the
+      // freed registers: a whole chunk stays in flight while this one is computed
       stage<KSTRIDE>(ks, kr);
       __builtin_amdgcn_sched_barrier(0);
       issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      stage<VSTRIDE>(vs, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
       // scores of both 16-token tiles
       f32x4 sc[2];
@@ -279,11 +284,6 @@ struct MfmaSeg {
 #pragma unroll
         for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(k_operand(tt, kb), qop[kb], sc[tt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      stage<VSTRIDE>(vs, vr);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
-      __builtin_amdgcn_sched_barrier(0);
 
       // online softmax for head c16 over the lane's 8 tokens, then across the 4 quarters
       float p8[8];
@@ -297,12 +297,18 @@ struct MfmaSeg {
       }
       cm = fmaxf(cm, __shfl_xor(cm, 16));
       cm = fmaxf(cm, __shfl_xor(cm, 32));
-      const float mn = fmaxf(m, cm);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
+      // lazy rescale: the reference max moves only when a score exceeds it by
+      // more than kSlack (log2 units), so weights stay below 2^kSlack and the
+      // accumulator rescale is skipped for almost every chunk
+      if (__ballot(cm > m + kSlack)) {
+        const float mn = fmaxf(m, cm);
+        const float alpha = fast_exp2(m - mn);
+        m = mn;
+        l *= alpha;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+      }
+      const float mn = m;
       u32x4 phi, plo;
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {

@@ -26,8 +26,9 @@
 // Arithmetic (fp32): score = (q . K) * scale * log2(e), the dot product per lane
 // with v_dot2 (16-bit and fp8 KV, fp8 converted exactly to the query's type)
 // or FMAs (fp32 KV), then a DPP sum over the LPR
-// lanes of a token; running max m and sum l with the rescale by
-// exp2(m_old - m_new) per chunk; acc += p * V.  Masked tokens get p = 0 and a
+// lanes of a token; a running reference max m and sum l, rescaled by
+// exp2(m_old - m_new) only when a chunk's max exceeds m by more than 8 (so
+// weights stay below 2^8 and most chunks skip the rescale); acc += p * V.  Masked tokens get p = 0 and a
 // finite (duplicated) V row, so nothing poisons the sum.
 #include "pa_sched.h"
 
@@ -36,6 +37,7 @@ namespace pa {
 namespace {
 
 constexpr int kWavesPerWG = 4;
+constexpr float kSlack = 8.0f;  // how far (log2 units) scores may exceed the running reference max
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
@@ -289,14 +291,18 @@ struct ValuSeg {
 #pragma unroll
         for (int i = 1; i < NL; ++i) cm = fmaxf(cm, sc[h][i]);
         cm = across_groups_max<LPR>(cm);
-        const float mn = fmaxf(m[h], cm);
-        const float alpha = fast_exp2(m[h] - mn);
-        l[h] *= alpha;
+        // lazy rescale: the reference max moves only when a score exceeds it by
+        // more than kSlack (log2 units); weights stay below 2^kSlack
+        if (cm > m[h] + kSlack) {  // uniform: m and cm are the same on every lane
+          const float mn = fmaxf(m[h], cm);
+          const float alpha = fast_exp2(m[h] - mn);
+          l[h] *= alpha;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[h][v] *= alpha;
+          for (int v = 0; v < VEC; ++v) acc[h][v] *= alpha;
+          m[h] = mn;
+        }
 #pragma unroll
-        for (int i = 0; i < NL; ++i) sc[h][i] = fast_exp2(sc[h][i] - mn);
-        m[h] = mn;
+        for (int i = 0; i < NL; ++i) sc[h][i] = fast_exp2(sc[h][i] - m[h]);
       }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
