@@ -95,6 +95,17 @@ template <typename MT> struct Piece<fp8_t, MT> {
   }
 };
 
+// Two ds_read_b64_tr_b16 (8 bytes at each lane's address, transposed across
+// each 16-lane group) forming one 16x16x32 operand.
+__device__ __forceinline__ u32x4 read_tr(const void *p0, const void *p1) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p0);
+  const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p1);
+  const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+  return u32x4{w0[0], w0[1], w1[0], w1[1]};
+}
+
 template <typename OT>
 __device__ __forceinline__ void store4(void *base, int64_t off, const float *x) {
   if constexpr (__is_same(OT, f32_t)) {
@@ -110,226 +121,89 @@ __device__ __forceinline__ void store4(void *base, int64_t off, const float *x) 
   }
 }
 
-template <typename KVT, typename MT, int D, int G, int BS>
-struct MfmaSeg {
-  static constexpr int KS = D / 32;        // k-steps of the QK contraction
-  static constexpr int NT = D / 16;        // 16-dim output tiles
-  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
-  static constexpr int EB = Elem<KVT>::kBytes;
-  static constexpr int PE = Piece<KVT, MT>::kElems;  // elements per 16-byte piece
-  static constexpr int LPR = D / PE;                  // lanes per cache row
-  static constexpr int RPI = 64 / LPR;                // rows per load instruction
-  static constexpr int NLD = CT / RPI;                // load instructions per chunk (K or V)
-  // halves per staged row; the paddings put the rows that one LDS access
-  // touches on distinct banks: 16 consecutive rows for the 16-byte K operand
-  // reads (a 4-bank shift per row), 4 consecutive rows for the transposed V
-  // reads (an 8-bank shift per row)
-  static constexpr int KSTRIDE = D + 8;
-  static constexpr int VSTRIDE = D + 16;
+// The arithmetic of one wavefront on one (sequence, kv head) segment, whatever
+// brings the chunk's rows into LDS: scores, online softmax, output update and
+// the segment's epilogue.
+template <typename MT, int D, int G>
+struct MfmaMath {
+  static constexpr int KS = D / 32;  // k-steps of the QK contraction
+  static constexpr int NT = D / 16;  // 16-dim output tiles
   static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
-  static_assert(RPI <= 16 && 16 % RPI == 0, "a load instruction stays inside one 16-token tile");
 
   const DecodeArgs &a;
-  const int lane, c16, j;   // lane, column / row within 16, quarter of the wave
-  const int lrow, lpiece;   // row of a load instruction and 16-byte piece of the row this lane loads
-  uint16_t *ks, *vs;        // this wavefront's LDS stages [CT][KSTRIDE], [CT][VSTRIDE], operand type
-  float m, l;               // softmax state of head c16 (lane-local, combined over j at the end)
-  f32x4 acc[NT];            // O^T tiles: dims 16 n + 4 j + i of head c16
+  const int c16, j;  // column / row within 16, quarter of the wave
+  float m, l;        // softmax state of head c16 (lane-local, combined over j at the end)
+  f32x4 acc[NT];     // O^T tiles: dims 16 n + 4 j + i of head c16
 
-  __device__ MfmaSeg(const DecodeArgs &args, int ln, uint16_t *kstage, uint16_t *vstage)
-      : a(args), lane(ln), c16(ln & 15), j(ln >> 4), lrow(ln / LPR), lpiece(ln % LPR), ks(kstage), vs(vstage) {}
+  __device__ MfmaMath(const DecodeArgs &args, int lane) : a(args), c16(lane & 15), j(lane >> 4) {}
 
-  // block ids of the chunk's two 16-token tiles (loads past `last` read its block)
-  __device__ __forceinline__ void fetch_blocks(const_i32 *bt, int cs, int last, int *blk) const {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      int b = bt[min(cs + 16 * tt, last) >> LOG2BS];
-      blk[tt] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-    }
-  }
-
-  // Whole cache rows: instruction i reads rows RPI i .. RPI i + RPI - 1 of the
-  // chunk, LPR lanes per row, 16 bytes each -- every row a contiguous run.
-  __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
-                                        u32x4 *dst) const {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int row = RPI * i + lrow;
-      const int t = min(cs + row, last);
-      const char *bb = base + (int64_t)blk[(RPI * i) / 16] * sb * EB;  // uniform block base
-      dst[i] = ld16_stream(bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + lpiece * PE) * EB));
-    }
-  }
-
-  // the chunk's rows into an LDS stage, as the operand type
-  template <int STRIDE>
-  __device__ __forceinline__ void stage(uint16_t *dst, const u32x4 *r) const {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      u32x4 o[PE / 8];
-      Piece<KVT, MT>::to_op(r[i], o);
-#pragma unroll
-      for (int h = 0; h < PE / 8; ++h) st16(dst + (RPI * i + lrow) * STRIDE + lpiece * PE + 8 * h, o[h]);
-    }
-  }
-
-  // A operand of QK for tile tt, k-step kb: K[16 tt + c16][32 kb + 8 j ..]
-  __device__ __forceinline__ u32x4 k_operand(int tt, int kb) const {
-    return *reinterpret_cast<const u32x4 *>(ks + (16 * tt + c16) * KSTRIDE + 32 * kb + 8 * j);
-  }
-
-  // A operand of PV for output tile n: V[tau(j, i)][16 n + c16], i < 8.
-  // ds_read_b64_tr_b16 hands lane i of a 16-lane group the elements
-  // M[4 r + i / 4][i % 4], r < 4, where M[k] are the four 16-bit values at lane
-  // k's address.  Lane k of quarter j therefore points at row tau(j, 4 h + k / 4)
-  // (h = which half of the operand), columns 16 n + 4 (k % 4) .. +3: lane i
-  // receives column 16 n + i of the four rows, in the contraction's order.
-  __device__ __forceinline__ u32x4 vt_operand(int n) const {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-    const int col = 16 * n + 4 * (c16 & 3);
-    const uint16_t *r0 = vs + (4 * j + (c16 >> 2)) * VSTRIDE + col;       // tokens 4 j .. 4 j + 3
-    const uint16_t *r1 = vs + (16 + 4 * j + (c16 >> 2)) * VSTRIDE + col;  // tokens 16 + 4 j ..
-    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)r0);
-    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)r1);
-    const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-    return u32x4{w0[0], w0[1], w1[0], w1[1]};
-  }
-
-  // where a segment's rows live
-  struct Ptrs {
-    const_i32 *bt;
-    const char *kb, *vb;
-    int last;
-  };
-  __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
-    Ptrs p;
-    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
-    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;
-    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
-    p.last = g.t_hi - 1;
-    return p;
-  }
-  // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
-  __device__ __forceinline__ void load_q(const SegInfo &g, u32x4 *dst) const {
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)g.s * a.q_ss +
-                           (int64_t)(g.kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
-#pragma unroll
-    for (int kb = 0; kb < KS; ++kb) {
-      dst[kb] = ld16(qrow + 32 * kb + 8 * j);
-      if (c16 >= G) dst[kb] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // pipeline state carried from one segment into the next
-  u32x4 qop[KS];
-  int blk[2];
-  u32x4 kr[NLD], vr[NLD];
-
-  __device__ void begin(const SegInfo &g) {
-    const Ptrs p = ptrs(g);
-    load_q(g, qop);
-    fetch_blocks(p.bt, g.t_lo, p.last, blk);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
-    __builtin_amdgcn_sched_barrier(0);
-    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  __device__ void run(const SegInfo &g, const SegInfo &nx, bool has) {
+  __device__ __forceinline__ void reset() {
     m = -INFINITY;
     l = 0.0f;
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (g.t_hi <= g.t_lo) {  // only if context_lens changed under the launch
-      if (has) begin(nx);
-      return;
+  }
+
+  // S^T of the chunk's two 16-token tiles; kop(tt, kb) is the A operand
+  // K[16 tt + c16][32 kb + 8 j ..]
+  template <class KOp>
+  __device__ __forceinline__ void scores(const u32x4 *qop, KOp kop, f32x4 *sc) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      sc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(kop(tt, kb), qop[kb], sc[tt]);
     }
-    const Ptrs p = ptrs(g);
-    // the chunk after this segment's last one: the next segment's first (or,
-    // for the range's last segment, this last chunk again -- a cache hit, unused)
-    const Ptrs pn = has ? ptrs(nx) : p;
-    u32x4 qn[KS];
-    load_q(has ? nx : g, qn);
+  }
 
-    const int nch = (g.t_hi - g.t_lo + CT - 1) / CT;
-    int cs = g.t_lo;
-    for (int c = 0; c < nch; ++c) {
-      const bool lastc = c + 1 == nch;
-      const int cn = lastc ? (has ? nx.t_lo : cs) : cs + CT;
-      const_i32 *btn = lastc ? pn.bt : p.bt;
-      const char *kbn = lastc ? pn.kb : p.kb;
-      const char *vbn = lastc ? pn.vb : p.vb;
-      const int lastn = lastc ? pn.last : p.last;
-      int nblk[2];
-      fetch_blocks(btn, cn, lastn, nblk);
-      __builtin_amdgcn_sched_barrier(0);
-
-      // this chunk's K and V rows to LDS, then the next chunk's loads into the
-      // freed registers: a whole chunk stays in flight while this one is computed
-      stage<KSTRIDE>(ks, kr);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
-      __builtin_amdgcn_sched_barrier(0);
-      stage<VSTRIDE>(vs, vr);
-      __builtin_amdgcn_sched_barrier(0);
-      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
-      __builtin_amdgcn_sched_barrier(0);
-      // scores of both 16-token tiles
-      f32x4 sc[2];
+  // online softmax for head c16 over the lane's 8 tokens (those past `last`
+  // masked), then across the 4 quarters; returns the weights as P^T operands
+  __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, u32x4 &phi, u32x4 &plo) {
+    float p8[8];
+    float cm = -INFINITY;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        sc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(k_operand(tt, kb), qop[kb], sc[tt]);
-      }
-
-      // online softmax for head c16 over the lane's 8 tokens, then across the 4 quarters
-      float p8[8];
-      float cm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
-        const float x = sc[i >> 2][i & 3] * a.qk_scale_log2;
-        p8[i] = cs + tok <= p.last ? x : -INFINITY;
-        cm = fmaxf(cm, p8[i]);
-      }
-      cm = fmaxf(cm, __shfl_xor(cm, 16));
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
-      // lazy rescale: the reference max moves only when a score exceeds it by
-      // more than kSlack (log2 units), so weights stay below 2^kSlack and the
-      // accumulator rescale is skipped for almost every chunk
-      if (__ballot(cm > m + kSlack)) {
-        const float mn = fmaxf(m, cm);
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
-        l *= alpha;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-      }
-      const float mn = m;
-      u32x4 phi, plo;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
-        l += e0 + e1;
-        const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
-        phi[i >> 1] = h0 | (h1 << 16);
-        plo[i >> 1] = Op<MT>::bits(e0 - Op<MT>::value(h0)) | (Op<MT>::bits(e1 - Op<MT>::value(h1)) << 16);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const u32x4 vt = vt_operand(n);
-        acc[n] = Op<MT>::mma(vt, phi, acc[n]);
-        acc[n] = Op<MT>::mma(vt, plo, acc[n]);
-      }
-      cs = cn;
-      blk[0] = nblk[0];
-      blk[1] = nblk[1];
+    for (int i = 0; i < 8; ++i) {
+      const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
+      const float x = sc[i >> 2][i & 3] * a.qk_scale_log2;
+      p8[i] = cs + tok <= last ? x : -INFINITY;
+      cm = fmaxf(cm, p8[i]);
     }
+    cm = fmaxf(cm, __shfl_xor(cm, 16));
+    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    // lazy rescale: the reference max moves only when a score exceeds it by
+    // more than kSlack (log2 units), so weights stay below 2^kSlack and the
+    // accumulator rescale is skipped for almost every chunk
+    if (__ballot(cm > m + kSlack)) {
+      const float mn = fmaxf(m, cm);
+      const float alpha = fast_exp2(m - mn);
+      m = mn;
+      l *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < KS; ++kb) qop[kb] = qn[kb];
+      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
+    }
+    const float mn = m;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
+      l += e0 + e1;
+      const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
+      phi[i >> 1] = h0 | (h1 << 16);
+      plo[i >> 1] = Op<MT>::bits(e0 - Op<MT>::value(h0)) | (Op<MT>::bits(e1 - Op<MT>::value(h1)) << 16);
+    }
+  }
+
+  // O^T += V^T P^T; vop(n) is the A operand V[tau(j, i)][16 n + c16], i < 8
+  template <class VOp>
+  __device__ __forceinline__ void accumulate(u32x4 phi, u32x4 plo, VOp vop) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const u32x4 vt = vop(n);
+      acc[n] = Op<MT>::mma(vt, phi, acc[n]);
+      acc[n] = Op<MT>::mma(vt, plo, acc[n]);
+    }
+  }
+
+  __device__ __forceinline__ void finish() {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
   }
@@ -365,18 +239,545 @@ struct MfmaSeg {
   }
 };
 
+// ---------------------------------------------------------------------------
+// fp8 caches: rows are loaded into registers, decoded, and staged in LDS as
+// the operand type (the loads of chunk c+1 are in flight while chunk c is
+// computed).
+template <typename KVT, typename MT, int D, int G, int BS>
+struct MfmaRegSeg : MfmaMath<MT, D, G> {
+  using Math = MfmaMath<MT, D, G>;
+  using Math::a;
+  using Math::c16;
+  using Math::j;
+  static constexpr int KS = Math::KS;
+  static constexpr int NT = Math::NT;
+  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
+  static constexpr int EB = Elem<KVT>::kBytes;
+  static constexpr int PE = Piece<KVT, MT>::kElems;  // elements per 16-byte piece
+  static constexpr int LPR = D / PE;                  // lanes per cache row
+  static constexpr int RPI = 64 / LPR;                // rows per load instruction
+  static constexpr int NLD = CT / RPI;                // load instructions per chunk (K or V)
+  // halves per staged row; the paddings put the rows that one LDS access
+  // touches on distinct banks: 16 consecutive rows for the 16-byte K operand
+  // reads (a 4-bank shift per row), 4 consecutive rows for the transposed V
+  // reads (an 8-bank shift per row)
+  static constexpr int KSTRIDE = D + 8;
+  static constexpr int VSTRIDE = D + 16;
+  static constexpr int kLdsBytes = 2 * CT * (KSTRIDE + VSTRIDE);
+  static_assert(RPI <= 16 && 16 % RPI == 0, "a load instruction stays inside one 16-token tile");
+
+  const int lrow, lpiece;  // row of a load instruction and 16-byte piece of the row this lane loads
+  uint16_t *ks, *vs;       // this wavefront's LDS stages [CT][KSTRIDE], [CT][VSTRIDE], operand type
+
+  __device__ MfmaRegSeg(const DecodeArgs &args, int ln, char *lds)
+      : Math(args, ln), lrow(ln / LPR), lpiece(ln % LPR), ks(reinterpret_cast<uint16_t *>(lds)),
+        vs(reinterpret_cast<uint16_t *>(lds) + CT * KSTRIDE) {}
+
+  // block ids of the chunk's two 16-token tiles (loads past `last` read its block)
+  __device__ __forceinline__ void fetch_blocks(const_i32 *bt, int cs, int last, int *blk) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      int b = bt[min(cs + 16 * tt, last) >> LOG2BS];
+      blk[tt] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+    }
+  }
+
+  // Whole cache rows: instruction i reads rows RPI i .. RPI i + RPI - 1 of the
+  // chunk, LPR lanes per row, 16 bytes each -- every row a contiguous run.
+  __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
+                                        u32x4 *dst) const {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int row = RPI * i + lrow;
+      const int t = min(cs + row, last);
+      const char *bb = base + (int64_t)blk[(RPI * i) / 16] * sb * EB;  // uniform block base
+      dst[i] = ld16_stream(bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + lpiece * PE) * EB));
+    }
+  }
+
+  // the chunk's rows into an LDS stage, as the operand type
+  template <int STRIDE>
+  __device__ __forceinline__ void stage(uint16_t *dst, const u32x4 *r) const {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      u32x4 o[PE / 8];
+      Piece<KVT, MT>::to_op(r[i], o);
+#pragma unroll
+      for (int h = 0; h < PE / 8; ++h) st16(dst + (RPI * i + lrow) * STRIDE + lpiece * PE + 8 * h, o[h]);
+    }
+  }
+
+  __device__ __forceinline__ u32x4 k_operand(int tt, int kb) const {
+    return *reinterpret_cast<const u32x4 *>(ks + (16 * tt + c16) * KSTRIDE + 32 * kb + 8 * j);
+  }
+
+  // ds_read_b64_tr_b16 hands lane i of a 16-lane group the elements
+  // M[4 r + i / 4][i % 4], r < 4, where M[k] are the four 16-bit values at lane
+  // k's address.  Lane k of quarter j therefore points at row tau(j, 4 h + k / 4)
+  // (h = which half of the operand), columns 16 n + 4 (k % 4) .. +3: lane i
+  // receives column 16 n + i of the four rows, in the contraction's order.
+  __device__ __forceinline__ u32x4 vt_operand(int n) const {
+    const int col = 16 * n + 4 * (c16 & 3);
+    const uint16_t *r0 = vs + (4 * j + (c16 >> 2)) * VSTRIDE + col;       // tokens 4 j .. 4 j + 3
+    const uint16_t *r1 = vs + (16 + 4 * j + (c16 >> 2)) * VSTRIDE + col;  // tokens 16 + 4 j ..
+    return read_tr(r0, r1);
+  }
+
+  // where a segment's rows live
+  struct Ptrs {
+    const_i32 *bt;
+    const char *kb, *vb;
+    int last;
+  };
+  __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
+    Ptrs p;
+    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
+    p.last = g.t_hi - 1;
+    return p;
+  }
+  // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
+  __device__ __forceinline__ void load_q(const SegInfo &g, u32x4 *dst) const {
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)g.s * a.q_ss +
+                           (int64_t)(g.kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+      dst[kb] = ld16(qrow + 32 * kb + 8 * j);
+      if (c16 >= G) dst[kb] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // pipeline state carried from one segment into the next
+  u32x4 qop[KS];
+  int blk[2];
+  u32x4 kr[NLD], vr[NLD];
+
+  __device__ void begin(const SegInfo &g, const Walker &) { begin(g); }
+  __device__ void publish(const SegInfo &g, const Split &sp) {
+    finish_partial<MT, G, D>(a, g.s, g.kvh, g.a0, g.n, sp, 16 * j + c16);
+  }
+  __device__ void end() {}
+
+  __device__ void begin(const SegInfo &g) {
+    const Ptrs p = ptrs(g);
+    load_q(g, qop);
+    fetch_blocks(p.bt, g.t_lo, p.last, blk);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  __device__ void run(const SegInfo &g, const SegInfo &nx, bool has) {
+    Math::reset();
+    if (g.t_hi <= g.t_lo) {  // only if context_lens changed under the launch
+      if (has) begin(nx);
+      return;
+    }
+    const Ptrs p = ptrs(g);
+    // the chunk after this segment's last one: the next segment's first (or,
+    // for the range's last segment, this last chunk again -- a cache hit, unused)
+    const Ptrs pn = has ? ptrs(nx) : p;
+    u32x4 qn[KS];
+    load_q(has ? nx : g, qn);
+
+    const int nch = (g.t_hi - g.t_lo + CT - 1) / CT;
+    int cs = g.t_lo;
+    for (int c = 0; c < nch; ++c) {
+      const bool lastc = c + 1 == nch;
+      const int cn = lastc ? (has ? nx.t_lo : cs) : cs + CT;
+      const_i32 *btn = lastc ? pn.bt : p.bt;
+      const char *kbn = lastc ? pn.kb : p.kb;
+      const char *vbn = lastc ? pn.vb : p.vb;
+      const int lastn = lastc ? pn.last : p.last;
+      int nblk[2];
+      fetch_blocks(btn, cn, lastn, nblk);
+      __builtin_amdgcn_sched_barrier(0);
+
+      // this chunk's K and V rows to LDS, then the next chunk's loads into the
+      // freed registers: a whole chunk stays in flight while this one is computed
+      stage<KSTRIDE>(ks, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
+      __builtin_amdgcn_sched_barrier(0);
+      stage<VSTRIDE>(vs, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 sc[2];
+      Math::scores(qop, [&](int tt, int kb) { return k_operand(tt, kb); }, sc);
+      u32x4 phi, plo;
+      Math::weights(sc, cs, p.last, phi, plo);
+      Math::accumulate(phi, plo, [&](int n) { return vt_operand(n); });
+      cs = cn;
+      blk[0] = nblk[0];
+      blk[1] = nblk[1];
+    }
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) qop[kb] = qn[kb];
+    Math::finish();
+  }
+};
+
+// ---------------------------------------------------------------------------
+// 16-bit caches: rows go from HBM straight into LDS (global_load_lds_dwordx4,
+// no registers on the way), into a per-wavefront ring of four half-chunk
+// slots -- K and V rows of two chunks -- and two query slots.  While chunk c
+// is computed the loads of V(c+1) and K(c+2) go out, so about two chunks of
+// rows are in flight at every wait.  The waits are explicit (vmcnt): every
+// load step issues the same number of instructions (past the range's end it
+// reloads its last chunk into a slot nobody reads), so waiting until at most
+// kAhead instructions are outstanding guarantees the awaited slot has landed;
+// occasional query loads only make that wait stricter.
+//
+// LDS placement: granule g (16 bytes) of row r of a slot sits at granule
+// phys(r, g).  Granules are grouped in 256-byte lines and permuted inside a
+// line by an XOR with a per-line constant, chosen so that the 16 rows of one
+// K operand read fall on 16 different bank groups and the 8 rows that each
+// half of a transposed V read covers fall on 8 different 32-byte bank groups.
+// A DMA instruction fills 1 KB of LDS in lane order, so each lane fetches
+// the global granule that belongs at its LDS position.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <typename MT, int D, int G, int BS>
+struct MfmaRingSeg : MfmaMath<MT, D, G> {
+  using Math = MfmaMath<MT, D, G>;
+  using Math::a;
+  using Math::c16;
+  using Math::j;
+  static constexpr int KS = Math::KS;
+  static constexpr int NT = Math::NT;
+  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
+  static constexpr int RB = 2 * D;                          // bytes per cache row
+  static constexpr int GPR = RB / 16;                       // 16-byte granules per row
+  static constexpr int HB = CT * RB;                        // bytes of a half-chunk slot
+  static constexpr int NLD = HB / 1024;                     // DMA instructions per half-chunk
+  static constexpr int RPI = 1024 / RB;                     // rows per DMA instruction
+  static constexpr int QB = G * RB > 1024 ? G * RB : 1024;  // bytes of a query slot
+  static constexpr int kLdsBytes = 4 * HB + 2 * QB;
+  static constexpr int kAhead = 3 * NLD;  // instructions issued after the half-chunk a wait is for
+  static constexpr int kNontemporal = 2;  // cache-policy operand of the DMA: streaming (nt)
+  static_assert(kLdsBytes * kWavesPerWG <= 160 * 1024, "ring fits the LDS of a CU");
+  static_assert(RPI <= 16 && 16 % RPI == 0, "a DMA instruction stays inside one 16-token tile");
+
+  typedef __attribute__((address_space(3))) void lds_void;
+  __device__ static lds_void *lds_addr(char *p) { return (lds_void *)p; }
+
+  __device__ static int swz(bool isv, int L) { return isv ? 2 * (L & (GPR / 2 - 1)) : (L & (GPR - 1)); }
+  __device__ static int phys(bool isv, int r, int g) {
+    const int q = r * GPR + g, L = q >> 4;
+    return (L << 4) | ((q & 15) ^ swz(isv, L));
+  }
+
+  struct Src {
+    const char *base;  // cache + kv head offset
+    int blk0, blk1;    // block ids of the chunk's two 16-token tiles
+    int cs, last;      // first token of the chunk, last token of its segment
+  };
+
+  char *ring;  // this wavefront's LDS: K0 V0 K1 V1 (HB each), Q0 Q1 (QB each)
+  const int lane;
+  int koff[KS];  // lane byte offset of the K operand of k-step kb, tile 0
+  int voff[NT];  // lane byte offset of the first half of the V^T operand of tile n
+
+  Split sp;  // the launch's split of the work over the workers
+
+  // load cursor: the worker's chunk stream, two chunks ahead of the arithmetic
+  Walker lw;
+  SegInfo ls;
+  bool lhas;
+  int lcs, llast;  // next chunk of ls to load; last token of ls
+  const_i32 *lbt;
+  int nblk[2];  // block ids of chunk lcs
+  int lord;     // non-empty segments whose query has been loaded
+  Src vpend;    // the chunk whose V rows go out next
+  Walker cw;    // the arithmetic's own walk over the same segments
+  int ccnt;     // chunks consumed by the arithmetic (ring slot parity)
+  int cord;     // non-empty segments consumed by the arithmetic (query slot parity)
+  u32x4 qop[KS];
+  // Cut segments whose partial stores are still in flight.  Stores issued
+  // after chunk c's arithmetic have at least kAhead DMA instructions behind
+  // them by the first wait of chunk c + 2, so from there on they are
+  // complete and the partial can be counted without draining the ring.
+  // A range has at most two cut segments (its last and its first), so at
+  // most two are ever pending.
+  struct Pending {
+    int s, kvh;
+    int64_t a0, n;
+    int ready;  // chunk count at whose first wait the stores are complete
+  };
+  Pending p0, p1;  // oldest first
+  int npend;
+
+  __device__ MfmaRingSeg(const DecodeArgs &args, int ln, char *lds)
+      : Math(args, ln), ring(lds), lane(ln), lw(args), cw(args) {
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) koff[kb] = 16 * phys(false, c16, 4 * kb + j);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      voff[n] = 16 * phys(true, 4 * j + (c16 >> 2), 2 * n + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+  }
+
+  __device__ __forceinline__ void fetch_blocks(int cs, int last, int *blk) const {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      int b = lbt[min(cs + 16 * tt, last) >> LOG2BS];
+      blk[tt] = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+    }
+  }
+
+  // the 32 rows of one chunk's K or V into a ring slot
+  template <bool ISV>
+  __device__ __forceinline__ void dma(const Src &src, int64_t sb, int64_t st, char *slot) const {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int P = 64 * i + lane;  // LDS granule this lane fills
+      const int L = P >> 4;
+      const int q = (L << 4) | ((P & 15) ^ swz(ISV, L));
+      const int r = q / GPR, g = q % GPR;
+      const int t = min(src.cs + r, src.last);
+      const int blk = (RPI * i) / 16 ? src.blk1 : src.blk0;
+      const char *bb = src.base + (int64_t)blk * sb * 2;  // uniform block base
+      const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
+      __builtin_amdgcn_global_load_lds(gp, lds_addr(slot + 1024 * i), 16, 0, kNontemporal);
+    }
+  }
+
+  // the G query rows of segment g into a query slot (rows past G in a 1 KB
+  // slot reload row 0)
+  __device__ __forceinline__ void dma_q(const SegInfo &g, char *slot) const {
+#pragma unroll
+    for (int i = 0; i < QB / 1024; ++i) {
+      const int b = 1024 * i + 16 * lane;
+      const int h = b / RB < G ? b / RB : 0;
+      const char *gp = reinterpret_cast<const char *>(a.q) +
+                       ((int64_t)g.s * a.q_ss + (int64_t)(g.kvh * G + h) * a.q_sh + (b % RB) / 2) * 2;
+      __builtin_amdgcn_global_load_lds(gp, lds_addr(slot + 1024 * i), 16, 0, 0);
+    }
+  }
+
+  __device__ __forceinline__ void next_load_seg() {
+    do {
+      lhas = lw.next(ls);
+    } while (lhas && ls.t_hi <= ls.t_lo);
+    if (lhas) {
+      lbt = as_const(a.block_tables) + (int64_t)ls.s * a.bt_ss;
+      lcs = ls.t_lo;
+      llast = ls.t_hi - 1;
+      fetch_blocks(lcs, llast, nblk);
+    }
+  }
+
+  // K rows of the cursor's next chunk (its query first, at a segment's start)
+  // into K slot `par`
+  __device__ __forceinline__ void issue_k(int par) {
+    char *slot = ring + par * 2 * HB;
+    if (lhas) {
+      if (lcs == ls.t_lo) {
+        dma_q(ls, ring + 4 * HB + (lord & 1) * QB);
+        ++lord;
+      }
+      const Src k{reinterpret_cast<const char *>(a.k_cache) + (int64_t)ls.kvh * a.k_sh * 2, nblk[0], nblk[1], lcs,
+                  llast};
+      vpend = Src{reinterpret_cast<const char *>(a.v_cache) + (int64_t)ls.kvh * a.v_sh * 2, nblk[0], nblk[1], lcs,
+                  llast};
+      dma<false>(k, a.k_sb, a.k_st, slot);
+      lcs += CT;
+      if (lcs < ls.t_hi)
+        fetch_blocks(lcs, llast, nblk);
+      else
+        next_load_seg();
+    } else {
+      dma<false>(vpend, a.v_sb, a.v_st, slot);  // nothing left: reload rows into a slot nobody reads
+    }
+  }
+
+  // V rows of the chunk whose K rows went out last, into V slot `par`
+  __device__ __forceinline__ void issue_v(int par) { dma<true>(vpend, a.v_sb, a.v_st, ring + (par * 2 + 1) * HB); }
+
+  // Transposed V reads are issued as inline assembly: the compiler does not
+  // see them as LDS loads, so it adds no wait for the DMA stream (the explicit
+  // vmcnt waits order them), and their completion is awaited explicitly.
+  __device__ static __forceinline__ u32x2 tr_read(const char *p) {
+    u32x2 d;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(d) : "v"((uint32_t)(uintptr_t)p));
+    return d;
+  }
+  template <int N>
+  __device__ static __forceinline__ void lgkm_wait(u32x2 &x0, u32x2 &x1, u32x2 &x2, u32x2 &x3) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3) : "n"(N));
+  }
+
+  // Start on this worker's range [b, e); false if there is nothing to do.
+  __device__ bool start(const Split &split, const Windows &first, int64_t b, int64_t e) {
+    sp = split;
+    ccnt = cord = lord = npend = 0;
+    vpend = Src{reinterpret_cast<const char *>(a.v_cache), 0, 0, 0, 0};  // reloaded when there is nothing left
+    if (!cw.init(first, b, e, lane)) return false;
+    lw = cw;
+    next_load_seg();
+    issue_k(0);
+    issue_v(0);
+    issue_k(1);
+    return true;
+  }
+
+  // the arithmetic's next segment
+  __device__ bool next_segment(SegInfo &g) { return cw.next(g); }
+
+  __device__ __forceinline__ void publish_front() {
+    publish_partial<MT, G, D>(a, p0.s, p0.kvh, p0.a0, p0.n, sp, lane);
+    p0 = p1;
+    --npend;
+  }
+
+  __device__ void publish(const SegInfo &g) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the partial's stores stay ahead of the next loads
+    const Pending p{g.s, g.kvh, g.a0, g.n, ccnt + 1};
+    if (npend == 0)
+      p0 = p;
+    else
+      p1 = p;
+    ++npend;
+  }
+
+  // no DMA may land after the wavefront's LDS is released; then count what is left
+  __device__ void end() {
+    wait_vm<0>();
+    while (npend > 0) publish_front();
+  }
+
+  __device__ void run(const SegInfo &g) {
+    Math::reset();
+    if (g.t_hi <= g.t_lo) return;  // only if context_lens changed under the launch
+    const int last = g.t_hi - 1;
+    const int nch = (g.t_hi - g.t_lo + CT - 1) / CT;
+    int cs = g.t_lo;
+    for (int c = 0; c < nch; ++c) {
+      const int par = ccnt & 1;
+      issue_v(par ^ 1);  // V(c+1)
+      wait_vm<kAhead>();  // K rows of this chunk (and, before them, the segment's query) have landed
+      __builtin_amdgcn_sched_barrier(0);
+      if (npend > 0 && p0.ready <= ccnt) {  // one per chunk; a second waits for the next
+        publish_front();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c == 0) {
+        const char *qs = ring + 4 * HB + (cord & 1) * QB + (c16 < G ? c16 : 0) * RB;
+#pragma unroll
+        for (int kb = 0; kb < KS; ++kb) {
+          qop[kb] = ld16(qs + (4 * kb + j) * 16);
+          if (c16 >= G) qop[kb] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      const char *ks = ring + par * 2 * HB;
+      u32x4 kop[2][KS];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KS; ++kb) kop[tt][kb] = ld16(ks + koff[kb] + tt * 16 * RB);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 sc[2];
+      Math::scores(qop, [&](int tt, int kb) { return kop[tt][kb]; }, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_k(par);  // K(c+2), into the slot just read
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 phi, plo;
+      Math::weights(sc, cs, last, phi, plo);
+      wait_vm<kAhead>();  // V rows of this chunk
+      __builtin_amdgcn_sched_barrier(0);
+      const char *vs = ring + (par * 2 + 1) * HB;
+      // two tiles of transposed reads in flight ahead of the tiles being multiplied
+      u32x2 vt[NT][2];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        vt[n][0] = tr_read(vs + voff[n]);
+        vt[n][1] = tr_read(vs + voff[n] + 16 * RB);
+      }
+#pragma unroll
+      for (int n = 0; n < NT; n += 2) {
+        // reads issued after tiles n, n+1: those of tiles n+2, n+3, if any
+        if (n + 3 < NT)
+          lgkm_wait<4>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
+        else
+          lgkm_wait<0>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
+        if (n + 4 < NT) {
+          vt[n + 4][0] = tr_read(vs + voff[n + 4]);
+          vt[n + 4][1] = tr_read(vs + voff[n + 4] + 16 * RB);
+          vt[n + 5][0] = tr_read(vs + voff[n + 5]);
+          vt[n + 5][1] = tr_read(vs + voff[n + 5] + 16 * RB);
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const u32x4 op{vt[n + d][0][0], vt[n + d][0][1], vt[n + d][1][0], vt[n + d][1][1]};
+          Math::acc[n + d] = Op<MT>::mma(op, phi, Math::acc[n + d]);
+          Math::acc[n + d] = Op<MT>::mma(op, plo, Math::acc[n + d]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      cs += CT;
+      ++ccnt;
+    }
+    ++cord;
+    Math::finish();
+  }
+};
+
+// One worker of the ring kernel: its range, segment by segment; the
+// segment owns both walks over it (loads ahead, arithmetic behind).
+template <typename MT, int G, int D, class Seg>
+__device__ void run_ring_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+  Windows first;
+  const Split sp = make_split(count_units<MT>(a, w, W, lane, first), W);
+  if (w >= sp.Ws) return;
+  if (!seg.start(sp, first, sp.begin(w), sp.begin(w + 1))) return;
+  SegInfo cur;
+  while (seg.next_segment(cur)) {
+    seg.run(cur);
+    if (cur.u_lo == 0 && cur.u_hi == cur.n) {
+      seg.write_out(cur.s, cur.kvh);
+    } else {
+      seg.write_partial(cur.first ? 2 * (int64_t)w : 2 * (int64_t)w + 1);
+      seg.publish(cur);
+    }
+  }
+  seg.end();
+}
+
+template <typename KVT, typename MT, int D, int G, int BS>
+struct SegFor {
+  typedef MfmaRegSeg<KVT, MT, D, G, BS> type;
+  __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
+    run_worker<MT, G, D>(a, w, W, lane, seg);
+  }
+};
+template <typename MT, int D, int G, int BS>
+struct SegFor<MT, MT, D, G, BS> {
+  typedef MfmaRingSeg<MT, D, G, BS> type;
+  __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
+    run_ring_worker<MT, G, D>(a, w, W, lane, seg);
+  }
+};
+
 template <typename KVT, typename MT, int D, int G, int BS>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
-  __shared__ uint16_t kstage[kWavesPerWG][CT * (D + 8)];
-  __shared__ uint16_t vstage[kWavesPerWG][CT * (D + 16)];
+  typedef typename SegFor<KVT, MT, D, G, BS>::type Seg;
+  __shared__ __attribute__((aligned(1024))) char lds[kWavesPerWG][Seg::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   // workgroups are dealt to the 8 XCDs round-robin; number them so that each
   // XCD's workers hold one contiguous stretch of the work order
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  MfmaSeg<KVT, MT, D, G, BS> seg(a, lane, kstage[wave], vstage[wave]);
-  run_worker<MT, G, D>(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
+  Seg seg(a, lane, lds[wave]);
+  SegFor<KVT, MT, D, G, BS>::run(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
 template <typename KVT, typename MT, int D, int G>

@@ -224,6 +224,12 @@ struct ValuSeg {
 
   // q, block ids and the K / V loads of g's first chunk; K before V, so that
   // the first wait of the chunk loop is for K alone
+  __device__ void begin(const SegInfo &g, const Walker &) { begin(g); }
+  __device__ void publish(const SegInfo &g, const Split &sp) {
+    finish_partial<QT, G, D>(a, g.s, g.kvh, g.a0, g.n, sp, lane);
+  }
+  __device__ void end() {}
+
   __device__ void begin(const SegInfo &g) {
     const Ptrs p = ptrs(g);
     load_q(g, q);

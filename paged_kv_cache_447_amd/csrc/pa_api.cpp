@@ -104,10 +104,11 @@ struct WsLayout {
 WsLayout workspace_layout(int64_t S, int64_t H, int64_t Hkv, int64_t D, int64_t W) {
   WsLayout l;
   const int64_t G = H / Hkv;
+  const int64_t slots = 2 * W;
   l.counters = 0;
   l.ml = (size_t)round_up(S * Hkv * 4, 256);
-  l.acc = l.ml + (size_t)round_up(2 * W * G * 2 * 4, 256);
-  l.total = l.acc + (size_t)round_up(2 * W * G * D * 4, 256);
+  l.acc = l.ml + (size_t)round_up(slots * G * 2 * 4, 256);
+  l.total = l.acc + (size_t)round_up(slots * G * D * 4, 256);
   return l;
 }
 

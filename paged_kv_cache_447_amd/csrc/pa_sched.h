@@ -50,11 +50,21 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// First unit of worker w's range, and the worker whose range holds unit x
-// (all ranges are non-empty because the launch never uses more workers than
-// units).
-__device__ __forceinline__ int64_t range_begin(int64_t w, int64_t T, int64_t W) { return w * T / W; }
-__device__ __forceinline__ int64_t unit_owner(int64_t x, int64_t T, int64_t W) { return ((x + 1) * W - 1) / T; }
+// The split of the unit order [0, T) into Ws = min(T, W) equal ranges, range
+// w worked by worker w (never more ranges than units, so none is empty).
+struct Split {
+  int64_t T, Ws;
+  // first unit of range p, and the range that holds unit x
+  __device__ __forceinline__ int64_t begin(int64_t p) const { return p * T / Ws; }
+  __device__ __forceinline__ int64_t owner(int64_t x) const { return ((x + 1) * Ws - 1) / T; }
+};
+
+__device__ __forceinline__ Split make_split(int64_t T, int64_t W) {
+  Split sp;
+  sp.T = T;
+  sp.Ws = T < W ? T : W;
+  return sp;
+}
 
 // A window of 64 consecutive sequences: units per sequence and their prefix sums.
 struct SeqWindow {
@@ -74,6 +84,34 @@ __device__ __forceinline__ SeqWindow load_window(const DecodeArgs &a, int s0, in
   win.incl = wave_incl_scan(win.n, lane);
   win.total = uniform(__shfl(win.incl, 63));
   return win;
+}
+
+// The first kWin windows (sequences 0 .. 64 kWin - 1), loaded together when a
+// worker starts; windows past them are loaded one by one when needed.
+constexpr int kWin = 4;
+struct Windows {
+  SeqWindow w[kWin];
+  int nw;  // windows held: min(kWin, ceil(num_seqs / 64))
+};
+
+__device__ __forceinline__ void load_windows(const DecodeArgs &a, int lane, Windows &ws) {
+  int L[kWin];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {  // all loads in flight together
+    const int s = 64 * i + lane;
+    L[i] = s < a.num_seqs ? clamp_ctx(a.context_lens[s], a.max_ctx) : 0;
+  }
+  ws.nw = 0;
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    SeqWindow &win = ws.w[i];
+    win.s0 = 64 * i;
+    win.L = L[i];
+    win.n = (win.L + a.part_tokens - 1) / a.part_tokens;
+    win.incl = wave_incl_scan(win.n, lane);
+    win.total = uniform(__shfl(win.incl, 63));
+    if (64 * i < a.num_seqs) ws.nw = i + 1;
+  }
 }
 
 // Per-segment partial result layout in the workspace.
@@ -104,18 +142,19 @@ __device__ __forceinline__ void store_elem(const DecodeArgs &a, int64_t idx, flo
 }
 
 // Merge the segments of item (s, kvh) whose units start at a0 (n units): the
-// caller is the last of its workers to finish.  One pass over the partials,
-// folding each into a running (M, L, O) per output element; the loads of
-// partial i+1 are in flight while partial i is folded in, so a merge costs
-// about one memory round trip per partial.  Lane l owns elements l + 64 k of
-// the [G][D] block, whose head (64 k) / D is the same for the whole wave.
+// caller is the last of its workers to finish.  The partials are read in
+// batches of up to PB, all loads of a batch in flight together, and folded
+// into a running (M, L, O) per output element, so a merge costs about one
+// memory round trip per batch.  Lane l owns elements l + 64 k of the [G][D]
+// block, whose head (64 k) / D is the same for the whole wave.
 template <typename QT, int G, int D>
-__device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, int64_t T, int64_t W,
-                           int lane) {
+__device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, const Split &sp, int lane) {
   constexpr int EPL = G * D / 64;
+  constexpr int PB0 = 64 / (EPL + 2);
+  constexpr int PB = PB0 < 1 ? 1 : (PB0 > 8 ? 8 : PB0);  // partials per batch: about 64 registers of loads
   static_assert((G * D) % 64 == 0 && D % 64 == 0, "a wave covers whole heads");
-  const int64_t w0 = unit_owner(a0, T, W), w1 = unit_owner(a0 + n - 1, T, W);
-  const bool first_is_last = range_begin(w0, T, W) < a0;  // w0 began in an earlier item
+  const int64_t w0 = sp.owner(a0), w1 = sp.owner(a0 + n - 1);
+  const bool first_is_last = sp.begin(w0) < a0;  // range w0 began in an earlier item
   const int cnt = (int)(w1 - w0 + 1);
   float M[EPL], L[EPL], O[EPL];
 #pragma unroll
@@ -124,37 +163,36 @@ __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int6
     L[k] = 0.0f;
     O[k] = 0.0f;
   }
-  float cm = 0.0f, cl = 0.0f, cacc[EPL];
-  auto load = [&](int i, float &m_, float &l_, float *acc_) {
-    const int64_t wi = w0 + i;
-    const int64_t slot = (i == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
-    const float *ml = slot_ml<G>(a, slot);
-    const int g = lane < G ? lane : 0;
-    m_ = load_shared(ml + 2 * g);
-    l_ = load_shared(ml + 2 * g + 1);
-    const float *pacc = slot_acc<G, D>(a, slot);
+  for (int i0 = 0; i0 < cnt; i0 += PB) {
+    float bm[PB], bl[PB], bacc[PB][EPL];
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) acc_[k] = load_shared(pacc + lane + 64 * k);
-  };
-  load(0, cm, cl, cacc);
-  for (int i = 0; i < cnt; ++i) {
-    float nm = 0.0f, nl = 0.0f, nacc[EPL];
-    if (i + 1 < cnt) load(i + 1, nm, nl, nacc);
+    for (int b = 0; b < PB; ++b) {
+      if (i0 + b >= cnt) break;
+      const int64_t wi = w0 + i0 + b;
+      const int64_t slot = (i0 + b == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
+      const float *ml = slot_ml<G>(a, slot);
+      const int g = lane < G ? lane : 0;
+      bm[b] = load_shared(ml + 2 * g);
+      bl[b] = load_shared(ml + 2 * g + 1);
+      const float *pacc = slot_acc<G, D>(a, slot);
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const int g = (64 * k) / D;
-      const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cm), g));
-      const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cl), g));
-      const float mn = fmaxf(M[k], mi);
-      const float f0 = fast_exp2(M[k] - mn), f1 = fast_exp2(mi - mn);
-      L[k] = L[k] * f0 + li * f1;
-      O[k] = O[k] * f0 + cacc[k] * f1;
-      M[k] = mn;
+      for (int k = 0; k < EPL; ++k) bacc[b][k] = load_shared(pacc + lane + 64 * k);
     }
-    cm = nm;
-    cl = nl;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) cacc[k] = nacc[k];
+    for (int b = 0; b < PB; ++b) {
+      if (i0 + b >= cnt) break;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        const int g = (64 * k) / D;
+        const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm[b]), g));
+        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl[b]), g));
+        const float mn = fmaxf(M[k], mi);
+        const float f0 = fast_exp2(M[k] - mn), f1 = fast_exp2(mi - mn);
+        L[k] = L[k] * f0 + li * f1;
+        O[k] = O[k] * f0 + bacc[b][k] * f1;
+        M[k] = mn;
+      }
+    }
   }
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
@@ -164,27 +202,33 @@ __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int6
   }
 }
 
-// Publish a segment's partial (already stored by the caller to `slot`) and,
-// if this worker is the item's last, merge.  Returns nothing; all lanes call.
+// Count a segment's partial (already stored by the caller to its slot, and
+// those stores complete) and, if it is the item's last, merge.  All lanes call.
 template <typename QT, int G, int D>
-__device__ __forceinline__ void finish_partial(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, int64_t T,
-                                               int64_t W, int lane) {
-  const int64_t w0 = unit_owner(a0, T, W), w1 = unit_owner(a0 + n - 1, T, W);
+__device__ __forceinline__ void publish_partial(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n,
+                                                const Split &sp, int lane) {
+  const int64_t w0 = sp.owner(a0), w1 = sp.owner(a0 + n - 1);
   const int cnt = (int)(w1 - w0 + 1);
   int32_t *ctr = a.counters + (int64_t)s * a.num_kv_heads + kvh;
-  // the partial's write-through stores are complete before the count goes up
-  // (the signal fences keep the compiler from moving memory operations across)
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   int old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = uniform(__shfl(old, 0));
   if (old == cnt - 1) {
     // every other segment's count, hence its stores, came before ours
-    merge_item<QT, G, D>(a, s, kvh, a0, n, T, W, lane);
+    merge_item<QT, G, D>(a, s, kvh, a0, n, sp, lane);
     if (lane == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Wait for the partial's write-through stores, then count it (the signal
+// fences keep the compiler from moving memory operations across the wait).
+template <typename QT, int G, int D>
+__device__ __forceinline__ void finish_partial(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n,
+                                               const Split &sp, int lane) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  publish_partial<QT, G, D>(a, s, kvh, a0, n, sp, lane);
 }
 
 // Zero the output rows of sequences with an empty context (sequence s is
@@ -213,18 +257,10 @@ struct UnitPos {
   int64_t item0;
 };
 
-// Find unit x (x < T) scanning the windows from the first one (`first` is the
-// already loaded window of sequences 0..63).  Returns false only if the
-// context lengths changed under the launch.
-__device__ __forceinline__ bool locate(const DecodeArgs &a, const SeqWindow &first, int64_t x, int lane,
-                                       UnitPos &p) {
-  int64_t base = 0;  // units (all kv heads) of the sequences before the window
-  SeqWindow win = first;
-  while (x >= base + (int64_t)win.total * a.num_kv_heads) {
-    if (win.s0 + 64 >= a.num_seqs) return false;
-    base += (int64_t)win.total * a.num_kv_heads;
-    win = load_window(a, win.s0 + 64, lane);
-  }
+// Unit x of window `win`, whose first unit is base + (units of its earlier
+// sequences); false if x is not in it.
+__device__ __forceinline__ bool locate_in(const DecodeArgs &a, const SeqWindow &win, int64_t base, int64_t x,
+                                          UnitPos &p) {
   const int64_t lo = base + (int64_t)(win.incl - win.n) * a.num_kv_heads;
   const int64_t hi = base + (int64_t)win.incl * a.num_kv_heads;
   const uint64_t hit = __ballot(win.n > 0 && lo <= x && x < hi);
@@ -235,6 +271,27 @@ __device__ __forceinline__ bool locate(const DecodeArgs &a, const SeqWindow &fir
   p.L = uniform(__shfl(win.L, ls));
   p.item0 = base + (int64_t)uniform(__shfl(win.incl - win.n, ls)) * a.num_kv_heads;
   return true;
+}
+
+// Find unit x (x < T): the held windows first, then the windows after them.
+// Returns false only if the context lengths changed under the launch.
+__device__ __forceinline__ bool locate(const DecodeArgs &a, const Windows &ws, int64_t x, int lane, UnitPos &p) {
+  int64_t base = 0;  // units (all kv heads) of the sequences before the window
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    if (i < ws.nw) {
+      const int64_t units = (int64_t)ws.w[i].total * a.num_kv_heads;
+      if (x < base + units) return locate_in(a, ws.w[i], base, x, p);
+      base += units;
+    }
+  }
+  for (int s0 = 64 * ws.nw; s0 < a.num_seqs; s0 += 64) {
+    const SeqWindow win = load_window(a, s0, lane);
+    const int64_t units = (int64_t)win.total * a.num_kv_heads;
+    if (x < base + units) return locate_in(a, win, base, x, p);
+    base += units;
+  }
+  return false;
 }
 
 // One segment of a worker's range: units [u_lo, u_hi) of item (s, kvh), as
@@ -252,17 +309,18 @@ struct SegInfo {
 // and w+1 is then the first or second thing both of them do, so its merge
 // happens early in the launch instead of in its tail.
 struct Walker {
-  const DecodeArgs &a;
+  const DecodeArgs *ap;
   int64_t b, e, a0_b, end_b, a0_e;
   UnitPos pb, pe, p;
   int kvh_b, kvh_e, kvh;
   int stage;  // 0: last segment next, 1: first segment next, 2: whole items, 3: done
   int64_t x;  // next unit of stage 2
 
-  __device__ Walker(const DecodeArgs &args) : a(args) {}
+  __device__ explicit Walker(const DecodeArgs &args) : ap(&args) {}
 
   // false if there is nothing to do (or context_lens changed under the launch)
-  __device__ bool init(const SeqWindow &first, int64_t b_, int64_t e_, int lane) {
+  __device__ bool init(const Windows &first, int64_t b_, int64_t e_, int lane) {
+    const DecodeArgs &a = *ap;
     b = b_;
     e = e_;
     if (!locate(a, first, b, lane, pb)) return false;
@@ -280,6 +338,7 @@ struct Walker {
   }
 
   __device__ void fill(SegInfo &g, const UnitPos &q, int kv, int u_lo, int u_hi, bool is_first) const {
+    const DecodeArgs &a = *ap;
     g.s = q.s;
     g.kvh = kv;
     g.u_lo = u_lo;
@@ -292,6 +351,7 @@ struct Walker {
   }
 
   __device__ bool next(SegInfo &g) {
+    const DecodeArgs &a = *ap;
     if (stage == 0) {
       fill(g, pe, kvh_e, 0, (int)(e - a0_e), false);
       stage = 1;
@@ -329,46 +389,65 @@ struct Walker {
 };
 
 // Drive one worker through its range.  Seg must provide
-//   void begin(const SegInfo &g)                            -- issue the loads of g's first chunk
+//   void begin(const SegInfo &g, const Walker &from)        -- issue the loads of g's first chunk(s);
+//       `from` yields the worker's segments from g on, for loads that run
+//       more than one segment ahead
 //   void run(const SegInfo &g, const SegInfo &nx, bool has) -- attend over g's tokens (its first chunk
 //       already in flight); while on g's last chunk, issue nx's first chunk if `has`
 //   void write_out(int s, int kvh)                          -- normalised output of a whole item
 //   void write_partial(int64_t slot)                        -- partial (m, l, acc) to a slot
+//   void publish(const SegInfo &g, const Split &sp)         -- count g's partial (finish_partial, now or
+//       once its stores are known complete)
+//   void end()                                              -- after the last segment (publishes what is left)
 // All lanes of the wave call every function; all control flow is uniform.
 // The load pipeline thus runs on from one segment into the next.
-template <typename QT, int G, int D, class Seg>
-__device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
-  // total units T; zero the outputs of empty sequences
+// Total units T of the launch (all kv heads); zeroes the outputs of empty
+// sequences on the way.
+template <typename QT>
+__device__ int64_t count_units(const DecodeArgs &a, int w, int W, int lane, Windows &first) {
   int64_t T = 0;
-  const SeqWindow first = load_window(a, 0, lane);
-  for (SeqWindow win = first;;) {
+  load_windows(a, lane, first);
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) {
+    if (i < first.nw) {
+      zero_empty_sequences<QT>(a, first.w[i], w, W, lane);
+      T += (int64_t)first.w[i].total;
+    }
+  }
+  for (int s0 = 64 * first.nw; s0 < a.num_seqs; s0 += 64) {
+    const SeqWindow win = load_window(a, s0, lane);
     zero_empty_sequences<QT>(a, win, w, W, lane);
     T += (int64_t)win.total;
-    if (win.s0 + 64 >= a.num_seqs) break;
-    win = load_window(a, win.s0 + 64, lane);
   }
-  T *= a.num_kv_heads;
-  const int64_t Wn = T < (int64_t)W ? T : (int64_t)W;  // never more workers than units
-  if (w >= Wn) return;
+  return T * a.num_kv_heads;
+}
+
+template <typename QT, int G, int D, class Seg>
+__device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+  Windows first;
+  const Split sp = make_split(count_units<QT>(a, w, W, lane, first), W);
+  if (w >= sp.Ws) return;
 
   Walker walk(a);
-  if (!walk.init(first, range_begin(w, T, Wn), range_begin(w + 1, T, Wn), lane)) return;
+  if (!walk.init(first, sp.begin(w), sp.begin(w + 1), lane)) return;
+  const Walker from = walk;
   SegInfo cur, nx;
   if (!walk.next(cur)) return;
+  seg.begin(cur, from);
   bool has = walk.next(nx);
-  seg.begin(cur);
   while (true) {
     seg.run(cur, nx, has);
     if (cur.u_lo == 0 && cur.u_hi == cur.n) {
       seg.write_out(cur.s, cur.kvh);
     } else {
       seg.write_partial(cur.first ? 2 * (int64_t)w : 2 * (int64_t)w + 1);
-      finish_partial<QT, G, D>(a, cur.s, cur.kvh, cur.a0, cur.n, T, Wn, lane);
+      seg.publish(cur, sp);
     }
-    if (!has) return;
+    if (!has) break;
     cur = nx;
     has = walk.next(nx);
   }
+  seg.end();
 }
 
 }  // namespace pa

@@ -107,8 +107,38 @@ def test_small_cases_match_oracle(case, split):
     assert err <= TOL_OUT[cfg.kv_dtype]
     assert err32 <= TOL_F32[cfg.kv_dtype]
     # every call leaves the merge counters at zero for the next one
-    S, Hkv = cfg.num_seqs, cfg.num_kv_heads
+    assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
+
+
+def assert_counters_zero(ws, S, Hkv):
     assert int(ws[: 4 * S * Hkv].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name,G,kv_dtype,workers", [("gqa70b", 8, "f16", 64), ("gqa70b", 4, "bf16", 100),
+                                                     ("gqa70b", 16, "f16", 32), ("gqa70b", 8, "f16", 0)])
+def test_few_workers_match_oracle_and_repeat_exactly(name, G, kv_dtype, workers):
+    """Grouped-query shapes on the matrix-core path with few workers for the
+    work (long ranges, many segments each, deferred publication of cut
+    segments): the results match the oracle, repeat bit for bit, and the merge
+    counters are back at zero after every call."""
+    cfg = scaled(get_config(name), num_seqs=24)
+    cfg = scaled(cfg, num_heads=cfg.num_kv_heads * G, kv_dtype=kv_dtype, q_dtype=kv_dtype)
+    log(f"[{name} G={G} {kv_dtype} workers={workers}]")
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    gpu_cache_write(cfg, inp)
+    ref, _, _ = oracle_step(cfg, host)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads, workers)
+    outs = []
+    for _ in range(3):
+        outs.append(gpu_decode(cfg, inp, out_dtype=torch.float32, num_workers=workers, workspace=ws))
+        torch.cuda.synchronize()
+        assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
+    e = max_abs_err(outs[0], ref)
+    log(f"    err32={e:.3e}")
+    assert e <= TOL_F32[cfg.kv_dtype]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
 
 
 @pytest.mark.parametrize("name", ["llama7b", "gqa70b", "fp8_long"])
