@@ -502,19 +502,6 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   int ccnt;     // chunks consumed by the arithmetic (ring slot parity)
   int cord;     // non-empty segments consumed by the arithmetic (query slot parity)
   u32x4 qop[KS];
-  // Cut segments whose partial stores are still in flight.  Stores issued
-  // after chunk c's arithmetic have at least kAhead DMA instructions behind
-  // them by the first wait of chunk c + 2, so from there on they are
-  // complete and the partial can be counted without draining the ring.
-  // A range has at most two cut segments (its last and its first), so at
-  // most two are ever pending.
-  struct Pending {
-    int s, kvh;
-    int64_t a0, n;
-    int ready;  // chunk count at whose first wait the stores are complete
-  };
-  Pending p0, p1;  // oldest first
-  int npend;
 
   __device__ MfmaRingSeg(const DecodeArgs &args, int ln, char *lds)
       : Math(args, ln), ring(lds), lane(ln), lw(args), cw(args) {
@@ -618,7 +605,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   // Start on this worker's range [b, e); false if there is nothing to do.
   __device__ bool start(const Split &split, const Windows &first, int64_t b, int64_t e) {
     sp = split;
-    ccnt = cord = lord = npend = 0;
+    ccnt = cord = lord = 0;
     vpend = Src{reinterpret_cast<const char *>(a.v_cache), 0, 0, 0, 0};  // reloaded when there is nothing left
     if (!cw.init(first, b, e, lane)) return false;
     lw = cw;
@@ -632,27 +619,14 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   // the arithmetic's next segment
   __device__ bool next_segment(SegInfo &g) { return cw.next(g); }
 
-  __device__ __forceinline__ void publish_front() {
-    publish_partial<MT, G, D>(a, p0.s, p0.kvh, p0.a0, p0.n, sp, lane);
-    p0 = p1;
-    --npend;
-  }
+  // Count a cut segment's partial.  Its write-through stores must be
+  // complete first, and a vmcnt count cannot tell stores from the DMA loads
+  // issued after them (loads and stores may complete out of order), so this
+  // waits for everything outstanding.
+  __device__ void publish(const SegInfo &g) { finish_partial<MT, G, D>(a, g.s, g.kvh, g.a0, g.n, sp, lane); }
 
-  __device__ void publish(const SegInfo &g) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // the partial's stores stay ahead of the next loads
-    const Pending p{g.s, g.kvh, g.a0, g.n, ccnt + 1};
-    if (npend == 0)
-      p0 = p;
-    else
-      p1 = p;
-    ++npend;
-  }
-
-  // no DMA may land after the wavefront's LDS is released; then count what is left
-  __device__ void end() {
-    wait_vm<0>();
-    while (npend > 0) publish_front();
-  }
+  // no DMA may land after the wavefront's LDS is released
+  __device__ void end() { wait_vm<0>(); }
 
   __device__ void run(const SegInfo &g) {
     Math::reset();
@@ -665,10 +639,6 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       issue_v(par ^ 1);  // V(c+1)
       wait_vm<kAhead>();  // K rows of this chunk (and, before them, the segment's query) have landed
       __builtin_amdgcn_sched_barrier(0);
-      if (npend > 0 && p0.ready <= ccnt) {  // one per chunk; a second waits for the next
-        publish_front();
-        __builtin_amdgcn_sched_barrier(0);
-      }
       if (c == 0) {
         const char *qs = ring + 4 * HB + (cord & 1) * QB + (c16 < G ? c16 : 0) * RB;
 #pragma unroll

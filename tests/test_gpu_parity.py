@@ -118,9 +118,9 @@ def assert_counters_zero(ws, S, Hkv):
                                                      ("gqa70b", 16, "f16", 32), ("gqa70b", 8, "f16", 0)])
 def test_few_workers_match_oracle_and_repeat_exactly(name, G, kv_dtype, workers):
     """Grouped-query shapes on the matrix-core path with few workers for the
-    work (long ranges, many segments each, deferred publication of cut
-    segments): the results match the oracle, repeat bit for bit, and the merge
-    counters are back at zero after every call."""
+    work (long ranges, many segments each, the load ring running across
+    segment boundaries): the results match the oracle, repeat bit for bit, and
+    the merge counters are back at zero after every call."""
     cfg = scaled(get_config(name), num_seqs=24)
     cfg = scaled(cfg, num_heads=cfg.num_kv_heads * G, kv_dtype=kv_dtype, q_dtype=kv_dtype)
     log(f"[{name} G={G} {kv_dtype} workers={workers}]")
