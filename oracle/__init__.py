@@ -60,6 +60,8 @@ def _load():
             i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
             lib.oracle_paged_decode.restype = i32
             lib.oracle_paged_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp] + [i64] * 7 + [dbl] * 3 + [i32]
+            lib.oracle_paged_prefill.restype = i32
+            lib.oracle_paged_prefill.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp] + [i64] * 7 + [dbl] * 3 + [i32]
             lib.oracle_cache_write.restype = i32
             lib.oracle_cache_write.argtypes = [vp, vp, i32, vp, vp, i32, vp] + [i64] * 5 + [ctypes.c_float] * 2
             lib.oracle_f16_to_double.restype = dbl
@@ -118,6 +120,37 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
                                  float(scale), float(k_scale), float(v_scale), int(nthreads))
     if rc != 0:
         raise OracleError(f"oracle_paged_decode: {STATUS.get(rc, rc)}")
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
+                  num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1) -> np.ndarray:
+    """Reference prefill (causal, the query rows of sequence s being its newest
+    query_start_loc[s+1] - query_start_loc[s] tokens); returns float64
+    [num_query_rows, num_heads, head_dim]."""
+    import torch
+
+    lib = _load()
+    q, k_cache, v_cache = _host(q), _host(k_cache), _host(v_cache)
+    bt = _host(block_tables, torch.int32)
+    cl = _host(context_lens, torch.int32)
+    qsl = _host(query_start_loc, torch.int32)
+    N, H, D = q.shape
+    NB, bs, Hkv, Dk = k_cache.shape
+    S = cl.shape[0]
+    if Hkv != num_kv_heads or Dk != D or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("cache shape does not match q / num_kv_heads")
+    if k_cache.dtype != v_cache.dtype:
+        raise ValueError("k_cache and v_cache dtypes differ")
+    if qsl.shape[0] != S + 1 or int(qsl[-1]) != N:
+        raise ValueError("query_start_loc must have num_seqs + 1 entries ending at the query row count")
+    W = bt.shape[1] if bt.dim() == 2 else 0
+    out = np.empty((N, H, D), dtype=np.float64)
+    rc = lib.oracle_paged_prefill(out.ctypes.data, q.data_ptr(), _code(q), k_cache.data_ptr(), v_cache.data_ptr(),
+                                  _code(k_cache), bt.data_ptr(), cl.data_ptr(), qsl.data_ptr(), S, H, Hkv, D, NB,
+                                  bs, W, float(scale), float(k_scale), float(v_scale), int(nthreads))
+    if rc != 0:
+        raise OracleError(f"oracle_paged_prefill: {STATUS.get(rc, rc)}")
     return out
 
 

@@ -27,6 +27,13 @@
  *     显存实战", closing paragraph on FP8 KV caches).
  *   - The cache write puts the K/V row of new token n at slot_mapping[n], slot
  *     = block * block_size + offset, and skips negative slots.
+ *   - Prefill (several query tokens per sequence): the query rows of sequence
+ *     s are rows query_start_loc[s] .. query_start_loc[s+1]-1 of q (the first
+ *     page's kernel interface takes a num_tokens-long query), and they are the
+ *     sequence's newest tokens, already in the cache: with q_len of them in a
+ *     context of context_lens[s], query j sits at position context_lens[s] -
+ *     q_len + j and attends to the tokens at positions 0 .. that position
+ *     (causal order, as every token of an autoregressive prompt).
  *
  * Arithmetic: every stored value is decoded exactly to double; the gather,
  * dot products, softmax (two passes: max, then exp and sum) and the weighted
@@ -289,6 +296,156 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
     for (; started < nthreads; ++started)
       if (pthread_create(&th[started], NULL, decode_worker, &J) != 0) break;
     if (started == 0) decode_worker(&J);
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    free(th);
+  }
+  pthread_mutex_destroy(&J.lock);
+  return J.status;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* prefill: several query tokens per sequence, causal */
+
+typedef struct {
+  double *out;
+  const void *q;
+  int q_dtype;
+  const void *k_cache, *v_cache;
+  int kv_dtype;
+  const int32_t *block_tables, *context_lens, *query_start_loc;
+  int64_t num_seqs, num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks;
+  double scale, k_scale, v_scale;
+  int64_t next_item;
+  pthread_mutex_t lock;
+  int status;
+} prefill_job;
+
+/* One (sequence, kv head): gather the context's K and V rows in logical order
+ * once, then for every query token of the sequence and every query head that
+ * reads this kv head, attend over the positions up to the token's own. */
+static int prefill_item(prefill_job *J, int64_t seq, int64_t kvh, double *Kc, double *Vc, double *w) {
+  const int64_t D = J->head_dim, H = J->num_heads, Hkv = J->num_kv_heads, bs = J->block_size;
+  const int64_t G = H / Hkv;
+  const int64_t L = J->context_lens[seq];
+  const int64_t r0 = J->query_start_loc[seq], r1 = J->query_start_loc[seq + 1];
+  const int64_t nq = r1 - r0;
+  if (L < 0 || nq < 0 || nq > L) return ORC_BAD_ARG;
+  if (nq == 0) return ORC_OK;
+  if ((L + bs - 1) / bs > J->max_blocks) return ORC_CTX_TOO_LONG;
+  const double ks = (J->kv_dtype == ORC_FP8) ? J->k_scale : 1.0;
+  const double vs = (J->kv_dtype == ORC_FP8) ? J->v_scale : 1.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const int64_t blk = J->block_tables[seq * J->max_blocks + t / bs];
+    if (blk < 0 || blk >= J->num_blocks) return ORC_BAD_BLOCK;
+    const int64_t src = ((blk * bs + t % bs) * Hkv + kvh) * D;
+    for (int64_t d = 0; d < D; ++d) {
+      Kc[t * D + d] = load_elem(J->k_cache, J->kv_dtype, src + d) * ks;
+      Vc[t * D + d] = load_elem(J->v_cache, J->kv_dtype, src + d) * vs;
+    }
+  }
+  for (int64_t j = 0; j < nq; ++j) {
+    const int64_t pos = L - nq + j; /* this query token's own position */
+    const int64_t n = pos + 1;      /* it sees positions 0 .. pos */
+    for (int64_t g = 0; g < G; ++g) {
+      const int64_t row = ((r0 + j) * H + kvh * G + g) * D;
+      double mx = -INFINITY;
+      for (int64_t t = 0; t < n; ++t) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += load_elem(J->q, J->q_dtype, row + d) * Kc[t * D + d];
+        w[t] = J->scale * dot;
+        if (w[t] > mx) mx = w[t];
+      }
+      double sum = 0.0;
+      for (int64_t t = 0; t < n; ++t) {
+        w[t] = exp(w[t] - mx);
+        sum += w[t];
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double a = 0.0;
+        for (int64_t t = 0; t < n; ++t) a += w[t] * Vc[t * D + d];
+        J->out[row + d] = a / sum;
+      }
+    }
+  }
+  return ORC_OK;
+}
+
+static void *prefill_worker(void *arg) {
+  prefill_job *J = (prefill_job *)arg;
+  const int64_t cap = J->max_blocks * J->block_size;
+  double *Kc = (double *)malloc(sizeof(double) * (size_t)(cap * J->head_dim + 1));
+  double *Vc = (double *)malloc(sizeof(double) * (size_t)(cap * J->head_dim + 1));
+  double *w = (double *)malloc(sizeof(double) * (size_t)(cap + 1));
+  int err = (Kc && Vc && w) ? ORC_OK : ORC_NO_MEMORY;
+  const int64_t n_items = J->num_seqs * J->num_kv_heads;
+  while (!err) {
+    pthread_mutex_lock(&J->lock);
+    const int64_t item = J->next_item++;
+    const int stop = J->status != ORC_OK;
+    pthread_mutex_unlock(&J->lock);
+    if (stop || item >= n_items) break;
+    err = prefill_item(J, item / J->num_kv_heads, item % J->num_kv_heads, Kc, Vc, w);
+  }
+  if (err) {
+    pthread_mutex_lock(&J->lock);
+    if (J->status == ORC_OK) J->status = err;
+    pthread_mutex_unlock(&J->lock);
+  }
+  free(Kc);
+  free(Vc);
+  free(w);
+  return NULL;
+}
+
+/* out: double [query_start_loc[num_seqs], num_heads, head_dim]; q has the same
+ * row count; query_start_loc: int32 [num_seqs + 1], non-decreasing from 0.
+ * Other arrays as for the decode above. */
+int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_cache, const void *v_cache,
+                         int kv_dtype, const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *query_start_loc, int64_t num_seqs, int64_t num_heads,
+                         int64_t num_kv_heads, int64_t head_dim, int64_t num_blocks, int64_t block_size,
+                         int64_t max_blocks_per_seq, double scale, double k_scale, double v_scale, int nthreads) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc) return ORC_BAD_ARG;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0)
+    return ORC_BAD_ARG;
+  if (!elem_size(q_dtype) || q_dtype == ORC_FP8 || !elem_size(kv_dtype)) return ORC_BAD_ARG;
+  if (query_start_loc[0] != 0) return ORC_BAD_ARG;
+  for (int64_t s = 0; s < num_seqs; ++s)
+    if (query_start_loc[s + 1] < query_start_loc[s]) return ORC_BAD_ARG;
+  prefill_job J;
+  memset(&J, 0, sizeof J);
+  J.out = out;
+  J.q = q;
+  J.q_dtype = q_dtype;
+  J.k_cache = k_cache;
+  J.v_cache = v_cache;
+  J.kv_dtype = kv_dtype;
+  J.block_tables = block_tables;
+  J.context_lens = context_lens;
+  J.query_start_loc = query_start_loc;
+  J.num_seqs = num_seqs;
+  J.num_heads = num_heads;
+  J.num_kv_heads = num_kv_heads;
+  J.head_dim = head_dim;
+  J.num_blocks = num_blocks;
+  J.block_size = block_size;
+  J.max_blocks = max_blocks_per_seq;
+  J.scale = scale;
+  J.k_scale = k_scale;
+  J.v_scale = v_scale;
+  J.status = ORC_OK;
+  pthread_mutex_init(&J.lock, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads == 1) {
+    prefill_worker(&J);
+  } else {
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    if (!th) return ORC_NO_MEMORY;
+    int started = 0;
+    for (; started < nthreads; ++started)
+      if (pthread_create(&th[started], NULL, prefill_worker, &J) != 0) break;
+    if (started == 0) prefill_worker(&J);
     for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
     free(th);
   }
