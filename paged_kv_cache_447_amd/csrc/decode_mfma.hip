@@ -38,42 +38,16 @@
 // K and V rows pass through LDS, so the next chunk's loads go out as soon as
 // this chunk's rows are staged, before any of its arithmetic.  fp8 caches are decoded exactly into the
 // query's 16-bit type on the way (every e4m3fn value is representable).
+#include "mfma_core.h"
 #include "pa_sched.h"
 
 namespace pa {
 
 namespace {
 
+using namespace mfma;
+
 constexpr int kWavesPerWG = 4;
-constexpr int CT = 32;  // tokens per chunk: two 16-token QK tiles, one 32-token PV step
-constexpr float kSlack = 8.0f;  // how far (log2 units) scores may exceed the running reference max
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef const __attribute__((address_space(4))) int32_t const_i32;
-
-__device__ __forceinline__ const_i32 *as_const(const int32_t *p) { return (const_i32 *)(uintptr_t)p; }
-
-// MFMA operand type (the query's 16-bit type)
-template <typename MT> struct Op;
-template <> struct Op<f16_t> {
-  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                  0, 0);
-  }
-  __device__ static uint32_t bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
-  __device__ static float value(uint32_t b) { return (float)__builtin_bit_cast(_Float16, (uint16_t)b); }
-};
-template <> struct Op<bf16_t> {
-  __device__ static f32x4 mma(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-  }
-  __device__ static uint32_t bits(float x) { return f32_to_bf16_rne(x); }
-  __device__ static float value(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
-};
 
 // A 16-byte piece of a cache row (8 16-bit elements or 16 fp8 codes) and its
 // conversion to the operand type.
@@ -95,117 +69,28 @@ template <typename MT> struct Piece<fp8_t, MT> {
   }
 };
 
-// Two ds_read_b64_tr_b16 (8 bytes at each lane's address, transposed across
-// each 16-lane group) forming one 16x16x32 operand.
-__device__ __forceinline__ u32x4 read_tr(const void *p0, const void *p1) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p0);
-  const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)p1);
-  const u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-  return u32x4{w0[0], w0[1], w1[0], w1[1]};
-}
-
-template <typename OT>
-__device__ __forceinline__ void store4(void *base, int64_t off, const float *x) {
-  if constexpr (__is_same(OT, f32_t)) {
-    u32x4 w;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = __builtin_bit_cast(uint32_t, x[i]);
-    st16(reinterpret_cast<float *>(base) + off, w);
-  } else {
-    u32x2 w;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) w[i] = Op<OT>::bits(x[2 * i]) | (Op<OT>::bits(x[2 * i + 1]) << 16);
-    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(base) + off) = w;
-  }
-}
-
 // The arithmetic of one wavefront on one (sequence, kv head) segment, whatever
 // brings the chunk's rows into LDS: scores, online softmax, output update and
 // the segment's epilogue.
 template <typename MT, int D, int G>
-struct MfmaMath {
-  static constexpr int KS = D / 32;  // k-steps of the QK contraction
-  static constexpr int NT = D / 16;  // 16-dim output tiles
+struct MfmaMath : MfmaCore<MT, D> {
+  using Core = MfmaCore<MT, D>;
+  using Core::acc;
+  using Core::c16;
+  using Core::j;
+  using Core::l;
+  using Core::m;
+  static constexpr int KS = Core::KS;
+  static constexpr int NT = Core::NT;
   static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
 
   const DecodeArgs &a;
-  const int c16, j;  // column / row within 16, quarter of the wave
-  float m, l;        // softmax state of head c16 (lane-local, combined over j at the end)
-  f32x4 acc[NT];     // O^T tiles: dims 16 n + 4 j + i of head c16
 
-  __device__ MfmaMath(const DecodeArgs &args, int lane) : a(args), c16(lane & 15), j(lane >> 4) {}
+  __device__ MfmaMath(const DecodeArgs &args, int lane) : Core(lane), a(args) {}
 
-  __device__ __forceinline__ void reset() {
-    m = -INFINITY;
-    l = 0.0f;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) acc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-
-  // S^T of the chunk's two 16-token tiles; kop(tt, kb) is the A operand
-  // K[16 tt + c16][32 kb + 8 j ..]
-  template <class KOp>
-  __device__ __forceinline__ void scores(const u32x4 *qop, KOp kop, f32x4 *sc) const {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < KS; ++kb) sc[tt] = Op<MT>::mma(kop(tt, kb), qop[kb], sc[tt]);
-    }
-  }
-
-  // online softmax for head c16 over the lane's 8 tokens (those past `last`
-  // masked), then across the 4 quarters; returns the weights as P^T operands
+  // online softmax for head c16 (tokens past `last` masked)
   __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, u32x4 &phi, u32x4 &plo) {
-    float p8[8];
-    float cm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
-      const float x = sc[i >> 2][i & 3] * a.qk_scale_log2;
-      p8[i] = cs + tok <= last ? x : -INFINITY;
-      cm = fmaxf(cm, p8[i]);
-    }
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
-    // lazy rescale: the reference max moves only when a score exceeds it by
-    // more than kSlack (log2 units), so weights stay below 2^kSlack and the
-    // accumulator rescale is skipped for almost every chunk
-    if (__ballot(cm > m + kSlack)) {
-      const float mn = fmaxf(m, cm);
-      const float alpha = fast_exp2(m - mn);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] *= alpha;
-    }
-    const float mn = m;
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
-      l += e0 + e1;
-      const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
-      phi[i >> 1] = h0 | (h1 << 16);
-      plo[i >> 1] = Op<MT>::bits(e0 - Op<MT>::value(h0)) | (Op<MT>::bits(e1 - Op<MT>::value(h1)) << 16);
-    }
-  }
-
-  // O^T += V^T P^T; vop(n) is the A operand V[tau(j, i)][16 n + c16], i < 8
-  template <class VOp>
-  __device__ __forceinline__ void accumulate(u32x4 phi, u32x4 plo, VOp vop) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-      const u32x4 vt = vop(n);
-      acc[n] = Op<MT>::mma(vt, phi, acc[n]);
-      acc[n] = Op<MT>::mma(vt, plo, acc[n]);
-    }
-  }
-
-  __device__ __forceinline__ void finish() {
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    Core::weights(sc, cs, last, a.qk_scale_log2, phi, plo);
   }
 
   __device__ void write_out(int s, int kvh) const {
@@ -432,20 +317,9 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
 // kAhead instructions are outstanding guarantees the awaited slot has landed;
 // occasional query loads only make that wait stricter.
 //
-// LDS placement: granule g (16 bytes) of row r of a slot sits at granule
-// phys(r, g).  Granules are grouped in 256-byte lines and permuted inside a
-// line by an XOR with a per-line constant, chosen so that the 16 rows of one
-// K operand read fall on 16 different bank groups and the 8 rows that each
-// half of a transposed V read covers fall on 8 different 32-byte bank groups.
-// A DMA instruction fills 1 KB of LDS in lane order, so each lane fetches
-// the global granule that belongs at its LDS position.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at their maxima
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
+// Rows sit in a slot in the swizzled placement of RowSlot (mfma_core.h).  A
+// DMA instruction fills 1 KB of LDS in lane order, so each lane fetches the
+// global granule that belongs at its LDS position.
 template <typename MT, int D, int G, int BS>
 struct MfmaRingSeg : MfmaMath<MT, D, G> {
   using Math = MfmaMath<MT, D, G>;
@@ -455,26 +329,19 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   static constexpr int KS = Math::KS;
   static constexpr int NT = Math::NT;
   static constexpr int LOG2BS = BS == 16 ? 4 : 5;
-  static constexpr int RB = 2 * D;                          // bytes per cache row
-  static constexpr int GPR = RB / 16;                       // 16-byte granules per row
-  static constexpr int HB = CT * RB;                        // bytes of a half-chunk slot
-  static constexpr int NLD = HB / 1024;                     // DMA instructions per half-chunk
-  static constexpr int RPI = 1024 / RB;                     // rows per DMA instruction
+  using Slot = RowSlot<D>;
+  static constexpr int RB = Slot::RB;                       // bytes per cache row
+  static constexpr int HB = Slot::HB;                       // bytes of a half-chunk slot
+  static constexpr int NLD = Slot::NLD;                     // DMA instructions per half-chunk
+  static constexpr int RPI = Slot::RPI;                     // rows per DMA instruction
   static constexpr int QB = G * RB > 1024 ? G * RB : 1024;  // bytes of a query slot
   static constexpr int kLdsBytes = 4 * HB + 2 * QB;
   static constexpr int kAhead = 3 * NLD;  // instructions issued after the half-chunk a wait is for
   static constexpr int kNontemporal = 2;  // cache-policy operand of the DMA: streaming (nt)
   static_assert(kLdsBytes * kWavesPerWG <= 160 * 1024, "ring fits the LDS of a CU");
-  static_assert(RPI <= 16 && 16 % RPI == 0, "a DMA instruction stays inside one 16-token tile");
 
   typedef __attribute__((address_space(3))) void lds_void;
   __device__ static lds_void *lds_addr(char *p) { return (lds_void *)p; }
-
-  __device__ static int swz(bool isv, int L) { return isv ? 2 * (L & (GPR / 2 - 1)) : (L & (GPR - 1)); }
-  __device__ static int phys(bool isv, int r, int g) {
-    const int q = r * GPR + g, L = q >> 4;
-    return (L << 4) | ((q & 15) ^ swz(isv, L));
-  }
 
   struct Src {
     const char *base;  // cache + kv head offset
@@ -506,10 +373,9 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   __device__ MfmaRingSeg(const DecodeArgs &args, int ln, char *lds)
       : Math(args, ln), ring(lds), lane(ln), lw(args), cw(args) {
 #pragma unroll
-    for (int kb = 0; kb < KS; ++kb) koff[kb] = 16 * phys(false, c16, 4 * kb + j);
+    for (int kb = 0; kb < KS; ++kb) koff[kb] = Slot::k_off(c16, j, kb);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      voff[n] = 16 * phys(true, 4 * j + (c16 >> 2), 2 * n + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+    for (int n = 0; n < NT; ++n) voff[n] = Slot::v_off(c16, j, n);
   }
 
   __device__ __forceinline__ void fetch_blocks(int cs, int last, int *blk) const {
@@ -525,10 +391,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   __device__ __forceinline__ void dma(const Src &src, int64_t sb, int64_t st, char *slot) const {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      const int P = 64 * i + lane;  // LDS granule this lane fills
-      const int L = P >> 4;
-      const int q = (L << 4) | ((P & 15) ^ swz(ISV, L));
-      const int r = q / GPR, g = q % GPR;
+      int r, g;
+      Slot::dma_target(ISV, i, lane, r, g);
       const int t = min(src.cs + r, src.last);
       const int blk = (RPI * i) / 16 ? src.blk1 : src.blk0;
       const char *bb = src.base + (int64_t)blk * sb * 2;  // uniform block base
@@ -588,19 +452,6 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
 
   // V rows of the chunk whose K rows went out last, into V slot `par`
   __device__ __forceinline__ void issue_v(int par) { dma<true>(vpend, a.v_sb, a.v_st, ring + (par * 2 + 1) * HB); }
-
-  // Transposed V reads are issued as inline assembly: the compiler does not
-  // see them as LDS loads, so it adds no wait for the DMA stream (the explicit
-  // vmcnt waits order them), and their completion is awaited explicitly.
-  __device__ static __forceinline__ u32x2 tr_read(const char *p) {
-    u32x2 d;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(d) : "v"((uint32_t)(uintptr_t)p));
-    return d;
-  }
-  template <int N>
-  __device__ static __forceinline__ void lgkm_wait(u32x2 &x0, u32x2 &x1, u32x2 &x2, u32x2 &x3) {
-    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(x0), "+v"(x1), "+v"(x2), "+v"(x3) : "n"(N));
-  }
 
   // Start on this worker's range [b, e); false if there is nothing to do.
   __device__ bool start(const Split &split, const Windows &first, int64_t b, int64_t e) {
@@ -663,34 +514,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       Math::weights(sc, cs, last, phi, plo);
       wait_vm<kAhead>();  // V rows of this chunk
       __builtin_amdgcn_sched_barrier(0);
-      const char *vs = ring + (par * 2 + 1) * HB;
-      // two tiles of transposed reads in flight ahead of the tiles being multiplied
-      u32x2 vt[NT][2];
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        vt[n][0] = tr_read(vs + voff[n]);
-        vt[n][1] = tr_read(vs + voff[n] + 16 * RB);
-      }
-#pragma unroll
-      for (int n = 0; n < NT; n += 2) {
-        // reads issued after tiles n, n+1: those of tiles n+2, n+3, if any
-        if (n + 3 < NT)
-          lgkm_wait<4>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
-        else
-          lgkm_wait<0>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
-        if (n + 4 < NT) {
-          vt[n + 4][0] = tr_read(vs + voff[n + 4]);
-          vt[n + 4][1] = tr_read(vs + voff[n + 4] + 16 * RB);
-          vt[n + 5][0] = tr_read(vs + voff[n + 5]);
-          vt[n + 5][1] = tr_read(vs + voff[n + 5] + 16 * RB);
-        }
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          const u32x4 op{vt[n + d][0][0], vt[n + d][0][1], vt[n + d][1][0], vt[n + d][1][1]};
-          Math::acc[n + d] = Op<MT>::mma(op, phi, Math::acc[n + d]);
-          Math::acc[n + d] = Op<MT>::mma(op, plo, Math::acc[n + d]);
-        }
-      }
+      Math::accumulate_slot(phi, plo, ring + (par * 2 + 1) * HB, [&](int n) { return voff[n]; });
       __builtin_amdgcn_sched_barrier(0);
       cs += CT;
       ++ccnt;
