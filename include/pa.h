@@ -1,7 +1,7 @@
 /*
- * pa.h -- C ABI of the paged-KV decode library (libpa.so) for AMD gfx950.
+ * pa.h -- C ABI of the paged-KV attention library (libpa.so) for AMD gfx950.
  *
- * Two operations, both defined on the pages this library follows:
+ * Three operations, all defined on the pages this library follows:
  *
  *   pa_decode       attention of one query token per head over a KV cache kept
  *                   in fixed-size physical blocks, found through a per-sequence
@@ -14,6 +14,10 @@
  *                   accumulates attention across blocks; the logical-to-physical
  *                   translation itself is section 5.1 of page
  *                   "vLLM框架中的KV cache优化与PagedAttention机制详解").
+ *   pa_prefill      the same attention for several query tokens per sequence
+ *                   (a prompt chunk, or draft tokens being verified), each
+ *                   token seeing the context up to its own position; the
+ *                   query tensor of the same section holds one row per token.
  *   pa_cache_write  scatter of new tokens' K/V rows into physical slots
  *                   (slot = block * block_size + offset, the address rule of
  *                   page "Paged KVCache：大模型推理显存管理优化方案", section 2.3).
@@ -137,6 +141,41 @@ PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int6
 PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
                            pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
                            const pa_opts *opts);
+
+/*
+ * pa_prefill -- paged attention for several causal query tokens per sequence.
+ *
+ *   q               [num_tokens, num_heads, head_dim] PA_F16 or PA_BF16: the
+ *                   query rows of every sequence of the step, sequence after
+ *                   sequence.
+ *   query_start_loc [num_seqs + 1] PA_I32, non-decreasing, from 0 to
+ *                   num_tokens: rows query_start_loc[s] .. query_start_loc[s+1]-1
+ *                   belong to sequence s.
+ *   context_lens    [num_seqs] PA_I32: tokens of sequence s in the cache,
+ *                   the step's own tokens included (their K/V rows written
+ *                   first, e.g. by pa_cache_write).
+ *   out             [num_tokens, num_heads, head_dim], q's dtype or PA_F32.
+ *                   With n = the rows of sequence s and L = context_lens[s],
+ *                   row j (0 <= j < n) is the token at position p = L - n + j:
+ *                   out[row, h, :] = softmax_t(scale * q[row,h,:] . K_t) . V_t
+ *                   over positions t = 0 .. p, K_t / V_t found through the
+ *                   block table as in pa_decode.  n = 1 is pa_decode's result;
+ *                   n = L is causal attention over a whole prompt.  Requires
+ *                   n <= L; a row whose position would be negative gets zeros.
+ *   k_cache,
+ *   v_cache         [num_blocks, block_size, num_kv_heads, head_dim], q's dtype.
+ *   block_tables    [num_seqs, max_blocks_per_seq] PA_I32, as in pa_decode.
+ *   block_size      16 or 32; num_kv_heads divides num_heads; head_dim 64 or 128.
+ *   opts            stream only (no workspace; scales, partition_size and
+ *                   num_workers are ignored; flags must be 0).
+ * The contents of query_start_loc are trusted like the block tables: values
+ * outside [0, num_tokens] are clamped, never followed out of bounds.
+ * Work: one launch; a workgroup per (sequence, kv head, tile of 64 or 128
+ * (query row, query head) pairs), streaming the positions its last row sees.
+ */
+PA_API pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
+                            pa_tensor block_tables, pa_tensor context_lens, pa_tensor query_start_loc,
+                            int32_t block_size, float scale, int32_t num_kv_heads, const pa_opts *opts);
 
 /*
  * pa_cache_write -- scatter new tokens into the paged cache.

@@ -1,4 +1,4 @@
-"""Python binding of libpa.so, the gfx950 paged-KV decode library.
+"""Python binding of libpa.so, the gfx950 paged-KV attention library.
 
 The functions here only marshal torch tensors into the C ABI of include/pa.h
 (device pointers, dtypes, shapes, strides, the current HIP stream) and turn
@@ -17,6 +17,7 @@ __all__ = [
     "PaError",
     "load_library",
     "decode",
+    "prefill",
     "cache_write",
     "workspace_size",
     "num_workers",
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_prefill.restype = i32
+    lib.pa_prefill.argtypes = [PaTensor] * 7 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_cache_write.restype = i32
     lib.pa_cache_write.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -198,6 +201,23 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
     o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                        describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, block_size: int, scale: float,
+            num_kv_heads: int, stream=None):
+    """pa_prefill: fill ``out`` [N, H, D] with causal paged attention of the
+    query rows of every sequence (rows query_start_loc[s] .. [s+1]-1 are the
+    newest tokens of sequence s); returns ``out``."""
+    lib = load_library()
+    _check_device(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
+    o = PaOpts()
+    o.stream = stream if stream is not None else _current_stream(q)
+    st = lib.pa_prefill(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
+                        describe(context_lens), describe(query_start_loc), block_size, scale, num_kv_heads,
+                        ctypes.byref(o))
     if st != 0:
         _raise(lib, st)
     return out

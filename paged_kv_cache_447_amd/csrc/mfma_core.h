@@ -145,6 +145,7 @@ struct MfmaCore {
   f32x4 acc[NT];
 
   __device__ explicit MfmaCore(int lane) : c16(lane & 15), j(lane >> 4) {}
+  __device__ MfmaCore() : MfmaCore(__lane_id()) {}
 
   __device__ __forceinline__ void reset() {
     m = -INFINITY;
@@ -215,45 +216,63 @@ struct MfmaCore {
     }
   }
 
-  // O^T += V^T P^T with the V^T operands read from a ring slot by the
-  // assembly reads, two tiles of reads in flight ahead of the tiles being
-  // multiplied; voff(n) is the lane's byte offset of tile n's first half.
+  // accumulate() with the V^T operands read from a ring slot by the assembly
+  // reads (see accumulate_slot_n)
   template <class VOff>
-  __device__ __forceinline__ void accumulate_slot(u32x4 phi, u32x4 plo, const char *vs, VOff voff) {
-    constexpr int RB = 2 * D;
-    u32x2 vt[NT][2];
-#pragma unroll
-    for (int n = 0; n < 4 && n < NT; ++n) {
-      vt[n][0] = tr_read_async(vs + voff(n));
-      vt[n][1] = tr_read_async(vs + voff(n) + 16 * RB);
-    }
-#pragma unroll
-    for (int n = 0; n < NT; n += 2) {
-      // reads issued after tiles n, n+1: those of tiles n+2, n+3, if any
-      if (n + 3 < NT)
-        lgkm_wait<4>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
-      else
-        lgkm_wait<0>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
-      if (n + 4 < NT) {
-        vt[n + 4][0] = tr_read_async(vs + voff(n + 4));
-        vt[n + 4][1] = tr_read_async(vs + voff(n + 4) + 16 * RB);
-        vt[n + 5][0] = tr_read_async(vs + voff(n + 5));
-        vt[n + 5][1] = tr_read_async(vs + voff(n + 5) + 16 * RB);
-      }
-#pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const u32x4 op{vt[n + d][0][0], vt[n + d][0][1], vt[n + d][1][0], vt[n + d][1][1]};
-        acc[n + d] = Op<MT>::mma(op, phi, acc[n + d]);
-        acc[n + d] = Op<MT>::mma(op, plo, acc[n + d]);
-      }
-    }
-  }
+  __device__ __forceinline__ void accumulate_slot(u32x4 phi, u32x4 plo, const char *vs, VOff voff);
 
   __device__ __forceinline__ void finish() {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
   }
 };
+
+// O^T += V^T P^T for NC cores (16 columns each) that share the chunk's V rows:
+// the V^T operands are read once from a ring slot by the assembly reads, two
+// tiles of reads in flight ahead of the tiles being multiplied, and each
+// operand is multiplied into every core; voff(n) is the lane's byte offset of
+// tile n's first half.
+template <int NC, typename MT, int D, class VOff>
+__device__ __forceinline__ void accumulate_slot_n(MfmaCore<MT, D> *core, const u32x4 *phi, const u32x4 *plo,
+                                                  const char *vs, VOff voff) {
+  constexpr int NT = D / 16;
+  constexpr int RB = 2 * D;
+  u32x2 vt[NT][2];
+#pragma unroll
+  for (int n = 0; n < 4 && n < NT; ++n) {
+    vt[n][0] = tr_read_async(vs + voff(n));
+    vt[n][1] = tr_read_async(vs + voff(n) + 16 * RB);
+  }
+#pragma unroll
+  for (int n = 0; n < NT; n += 2) {
+    // reads issued after tiles n, n+1: those of tiles n+2, n+3, if any
+    if (n + 3 < NT)
+      lgkm_wait<4>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
+    else
+      lgkm_wait<0>(vt[n][0], vt[n][1], vt[n + 1][0], vt[n + 1][1]);
+    if (n + 4 < NT) {
+      vt[n + 4][0] = tr_read_async(vs + voff(n + 4));
+      vt[n + 4][1] = tr_read_async(vs + voff(n + 4) + 16 * RB);
+      vt[n + 5][0] = tr_read_async(vs + voff(n + 5));
+      vt[n + 5][1] = tr_read_async(vs + voff(n + 5) + 16 * RB);
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const u32x4 op{vt[n + d][0][0], vt[n + d][0][1], vt[n + d][1][0], vt[n + d][1][1]};
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        core[ct].acc[n + d] = Op<MT>::mma(op, phi[ct], core[ct].acc[n + d]);
+        core[ct].acc[n + d] = Op<MT>::mma(op, plo[ct], core[ct].acc[n + d]);
+      }
+    }
+  }
+}
+
+template <typename MT, int D>
+template <class VOff>
+__device__ __forceinline__ void MfmaCore<MT, D>::accumulate_slot(u32x4 phi, u32x4 plo, const char *vs, VOff voff) {
+  accumulate_slot_n<1>(this, &phi, &plo, vs, voff);
+}
 
 }  // namespace mfma
 }  // namespace pa

@@ -247,6 +247,104 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   return PA_OK;
 }
 
+pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
+                     pa_tensor context_lens, pa_tensor query_start_loc, int32_t block_size, float scale,
+                     int32_t num_kv_heads, const pa_opts *opts) {
+  pa_opts o;
+  std::memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  pa_status st;
+  if ((st = check_tensor(out, "out", 3, true))) return st;
+  if ((st = check_tensor(q, "q", 3, true))) return st;
+  if ((st = check_tensor(k_cache, "k_cache", 4, true))) return st;
+  if ((st = check_tensor(v_cache, "v_cache", 4, true))) return st;
+  if ((st = check_tensor(block_tables, "block_tables", 2, false))) return st;
+  if ((st = check_tensor(context_lens, "context_lens", 1, false))) return st;
+  if ((st = check_tensor(query_start_loc, "query_start_loc", 1, false))) return st;
+
+  if (q.dtype != PA_F16 && q.dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q: dtype must be F16 or BF16");
+  if (k_cache.dtype != q.dtype || v_cache.dtype != q.dtype)
+    return fail(PA_ERR_DTYPE, "k_cache and v_cache must have q's dtype");
+  if (out.dtype != q.dtype && out.dtype != PA_F32) return fail(PA_ERR_DTYPE, "out: dtype must be q's dtype or F32");
+  if (block_tables.dtype != PA_I32) return fail(PA_ERR_DTYPE, "block_tables: dtype must be I32");
+  if (context_lens.dtype != PA_I32) return fail(PA_ERR_DTYPE, "context_lens: dtype must be I32");
+  if (query_start_loc.dtype != PA_I32) return fail(PA_ERR_DTYPE, "query_start_loc: dtype must be I32");
+
+  const int64_t N = q.shape[0], H = q.shape[1], D = q.shape[2];
+  const int64_t S = context_lens.shape[0], NB = k_cache.shape[0];
+  for (int i = 0; i < 3; ++i)
+    if (out.shape[i] != q.shape[i]) return fail(PA_ERR_SHAPE, "out shape differs from q shape in dim %d", i);
+  for (int i = 0; i < 4; ++i)
+    if (k_cache.shape[i] != v_cache.shape[i]) return fail(PA_ERR_SHAPE, "k_cache and v_cache shapes differ");
+  if (k_cache.shape[1] != block_size)
+    return fail(PA_ERR_SHAPE, "block_size %d != k_cache.shape[1] %lld", block_size, (long long)k_cache.shape[1]);
+  if (k_cache.shape[2] != num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_kv_heads %d != k_cache.shape[2] %lld", num_kv_heads, (long long)k_cache.shape[2]);
+  if (k_cache.shape[3] != D) return fail(PA_ERR_SHAPE, "k_cache head_dim %lld != q head_dim %lld",
+                                         (long long)k_cache.shape[3], (long long)D);
+  if (num_kv_heads <= 0 || H % num_kv_heads)
+    return fail(PA_ERR_SHAPE, "num_heads %lld not a multiple of num_kv_heads %d", (long long)H, num_kv_heads);
+  if (block_tables.shape[0] != S) return fail(PA_ERR_SHAPE, "block_tables has %lld rows, context_lens %lld entries",
+                                              (long long)block_tables.shape[0], (long long)S);
+  if (query_start_loc.shape[0] != S + 1)
+    return fail(PA_ERR_SHAPE, "query_start_loc has %lld entries, expected num_seqs + 1 = %lld",
+                (long long)query_start_loc.shape[0], (long long)(S + 1));
+  if (block_size != 16 && block_size != 32) return fail(PA_ERR_UNSUPPORTED, "block_size %d (built: 16, 32)", block_size);
+  if (!pa::prefill_supported(kv_kind(k_cache.dtype), (int)D))
+    return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
+  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  const int64_t W = block_tables.shape[1];
+  const int64_t G = num_kv_heads > 0 ? H / num_kv_heads : 0;
+  if (S > INT32_MAX - 1 || N * G > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many sequences or query rows");
+  if (W * block_size > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "table width too large");
+  if (NB > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "more than 2^31-1 blocks");
+  if (S == 0 || N == 0 || H == 0) return PA_OK;
+  if (NB == 0 || W == 0) return fail(PA_ERR_SHAPE, "empty cache or block table");
+
+  pa::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.out = out.data;
+  a.q = q.data;
+  a.k_cache = k_cache.data;
+  a.v_cache = v_cache.data;
+  a.block_tables = static_cast<const int32_t *>(block_tables.data);
+  a.context_lens = static_cast<const int32_t *>(context_lens.data);
+  a.query_start_loc = static_cast<const int32_t *>(query_start_loc.data);
+  a.q_sn = q.stride[0];
+  a.q_sh = q.stride[1];
+  a.o_sn = out.stride[0];
+  a.o_sh = out.stride[1];
+  a.k_sb = k_cache.stride[0];
+  a.k_st = k_cache.stride[1];
+  a.k_sh = k_cache.stride[2];
+  a.v_sb = v_cache.stride[0];
+  a.v_st = v_cache.stride[1];
+  a.v_sh = v_cache.stride[2];
+  a.bt_ss = block_tables.stride[0];
+  a.num_seqs = (int32_t)S;
+  a.num_rows = (int32_t)N;
+  a.num_heads = (int32_t)H;
+  a.num_kv_heads = num_kv_heads;
+  a.group = (int32_t)G;
+  a.head_dim = (int32_t)D;
+  a.num_blocks = (int32_t)NB;
+  a.block_size = block_size;
+  a.max_ctx = (int32_t)(W * block_size);
+  a.tile_cols = pa::prefill_tile_cols(N, S, (int)G);
+  // every sequence's tiles: at most N * G / tile_cols whole ones plus one partial tile each
+  const int64_t slots = (N * G + a.tile_cols - 1) / a.tile_cols + S;
+  if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");
+  a.tile_slots = (int32_t)slots;
+  a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.kv_kind = kv_kind(k_cache.dtype);
+  a.out_f32 = out.dtype == PA_F32;
+
+  hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(o.stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "prefill kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor v_cache, pa_tensor slot_mapping,
                          const pa_opts *opts) {
   pa_opts o;
@@ -334,6 +432,6 @@ const char *pa_status_string(pa_status s) {
 
 const char *pa_last_error(void) { return g_last_error; }
 
-const char *pa_version(void) { return "0.2.0"; }
+const char *pa_version(void) { return "0.3.0"; }
 
 }  // extern "C"

@@ -45,6 +45,34 @@ struct DecodeArgs {
   int32_t out_f32;              // 1: out is fp32, 0: out has q's dtype
 };
 
+// Everything a prefill launch needs, already validated; strides in elements.
+// Query rows qsl[s] .. qsl[s+1]-1 belong to sequence s and are its newest
+// tokens: row j of n sits at position context_len - n + j and sees the
+// positions up to its own.  The (row, query head) pairs of a sequence and kv
+// head -- its "columns", row-major, G heads per row -- are cut into tiles of a
+// fixed number of columns; one workgroup computes one tile.
+struct PrefillArgs {
+  void *out;
+  const void *q;
+  const void *k_cache;
+  const void *v_cache;
+  const int32_t *block_tables;
+  const int32_t *context_lens;
+  const int32_t *query_start_loc;  // [S + 1]
+  int64_t q_sn, q_sh;              // q strides: row, head
+  int64_t o_sn, o_sh;              // out strides
+  int64_t k_sb, k_st, k_sh;        // k_cache strides: block, token, kv head
+  int64_t v_sb, v_st, v_sh;        // v_cache strides
+  int64_t bt_ss;                   // block-table row stride
+  int32_t num_seqs, num_rows, num_heads, num_kv_heads, group, head_dim;
+  int32_t num_blocks, block_size, max_ctx;
+  int32_t tile_slots;              // tile slots per kv head in the grid (>= the tiles of all sequences)
+  int32_t tile_cols;               // columns per tile
+  float qk_scale_log2;             // scale * log2(e)
+  int32_t kv_kind;                 // KvKind of the caches (= q's)
+  int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype
+};
+
 struct CacheWriteArgs {
   const void *k;
   const void *v;
@@ -73,6 +101,10 @@ bool decode_uses_mfma(int kv_kind, int head_dim, int group);
 int decode_mfma_chunk_tokens();
 hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
+// causal multi-token queries on the matrix cores (prefill_mfma.hip)
+bool prefill_supported(int kv_kind, int head_dim);
+int prefill_tile_cols(int64_t num_rows, int64_t num_seqs, int group);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 // Which (kv dtype, q dtype, head_dim, group size) the decode kernels were built for.
 bool decode_supported(int kv_kind, int q_kind, int head_dim, int group);

@@ -1,0 +1,337 @@
+// Paged prefill on the matrix cores: several query tokens per sequence (a
+// prompt chunk, or the draft tokens of a speculative step), each attending
+// causally to the cached context up to its own position.
+//
+// The query rows of a sequence are its newest tokens; their K/V rows are
+// already in the cache (written by the cache-write scatter), so every score
+// reads K and V through the block table exactly as decode does: logical block
+// t / block_size to physical block, offset t % block_size (page
+// "vLLM框架中的KV cache优化与PagedAttention机制详解", section 5.1; address rule of
+// page "Paged KVCache：大模型推理显存管理优化方案", section 2.3).  The query tensor
+// holds one row per token of the step, as in the kernel interface of page
+// "vLLM推理引擎架构：PagedAttention机制与高吞吐推理" (section 2.3), and a prompt
+// takes ceil(prompt_len / block_size) blocks (section 2.2 of the same page).
+//
+// Work: the columns of a (sequence, kv head) pair are its (query row, query
+// head) pairs, row-major with the G heads of the group; each workgroup of 4
+// wavefronts computes a tile of 4 x 16 NC columns, each wavefront 16 NC of
+// them as NC MfmaCore column sets (mfma_core.h).  A column's scores are masked
+// past its own position, so one chunk pass serves rows with different limits.
+// The workgroup streams the K and V rows of positions 0 .. (its last row's
+// position) in 32-token chunks through a three-slot LDS ring: each wavefront
+// loads an eighth of every chunk straight from HBM into LDS, and one barrier
+// per chunk both publishes a chunk to all four wavefronts and frees the slot
+// that the next loads go into, so two chunks are in flight during each
+// chunk's arithmetic.  Every wavefront reads the K operands and transposed V
+// operands of the chunk from LDS and multiplies them into all NC of its
+// column sets.
+#include "mfma_core.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 4;  // wavefronts per workgroup, sharing one K/V stream
+constexpr int kRing = 3;   // chunk slots of the LDS ring
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ lds_void *lds_addr(char *p) { return (lds_void *)p; }
+
+// A workgroup barrier without the memory fence of __syncthreads(), whose
+// wait for every outstanding load would drain the ring; the chunk loads are
+// awaited explicitly before it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Query rows [lo, hi) of sequence i (clamped into [0, num_rows]).
+__device__ __forceinline__ void seq_rows(const PrefillArgs &a, int i, int &lo, int &hi) {
+  lo = clampi(a.query_start_loc[i], 0, a.num_rows);
+  hi = clampi(a.query_start_loc[i + 1], lo, a.num_rows);
+}
+
+// The sequence and tile of tile slot t: sequences in order, each cut into
+// ceil(rows * G / tile_cols) tiles.  false if t is past the last tile.  All
+// results are wave-uniform.
+__device__ bool locate_tile(const PrefillArgs &a, int t, int lane, int &seq, int &tile) {
+  int carry = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int i = base + lane;
+    int tiles = 0;
+    if (i < a.num_seqs) {
+      int lo, hi;
+      seq_rows(a, i, lo, hi);
+      tiles = (int)(((int64_t)(hi - lo) * a.group + a.tile_cols - 1) / a.tile_cols);
+    }
+    const int incl = wave_incl_scan(tiles, lane);
+    const int total = uniform(__shfl(incl, 63));
+    if (t < carry + total) {
+      const int k = uniform(__builtin_ctzll(__ballot(carry + incl > t)));
+      seq = base + k;
+      tile = t - carry - uniform(__shfl(incl - tiles, k));
+      return true;
+    }
+    carry += total;
+  }
+  return false;
+}
+
+template <typename MT, int D, int BS, int NC>
+struct PrefillTile {
+  using Slot = RowSlot<D>;
+  using Core = MfmaCore<MT, D>;
+  static constexpr int KS = D / 32;
+  static constexpr int NT = D / 16;
+  static constexpr int RB = Slot::RB;
+  static constexpr int HB = Slot::HB;                 // bytes of the K (or V) rows of a chunk
+  static constexpr int PER = Slot::NLD / kWaves;      // DMA instructions per wavefront per K (or V) chunk
+  static constexpr int CB = 2 * HB;                   // bytes of a ring slot: K rows, then V rows
+  static constexpr int kLdsBytes = kRing * CB;
+  static constexpr int LOG2BS = BS == 16 ? 4 : 5;
+  static_assert(Slot::NLD % kWaves == 0, "every wavefront loads the same share of a chunk");
+  static_assert(Slot::RPI * PER == 8, "a wavefront's share is 8 rows inside one 16-token tile");
+  static_assert(kLdsBytes <= 64 * 1024, "two workgroups fit the LDS of a CU");
+
+  const PrefillArgs &a;
+  char *const ring;
+  const int lane, wave, c16, jq;
+
+  // the workgroup's tile
+  int s, kvh, q0, pos0, c_hi, last_max;
+  const_i32 *bt;
+  const char *kbase, *vbase;
+  // this wavefront's columns
+  int wlast;          // last position any of them sees (-1: no columns)
+  int last[NC];       // per lane: the position its column sees up to
+  int row[NC], head[NC];
+  bool valid[NC];
+  u32x4 qop[NC][KS];
+  Core core[NC];
+  int koff[KS], voff[NT];
+
+  __device__ PrefillTile(const PrefillArgs &args, char *lds, int ln, int wv)
+      : a(args), ring(lds), lane(ln), wave(wv), c16(ln & 15), jq(ln >> 4) {
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) koff[kb] = Slot::k_off(c16, jq, kb);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) voff[n] = Slot::v_off(c16, jq, n);
+  }
+
+  // Set up tile `tile` of sequence `seq` for kv head `kh`; false if none of
+  // its rows sees a position (then its outputs are written as zeros).
+  __device__ bool setup(int seq, int tile, int kh) {
+    s = seq;
+    kvh = kh;
+    int q1;
+    seq_rows(a, s, q0, q1);
+    const int nq = q1 - q0;
+    const int L = clamp_ctx(a.context_lens[s], a.max_ctx);
+    pos0 = L - nq;  // position of the sequence's first query row
+    const int c_lo = tile * a.tile_cols;
+    c_hi = min(c_lo + a.tile_cols, nq * a.group);
+    last_max = pos0 + (c_hi - 1) / a.group;
+    bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
+    kbase = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * 2;
+    vbase = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * 2;
+    const int w_lo = c_lo + 16 * NC * wave;
+    wlast = w_lo < c_hi ? pos0 + (min(w_lo + 16 * NC, c_hi) - 1) / a.group : -1;
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      const int col = w_lo + 16 * ct + c16;
+      valid[ct] = col < c_hi;
+      const int r = valid[ct] ? col / a.group : 0;
+      row[ct] = q0 + r;
+      head[ct] = kvh * a.group + (valid[ct] ? col - r * a.group : 0);
+      // padding columns (never written) run with the tile's limit
+      last[ct] = valid[ct] ? pos0 + r : last_max;
+    }
+    return last_max >= 0;
+  }
+
+  // q^T operands: lane (c16, jq) of set ct holds q[row][head][32 kb + 8 jq ..]
+  // (a padding column holds the tile's first row: finite, never written)
+  __device__ __forceinline__ void load_q() {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      const uint16_t *qr =
+          reinterpret_cast<const uint16_t *>(a.q) + (int64_t)row[ct] * a.q_sn + (int64_t)head[ct] * a.q_sh;
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) qop[ct][kb] = ld16(qr + 32 * kb + 8 * jq);
+    }
+  }
+
+  // Physical block of this wavefront's 8 rows of chunk c (rows 8 wave .. +7
+  // lie in 16-token tile wave / 2; rows past last_max read last_max's row,
+  // chunks past the end included).
+  __device__ __forceinline__ int block_of(int c) const {
+    const int t = min(CT * c + 16 * (wave >> 1), last_max);
+    const int b = bt[t >> LOG2BS];
+    return b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+  }
+
+  // this wavefront's share of chunk c's K and V rows into ring slot `slot`
+  __device__ __forceinline__ void issue(int c, int blk, int slot) {
+    char *dst = ring + slot * CB;
+    const int cs = CT * c;
+#pragma unroll
+    for (int isv = 0; isv < 2; ++isv) {
+      const char *base = isv ? vbase : kbase;
+      const int64_t sb = isv ? a.v_sb : a.k_sb, st = isv ? a.v_st : a.k_st;
+      const char *bb = base + (int64_t)blk * sb * 2;  // uniform block base
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        const int i = wave * PER + p;
+        int r, g;
+        Slot::dma_target(isv, i, lane, r, g);
+        const int t = min(cs + r, last_max);
+        const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
+        __builtin_amdgcn_global_load_lds(gp, lds_addr(dst + isv * HB + 1024 * i), 16, 0, 0);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(int c) {
+    const int cs = CT * c;
+    const char *ks = ring + (c % kRing) * CB;
+    u32x4 kop[2][KS];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) kop[tt][kb] = ld16(ks + koff[kb] + tt * 16 * RB);
+    u32x4 phi[NC], plo[NC];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      f32x4 sc[2];
+      core[ct].scores(qop[ct], [&](int tt, int kb) { return kop[tt][kb]; }, sc);
+      core[ct].weights(sc, cs, last[ct], a.qk_scale_log2, phi[ct], plo[ct]);
+    }
+    accumulate_slot_n<NC>(core, phi, plo, ks + HB, [&](int n) { return voff[n]; });
+  }
+
+  __device__ void run() {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].reset();
+    load_q();
+    const int nch = last_max / CT + 1;
+    // every chunk index issued is loaded (past nch it reloads the last rows
+    // into a slot that nobody reads), so each wavefront always has exactly
+    // 2 PER loads per chunk outstanding behind the one awaited
+    issue(0, block_of(0), 0);
+    issue(1, block_of(1), 1);
+    int nblk = block_of(2);
+    for (int c = 0; c < nch; ++c) {
+      wait_vm<2 * PER>();  // this wavefront's share of chunk c (and the queries before it) has landed
+      wg_barrier();        // every share of chunk c has; everybody is done with chunk c - 1
+      __builtin_amdgcn_sched_barrier(0);
+      issue(c + 2, nblk, (c + 2) % kRing);
+      nblk = block_of(c + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if (CT * c <= wlast) compute(c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<0>();  // no load may land after the workgroup's LDS is released
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].finish();
+  }
+
+  template <typename OT>
+  __device__ __forceinline__ void store(int ct, bool zero) const {
+    const float inv = 1.0f / core[ct].l;
+    const bool z = zero || last[ct] < 0;
+    const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      float o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = z ? 0.0f : core[ct].acc[n][i] * inv;
+      store4<OT>(a.out, off + 16 * n, o);
+    }
+  }
+
+  // outputs of the valid columns (zeros when `zero`, or for a row before position 0)
+  __device__ void write_out(bool zero) const {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      if (!valid[ct]) continue;
+      if (a.out_f32)
+        store<f32_t>(ct, zero);
+      else
+        store<MT>(ct, zero);
+    }
+  }
+};
+
+template <typename MT, int D, int BS, int NC>
+__global__ void __launch_bounds__(64 * kWaves) prefill_mfma(const PrefillArgs a) {
+  typedef PrefillTile<MT, D, BS, NC> Tile;
+  __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  // workgroups are dealt to the 8 XCDs round-robin; number them so that the
+  // tiles of one kv head, which read the same K/V rows, share an XCD's L2
+  const int nb = gridDim.x, b = blockIdx.x;
+  const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+  const int kvh = bx / a.tile_slots;
+  if (kvh >= a.num_kv_heads) return;
+  int seq, tile;
+  if (!locate_tile(a, bx - kvh * a.tile_slots, lane, seq, tile)) return;  // the same for all four wavefronts
+  Tile t(a, lds, lane, wave);
+  if (!t.setup(seq, tile, kvh)) {
+    t.write_out(true);
+    return;
+  }
+  t.run();
+  t.write_out(false);
+}
+
+template <typename MT, int D, int BS>
+hipError_t launch_nc(const PrefillArgs &a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.tile_slots * a.num_kv_heads;
+  const dim3 grid((unsigned)((n + 7) / 8 * 8)), block(64 * kWaves);
+  if (a.tile_cols == 64 * kWaves / 2)
+    hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename MT, int D>
+hipError_t launch_bs(const PrefillArgs &a, hipStream_t stream) {
+  return a.block_size == 16 ? launch_nc<MT, D, 16>(a, stream) : launch_nc<MT, D, 32>(a, stream);
+}
+
+template <typename MT>
+hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_bs<MT, 64>(a, stream);
+    case 128: return launch_bs<MT, 128>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool prefill_supported(int kv_kind, int head_dim) {
+  return (kv_kind == KV_F16 || kv_kind == KV_BF16) && (head_dim == 64 || head_dim == 128);
+}
+
+// Columns per tile: 32 per wavefront when the sequences average at least two
+// such tiles' worth of columns (each K/V operand read from LDS then feeds
+// twice the arithmetic), else 16.
+int prefill_tile_cols(int64_t num_rows, int64_t num_seqs, int group) {
+  const int64_t wide = 32 * kWaves;
+  return num_rows * group >= 2 * wide * num_seqs ? (int)wide : 16 * kWaves;
+}
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
+  switch (a.kv_kind) {
+    case KV_F16: return launch_d<f16_t>(a, stream);
+    case KV_BF16: return launch_d<bf16_t>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -43,9 +43,9 @@ def lib():
     return pa.load_library()
 
 
-def test_header_declares_the_two_operations():
+def test_header_declares_the_operations():
     syms = declared_symbols()
-    for s in ("pa_decode", "pa_cache_write", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
+    for s in ("pa_decode", "pa_prefill", "pa_cache_write", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
               "pa_last_error"):
         assert s in syms
 
@@ -226,3 +226,43 @@ def test_cache_write_errors(lib):
     o.k_scale = -1.0
     expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), o), -7, "scale")
     expect(lib, call_write(lib, good_write(D=8, kin=pa.PA_F16, kc=pa.PA_FP8_E4M3)), -4)  # 8-byte rows
+
+
+def good_prefill(N=40, S=3, H=8, Hkv=2, D=128, NB=64, bs=16, W=8, q=pa.PA_F16, kv=pa.PA_F16, out=None):
+    return [T([N, H, D], out if out is not None else q), T([N, H, D], q), T([NB, bs, Hkv, D], kv),
+            T([NB, bs, Hkv, D], kv), T([S, W], pa.PA_I32), T([S], pa.PA_I32), T([S + 1], pa.PA_I32)]
+
+
+def call_prefill(lib, args, bs=16, scale=0.1, Hkv=2, opts=None):
+    return lib.pa_prefill(*args, bs, scale, Hkv, ctypes.byref(opts or pa.PaOpts()))
+
+
+def test_prefill_errors(lib):
+    expect(lib, call_prefill(lib, good_prefill(q=pa.PA_F32, kv=pa.PA_F32)), -2, "q")
+    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3)), -2)
+    expect(lib, call_prefill(lib, good_prefill(q=pa.PA_BF16, kv=pa.PA_F16)), -2)
+    expect(lib, call_prefill(lib, good_prefill(out=pa.PA_BF16)), -2, "out")
+    a = good_prefill()
+    a[6] = T([3], pa.PA_I32)  # one entry short
+    expect(lib, call_prefill(lib, a), -3, "query_start_loc")
+    a = good_prefill()
+    a[6] = T([4], pa.PA_I64)
+    expect(lib, call_prefill(lib, a), -2, "query_start_loc")
+    a = good_prefill()
+    a[4] = T([4, 8], pa.PA_I32)
+    expect(lib, call_prefill(lib, a), -3, "block_tables")
+    expect(lib, call_prefill(lib, good_prefill(), bs=32), -3, "block_size")
+    expect(lib, call_prefill(lib, good_prefill(), Hkv=3), -3)
+    expect(lib, call_prefill(lib, good_prefill(D=96)), -5, "head_dim")
+    expect(lib, call_prefill(lib, good_prefill(bs=8), bs=8), -5, "block_size")
+    expect(lib, call_prefill(lib, good_prefill(), scale=0.0), -7, "scale")
+    expect(lib, call_prefill(lib, good_prefill(), scale=float("nan")), -7, "scale")
+    o = pa.PaOpts()
+    o.flags = 1
+    expect(lib, call_prefill(lib, good_prefill(), opts=o), -7, "flags")
+    a = good_prefill()
+    a[1] = T([40, 8, 128], pa.PA_F16, data=0)
+    expect(lib, call_prefill(lib, a), -1)
+    a = good_prefill()
+    a[1] = T([40, 8, 128], pa.PA_F16, strides=[8 * 128, 128, 2])
+    expect(lib, call_prefill(lib, a), -4)

@@ -1,0 +1,220 @@
+"""GPU parity of the prefill path: the step's new K/V rows go into the cache
+(pa_cache_write), then pa_prefill runs through the C ABI; the fp64 oracle does
+the same on host copies of the generator's bytes.  Nothing expected comes
+from the HIP path.  Run on an MI355X with ``pytest -m gpu``."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_447_amd as pa
+from pa_workloads import get_config, scaled
+from pa_workloads.prefill import PREFILL_CONFIGS, PrefillConfig, make_prefill_inputs, make_prefill_layout
+from tests.gpu_common import NTHREADS, TOL_F32, TOL_OUT, host_inputs, log, max_abs_err
+
+pytestmark = pytest.mark.gpu
+
+
+def P(name, base, q_len):
+    return PrefillConfig(name=name, base=scaled(base, name=name), q_len=q_len)
+
+
+CASES = {
+    # three sequences, 4 query heads per kv head, head_dim 64: 5 / 17 / 33 new tokens
+    "small_gqa4_d64": PREFILL_CONFIGS["prefill_small"],
+    # long prompt chunks on 4 MHA heads, bf16, block 32: the 32-column-per-wavefront tiles
+    "mha_bf16_bs32_wide": P("mha_bf16_bs32_wide",
+                            scaled(get_config("llama7b"), num_seqs=3, num_heads=4, num_kv_heads=4, block_size=32,
+                                   kv_dtype="bf16", q_dtype="bf16", num_blocks=120, max_blocks_per_seq=40,
+                                   ctx_kind="fixed", ctx_fixed=(300, 700, 1000)),
+                            (300, 290, 333)),
+    # speculative verification: 4 draft tokens x 8 heads per kv head
+    "verify_gqa8": P("verify_gqa8",
+                     scaled(get_config("gqa70b"), num_seqs=12, num_blocks=2000, max_blocks_per_seq=64, ctx_lo=4,
+                            ctx_hi=2048), 4),
+    # whole prompts (row 0 at position 0), G = 2, f16, lengths around the 32-token chunk
+    "whole_prompt_gqa2": P("whole_prompt_gqa2",
+                           scaled(get_config("llama7b"), num_seqs=5, num_heads=8, num_kv_heads=4,
+                                  num_blocks=60, max_blocks_per_seq=10, ctx_kind="fixed",
+                                  ctx_fixed=(1, 31, 32, 33, 97)),
+                           (1, 31, 32, 33, 97)),
+    # G = 16 at head_dim 64 in bf16, block 16; several q_len including empty sequences
+    "gqa16_d64_mixed": P("gqa16_d64_mixed",
+                         scaled(get_config("gqa70b"), num_seqs=6, num_heads=32, num_kv_heads=2, head_dim=64,
+                                block_size=16, kv_dtype="bf16", q_dtype="bf16", num_blocks=400,
+                                max_blocks_per_seq=48, ctx_kind="fixed", ctx_fixed=(50, 700, 9, 300, 64, 129),
+                                allocator="shuffled"),
+                         (0, 40, 9, 1, 0, 77)),
+    # MHA f16 block 16, head_dim 128, uneven q_len straddling the 64-column tile
+    "mha_f16_tiles": P("mha_f16_tiles",
+                       scaled(get_config("llama7b"), num_seqs=4, num_heads=6, num_kv_heads=6, num_blocks=300,
+                              max_blocks_per_seq=40, ctx_kind="fixed", ctx_fixed=(63, 64, 65, 600)),
+                       (63, 64, 65, 129)),
+}
+
+
+def setup(pcfg, device="cuda"):
+    pl = make_prefill_layout(pcfg)
+    inp = make_prefill_inputs(pcfg, pl, device)
+    return pl, inp
+
+
+def gpu_step(pcfg, inp, out_dtype=None, stream=None):
+    cfg = pcfg.base
+    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"])
+    out = torch.empty(inp["q"].shape, dtype=out_dtype or inp["q"].dtype, device=inp["q"].device)
+    pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, stream=stream)
+    return out
+
+
+def gpu_prefill(pcfg, inp, out_dtype=None):
+    cfg = pcfg.base
+    out = torch.empty(inp["q"].shape, dtype=out_dtype or inp["q"].dtype, device=inp["q"].device)
+    pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads)
+    return out
+
+
+def oracle_write(host):
+    return oracle.cache_write(host["k_new"], host["v_new"], host["k_cache"], host["v_cache"], host["slot_mapping"],
+                              inplace=True)
+
+
+def _bytes(t):
+    return t.detach().cpu().contiguous().view(torch.uint8)
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_small_prefill_matches_oracle(case):
+    pcfg = CASES[case]
+    cfg = pcfg.base
+    log(f"[{case}] generating")
+    pl, inp = setup(pcfg)
+    host = host_inputs(inp)
+    out = gpu_step(pcfg, inp)
+    out32 = gpu_prefill(pcfg, inp, torch.float32)
+    torch.cuda.synchronize()
+    kc, vc = oracle_write(host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8))
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8))
+    ref = oracle.paged_prefill(host["q"], kc, vc, host["block_tables"], host["context_lens"],
+                               host["query_start_loc"], cfg.softmax_scale, cfg.num_kv_heads, nthreads=NTHREADS)
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    log(f"    rows={out.shape[0]} err={err:.3e} err32={err32:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
+
+
+def sample_rows(pl, per_seq_rows):
+    """(row, sequence, position) triples: the given local rows of every sequence (those it has)."""
+    qsl, ctx = pl.query_start_loc, pl.layout.context_lens
+    picks = []
+    for s in range(len(ctx)):
+        n = int(qsl[s + 1] - qsl[s])
+        for j in sorted({r if r >= 0 else n + r for r in per_seq_rows}):
+            if 0 <= j < n:
+                picks.append((int(qsl[s]) + j, s, int(ctx[s]) - n + j))
+    return picks
+
+
+def oracle_rows(pcfg, host, kc, vc, picks):
+    """Each sampled row on its own: a decode over the context cut after its
+    position (the equivalence the oracle's own tests pin)."""
+    cfg = pcfg.base
+    rows = torch.tensor([r for r, _, _ in picks])
+    seqs = torch.tensor([s for _, s, _ in picks])
+    q = host["q"][rows].contiguous()
+    bt = host["block_tables"][seqs].contiguous()
+    lens = torch.tensor([p + 1 for _, _, p in picks], dtype=torch.int32)
+    return oracle.paged_decode(q, kc, vc, bt, lens, cfg.softmax_scale, cfg.num_kv_heads, nthreads=NTHREADS)
+
+
+@pytest.mark.parametrize("name", ["prefill_7b", "verify_gqa70b"])
+def test_full_size_prefill_sampled_rows(name):
+    """Full-size workloads in the launch configuration the benchmark times:
+    every output finite, and rows at tile edges of every sequence equal to the
+    oracle's."""
+    pcfg = PREFILL_CONFIGS[name]
+    cfg = pcfg.base
+    log(f"[{name}] generating")
+    pl, inp = setup(pcfg)
+    host = host_inputs(inp)
+    out = gpu_step(pcfg, inp)
+    out32 = gpu_prefill(pcfg, inp, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out32).all()
+    kc, vc = oracle_write(host)
+    picks = sample_rows(pl, [0, 1, 15, 16, 63, 64, 127, 128, 255, 256, -2, -1])
+    log(f"[{name}] oracle on {len(picks)} rows")
+    ref = oracle_rows(pcfg, host, kc, vc, picks)
+    rows = torch.tensor([r for r, _, _ in picks], device=out.device)
+    err = max_abs_err(out[rows], ref)
+    err32 = max_abs_err(out32[rows], ref)
+    log(f"    err={err:.3e} err32={err32:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
+
+
+def test_single_row_prefill_is_decode():
+    """q_len = 1 for every sequence: the oracle's decode of the same step."""
+    pcfg = P("one_row", scaled(get_config("gqa70b"), num_seqs=9, num_blocks=800, max_blocks_per_seq=40, ctx_lo=1,
+                               ctx_hi=1200), 1)
+    cfg = pcfg.base
+    pl, inp = setup(pcfg)
+    host = host_inputs(inp)
+    out32 = gpu_step(pcfg, inp, torch.float32)
+    torch.cuda.synchronize()
+    kc, vc = oracle_write(host)
+    ref = oracle.paged_decode(host["q"], kc, vc, host["block_tables"], host["context_lens"], cfg.softmax_scale,
+                              cfg.num_kv_heads, nthreads=NTHREADS)
+    assert max_abs_err(out32, ref) <= TOL_F32[cfg.kv_dtype]
+
+
+def test_rows_before_position_zero_get_zeros_and_others_are_unaffected():
+    """More query rows than context (outside the contract): the rows whose
+    position would be negative are zeros, the rest match the oracle run on the
+    valid rows alone."""
+    pcfg = CASES["small_gqa4_d64"]
+    cfg = pcfg.base
+    pl, inp = setup(pcfg)
+    host = host_inputs(inp)
+    gpu_step(pcfg, inp)
+    # sequence 1's context cut to 3 tokens fewer than its 17 query rows
+    ctx = inp["context_lens"].clone()
+    ctx[1] = int(pl.q_lens[1]) - 3
+    out = torch.empty(inp["q"].shape, dtype=torch.float32, device="cuda")
+    pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], ctx, inp["query_start_loc"],
+               cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads)
+    torch.cuda.synchronize()
+    kc, vc = oracle_write(host)
+    qsl = pl.query_start_loc
+    lo = int(qsl[1])
+    assert torch.count_nonzero(out[lo: lo + 3]).item() == 0
+    picks = [(lo + j, 1, j - 3) for j in range(3, int(pl.q_lens[1]))]
+    ref = oracle_rows(pcfg, host, kc, vc, picks)
+    rows = torch.tensor([r for r, _, _ in picks], device="cuda")
+    assert max_abs_err(out[rows], ref) <= TOL_F32[cfg.kv_dtype]
+    # the other sequences are untouched by the change
+    others = [r for s in (0, 2) for r in range(int(qsl[s]), int(qsl[s + 1]))]
+    full = oracle.paged_prefill(host["q"], kc, vc, host["block_tables"], host["context_lens"],
+                                host["query_start_loc"], cfg.softmax_scale, cfg.num_kv_heads)
+    assert max_abs_err(out[torch.tensor(others, device="cuda")], full[others]) <= TOL_F32[cfg.kv_dtype]
+
+
+def test_prefill_repeats_bit_identically_and_on_a_side_stream():
+    pcfg = CASES["mha_bf16_bs32_wide"]
+    pl, inp = setup(pcfg)
+    a = gpu_step(pcfg, inp)
+    b = gpu_prefill(pcfg, inp)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        c = torch.empty_like(a)
+        cfg = pcfg.base
+        pa.prefill(c, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, stream=s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
