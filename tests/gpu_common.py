@@ -67,6 +67,23 @@ def max_abs_err(out: torch.Tensor, ref: np.ndarray) -> float:
     return float(np.abs(got - ref).max()) if got.size else 0.0
 
 
+# Half an ulp, relative to the magnitude: the most that storing a value in the
+# output dtype can move it.  Prefill rows near position 0 average a handful of
+# V rows, so |out| reaches 2-4, where a bf16 half-ulp (2^-8 |x|) alone exceeds
+# 2e-3; stored 16-bit outputs are therefore held to TOL_OUT beyond their own
+# rounding (the fp32-output checks bound the kernel's error without it).
+OUT_ROUNDING = {torch.float16: 2.0**-11, torch.bfloat16: 2.0**-8, torch.float32: 0.0}
+
+
+def max_err_beyond_rounding(out: torch.Tensor, ref: np.ndarray) -> float:
+    got = out.detach().cpu().to(torch.float64).numpy()
+    assert np.isfinite(got).all(), "non-finite output"
+    if not got.size:
+        return 0.0
+    u = OUT_ROUNDING[out.dtype]
+    return float((np.abs(got - ref) - u * np.maximum(np.abs(got), np.abs(ref))).max())
+
+
 def setup(cfg, device="cuda"):
     layout = make_layout(cfg)
     inp = make_inputs(cfg, layout, device)
