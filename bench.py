@@ -1,6 +1,10 @@
-"""Paged decode benchmark on one MI355X.
+"""Paged decode (and prefill) benchmark on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+With a prefill workload as --config (prefill_7b, verify_gqa70b, prefill_small)
+a step is instead the cache write of every new token of the step followed by
+pa_prefill over all query rows, and the line reports attention TFLOP/s.
 
 A step is one pass of the whole hot path over one batch: the cache write of
 each sequence's new token, then paged decode (one launch: balanced
@@ -50,28 +54,33 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["pa_sched.h", "pa_device.h", "pa_internal.h", "decode_valu.hip", "decode_mfma.hip"]
+KERNEL_SOURCES = {
+    "decode": ["pa_sched.h", "pa_device.h", "pa_internal.h", "mfma_core.h", "decode_valu.hip", "decode_mfma.hip"],
+    "prefill": ["pa_device.h", "pa_internal.h", "mfma_core.h", "prefill_mfma.hip"],
+}
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, TFLOP/s
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kind: str = "decode") -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(ROOT, "paged_kv_cache_447_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed counter summary, or None if
-    there is none for this workload or the kernel sources changed since."""
+def measured_traffic(workload: str, kind: str = "decode"):
+    """HBM bytes per launch of the workload's main kernel from the committed
+    counter summary, or None if there is none for this workload or the kernel
+    sources changed since."""
     try:
         with open(TRAFFIC) as f:
             rec = json.load(f).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(kind):
         return None
     return rec.get("bytes_per_launch")
 
@@ -96,6 +105,12 @@ def main():
     pa.load_library()  # fails loudly if libpa.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    from pa_workloads.prefill import PREFILL_CONFIGS
+
+    if args.config in PREFILL_CONFIGS:
+        print(json.dumps(bench_prefill(args, PREFILL_CONFIGS[args.config], dev)), flush=True)
+        return
 
     cfg = get_config(args.config)
     part = cfg.partition_size if args.partition_size < 0 else args.partition_size
@@ -248,6 +263,167 @@ def main():
             "tokens_per_s": round(cfg.num_seqs * reps / el, 2),
         }
     print(json.dumps(result), flush=True)
+
+
+def bench_prefill(args, pcfg, dev) -> dict:
+    """One step = cache write of the step's new K/V rows, then pa_prefill over
+    every query row.  Same protocol as decode: rotating input sets, warmup,
+    whole steps timed back to back, then HIP events around the prefill launch."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_447_amd as pa
+    from pa_workloads.generate import ELEM_BYTES
+    from pa_workloads.prefill import make_prefill_inputs, make_prefill_layout, prefill_flops, prefill_kv_bytes
+
+    cfg = pcfg.base
+    pl = make_prefill_layout(pcfg)
+    ctx = pl.layout.context_lens
+    N = int(pl.query_start_loc[-1])
+    flops = prefill_flops(pcfg, pl)
+    kvb = prefill_kv_bytes(pcfg, pl)
+    eq = ELEM_BYTES[cfg.q_dtype]
+    # what the prefill launch must move at least: every context K/V row once
+    # per (sequence, kv head), the queries, the outputs, the table entries read
+    alg_bytes = kvb + 2 * N * cfg.num_heads * cfg.head_dim * eq + 4 * int(np.sum(-(-ctx // cfg.block_size))) + \
+        4 * (2 * cfg.num_seqs + 1)
+    pool_bytes = 2 * cfg.num_blocks * cfg.block_size * cfg.num_kv_heads * cfg.head_dim * ELEM_BYTES[cfg.kv_dtype]
+    nsets = max(2, math.ceil(1e9 / max(1, kvb)))
+    nsets = min(nsets, max(2, int(40e9 // pool_bytes)))
+    sets = []
+    for i in range(nsets):
+        inp = make_prefill_inputs(pcfg, pl, dev, seed_offset=i)
+        inp["out"] = torch.empty_like(inp["q"])
+        sets.append(inp)
+    host0 = None
+    if not args.no_cpu_baseline:
+        host0 = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in sets[0].items() if k != "out"}
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def write(inp):
+        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"], stream=sptr)
+
+    def prefill(inp):
+        pa.prefill(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, stream=sptr)
+
+    for i in range(args.warmup):
+        write(sets[i % nsets])
+        prefill(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        write(sets[i % nsets])
+        prefill(sets[i % nsets])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        inp = sets[i % nsets]
+        write(inp)
+        evs[i][0].record(stream)
+        prefill(inp)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    for inp in sets:
+        if not torch.isfinite(inp["out"]).all():
+            raise RuntimeError("non-finite prefill output")
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ridge = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = flops / alg_bytes >= ridge
+    tflops = flops / (kernel_ms * 1e-3) / 1e12
+    gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof.update({
+        "traffic": measured_traffic(cfg.name, "prefill"),
+        "kernel": "prefill (paged K/V gather + causal QK + online softmax + PV)",
+        "kernel_ms": round(kernel_ms, 5),
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": alg_bytes,
+        "flops_per_byte": round(flops / alg_bytes, 2),
+    })
+    result = {
+        "metric": "paged prefill attention TFLOP/s (causal flops per step / step time) at 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded block allocator)",
+        "config": {
+            "workload": cfg.name,
+            "num_seqs": cfg.num_seqs,
+            "query_rows": N,
+            "num_heads": cfg.num_heads,
+            "num_kv_heads": cfg.num_kv_heads,
+            "head_dim": cfg.head_dim,
+            "block_size": cfg.block_size,
+            "kv_dtype": cfg.kv_dtype,
+            "mean_context": float(np.mean(ctx)),
+            "input_sets": nsets,
+        },
+        "query_tokens_per_s": round(N / (ms_per_step * 1e-3), 1),
+        "kv_gb_per_s": round(kvb / (ms_per_step * 1e-3) / 1e9, 2),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if host0 is not None:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        nthreads = max(1, min(cores, 64))
+        kc, vc = oracle.cache_write(host0["k_new"], host0["v_new"], host0["k_cache"], host0["v_cache"],
+                                    host0["slot_mapping"], inplace=True)
+        # the sample: the step's first sequence (all of its query rows), repeated
+        qsl = host0["query_start_loc"]
+        n0 = int(qsl[1])
+        q0 = host0["q"][:n0].contiguous()
+        sub_flops = 4 * cfg.head_dim * cfg.num_heads * (n0 * (int(ctx[0]) - n0) + n0 * (n0 + 1) // 2)
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            oracle.paged_prefill(q0, kc, vc, host0["block_tables"][:1], host0["context_lens"][:1],
+                                 qsl[:2].contiguous(), cfg.softmax_scale, cfg.num_kv_heads, nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {
+            "value": round(sub_flops * reps / el / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{reps} x the fp64 prefill of sequence 0 of {cfg.name} ({n0} query rows, context "
+                      f"{int(ctx[0])}, all {cfg.num_heads} heads), {el:.1f} s wall, {nthreads} threads",
+        }
+    return result
 
 
 if __name__ == "__main__":

@@ -18,11 +18,11 @@
 // them as NC MfmaCore column sets (mfma_core.h).  A column's scores are masked
 // past its own position, so one chunk pass serves rows with different limits.
 // The workgroup streams the K and V rows of positions 0 .. (its last row's
-// position) in 32-token chunks through a three-slot LDS ring: each wavefront
-// loads an eighth of every chunk straight from HBM into LDS, and one barrier
-// per chunk both publishes a chunk to all four wavefronts and frees the slot
-// that the next loads go into, so two chunks are in flight during each
-// chunk's arithmetic.  Every wavefront reads the K operands and transposed V
+// position) in 32-token chunks through an LDS ring of R slots (80 KB, so that
+// two workgroups share a CU): each wavefront loads a quarter of every chunk
+// straight from HBM into LDS, and one barrier per chunk both publishes a chunk
+// to all four wavefronts and frees the slot that the next loads go into, so
+// R - 1 chunks are in flight during each chunk's arithmetic.  Every wavefront reads the K operands and transposed V
 // operands of the chunk from LDS and multiplies them into all NC of its
 // column sets.
 #include "mfma_core.h"
@@ -34,8 +34,8 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 4;  // wavefronts per workgroup, sharing one K/V stream
-constexpr int kRing = 3;   // chunk slots of the LDS ring
+constexpr int kWaves = 4;            // wavefronts per workgroup, sharing one K/V stream
+constexpr int kLdsPerWG = 80 * 1024;  // two workgroups per CU share its 160 KB of LDS
 
 typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ lds_void *lds_addr(char *p) { return (lds_void *)p; }
@@ -54,8 +54,8 @@ __device__ __forceinline__ void seq_rows(const PrefillArgs &a, int i, int &lo, i
 }
 
 // The sequence and tile of tile slot t: sequences in order, each cut into
-// ceil(rows * G / tile_cols) tiles.  false if t is past the last tile.  All
-// results are wave-uniform.
+// ceil(rows * G / tile_cols) tiles, taken last tile first.  false if t is past
+// the last tile.  All results are wave-uniform.
 __device__ bool locate_tile(const PrefillArgs &a, int t, int lane, int &seq, int &tile) {
   int carry = 0;
   for (int base = 0; base < a.num_seqs; base += 64) {
@@ -71,7 +71,8 @@ __device__ bool locate_tile(const PrefillArgs &a, int t, int lane, int &seq, int
     if (t < carry + total) {
       const int k = uniform(__builtin_ctzll(__ballot(carry + incl > t)));
       seq = base + k;
-      tile = t - carry - uniform(__shfl(incl - tiles, k));
+      // a sequence's last tile (whose rows see the most positions) first
+      tile = uniform(__shfl(incl, k)) - 1 - (t - carry);
       return true;
     }
     carry += total;
@@ -89,11 +90,12 @@ struct PrefillTile {
   static constexpr int HB = Slot::HB;                 // bytes of the K (or V) rows of a chunk
   static constexpr int PER = Slot::NLD / kWaves;      // DMA instructions per wavefront per K (or V) chunk
   static constexpr int CB = 2 * HB;                   // bytes of a ring slot: K rows, then V rows
-  static constexpr int kLdsBytes = kRing * CB;
+  static constexpr int R = kLdsPerWG / CB < 8 ? kLdsPerWG / CB : 8;  // ring slots
+  static constexpr int kLdsBytes = R * CB;
   static constexpr int LOG2BS = BS == 16 ? 4 : 5;
   static_assert(Slot::NLD % kWaves == 0, "every wavefront loads the same share of a chunk");
   static_assert(Slot::RPI * PER == 8, "a wavefront's share is 8 rows inside one 16-token tile");
-  static_assert(kLdsBytes <= 64 * 1024, "two workgroups fit the LDS of a CU");
+  static_assert(R >= 3 && 2 * (R - 2) * PER < 64, "ring depth within the wait counter's range");
 
   const PrefillArgs &a;
   char *const ring;
@@ -193,9 +195,9 @@ struct PrefillTile {
     }
   }
 
-  __device__ __forceinline__ void compute(int c) {
+  __device__ __forceinline__ void compute(int c, int slot) {
     const int cs = CT * c;
-    const char *ks = ring + (c % kRing) * CB;
+    const char *ks = ring + slot * CB;
     u32x4 kop[2][KS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -216,21 +218,25 @@ struct PrefillTile {
     for (int ct = 0; ct < NC; ++ct) core[ct].reset();
     load_q();
     const int nch = last_max / CT + 1;
-    // every chunk index issued is loaded (past nch it reloads the last rows
-    // into a slot that nobody reads), so each wavefront always has exactly
-    // 2 PER loads per chunk outstanding behind the one awaited
-    issue(0, block_of(0), 0);
-    issue(1, block_of(1), 1);
-    int nblk = block_of(2);
+    // Chunks c .. c + R - 2 are in flight while chunk c is computed.  Every
+    // chunk index issued is loaded (past nch it reloads the last rows into a
+    // slot that nobody reads), so each wavefront always has exactly
+    // (R - 2) * 2 PER loads outstanding behind the chunk it waits for.
+#pragma unroll
+    for (int c = 0; c < R - 1; ++c) issue(c, block_of(c), c);
+    int nblk = block_of(R - 1);
+    int slot = 0, islot = R - 1;  // ring slots of chunk c and of chunk c + R - 1
     for (int c = 0; c < nch; ++c) {
-      wait_vm<2 * PER>();  // this wavefront's share of chunk c (and the queries before it) has landed
-      wg_barrier();        // every share of chunk c has; everybody is done with chunk c - 1
+      wait_vm<(R - 2) * 2 * PER>();  // this wavefront's share of chunk c (and the queries before it) has landed
+      wg_barrier();                   // every share of chunk c has; everybody is done with chunk c - 1
       __builtin_amdgcn_sched_barrier(0);
-      issue(c + 2, nblk, (c + 2) % kRing);
-      nblk = block_of(c + 3);
+      issue(c + R - 1, nblk, islot);
+      nblk = block_of(c + R);
       __builtin_amdgcn_sched_barrier(0);
-      if (CT * c <= wlast) compute(c);
+      if (CT * c <= wlast) compute(c, slot);
       __builtin_amdgcn_sched_barrier(0);
+      slot = slot + 1 == R ? 0 : slot + 1;
+      islot = islot + 1 == R ? 0 : islot + 1;
     }
     wait_vm<0>();  // no load may land after the workgroup's LDS is released
 #pragma unroll
@@ -265,7 +271,7 @@ struct PrefillTile {
 };
 
 template <typename MT, int D, int BS, int NC>
-__global__ void __launch_bounds__(64 * kWaves) prefill_mfma(const PrefillArgs a) {
+__global__ void __launch_bounds__(64 * kWaves, 2) prefill_mfma(const PrefillArgs a) {
   typedef PrefillTile<MT, D, BS, NC> Tile;
   __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
   const int lane = threadIdx.x & 63;
