@@ -125,7 +125,7 @@ def main():
     sets = []
     for i in range(nsets):
         inp = make_inputs(cfg, layout, dev, seed_offset=i)
-        inp["out"] = torch.empty_like(inp["q"])
+        inp["out"] = torch.zeros_like(inp["q"])  # sets that a short run never reaches stay finite
         inp["ws"] = pa.new_workspace(inp["q"], cfg.num_kv_heads, args.num_workers)
         sets.append(inp)
     host0 = None
@@ -274,7 +274,8 @@ def bench_prefill(args, pcfg, dev) -> dict:
 
     import paged_kv_cache_447_amd as pa
     from pa_workloads.generate import ELEM_BYTES
-    from pa_workloads.prefill import make_prefill_inputs, make_prefill_layout, prefill_flops, prefill_kv_bytes
+    from pa_workloads.prefill import (make_prefill_inputs, make_prefill_layout, prefill_algorithmic_bytes,
+                                      prefill_flops, prefill_kv_bytes)
 
     cfg = pcfg.base
     pl = make_prefill_layout(pcfg)
@@ -282,18 +283,14 @@ def bench_prefill(args, pcfg, dev) -> dict:
     N = int(pl.query_start_loc[-1])
     flops = prefill_flops(pcfg, pl)
     kvb = prefill_kv_bytes(pcfg, pl)
-    eq = ELEM_BYTES[cfg.q_dtype]
-    # what the prefill launch must move at least: every context K/V row once
-    # per (sequence, kv head), the queries, the outputs, the table entries read
-    alg_bytes = kvb + 2 * N * cfg.num_heads * cfg.head_dim * eq + 4 * int(np.sum(-(-ctx // cfg.block_size))) + \
-        4 * (2 * cfg.num_seqs + 1)
+    alg_bytes = prefill_algorithmic_bytes(pcfg, pl)
     pool_bytes = 2 * cfg.num_blocks * cfg.block_size * cfg.num_kv_heads * cfg.head_dim * ELEM_BYTES[cfg.kv_dtype]
     nsets = max(2, math.ceil(1e9 / max(1, kvb)))
     nsets = min(nsets, max(2, int(40e9 // pool_bytes)))
     sets = []
     for i in range(nsets):
         inp = make_prefill_inputs(pcfg, pl, dev, seed_offset=i)
-        inp["out"] = torch.empty_like(inp["q"])
+        inp["out"] = torch.zeros_like(inp["q"])  # sets that a short run never reaches stay finite
         sets.append(inp)
     host0 = None
     if not args.no_cpu_baseline:

@@ -171,3 +171,15 @@ def prefill_kv_bytes(pcfg: PrefillConfig, pl: PrefillLayout) -> int:
     cfg = pcfg.base
     return int(2 * int(pl.layout.context_lens.astype(np.int64).sum()) * cfg.num_kv_heads * cfg.head_dim
                * ELEM_BYTES[cfg.kv_dtype])
+
+
+def prefill_algorithmic_bytes(pcfg: PrefillConfig, pl: PrefillLayout) -> int:
+    """Bytes a prefill launch must move at least: every context K/V row once per
+    (sequence, kv head), the queries, the outputs (query dtype), the block-table
+    entries it reads, the context lengths and query offsets."""
+    cfg = pcfg.base
+    N = int(pl.query_start_loc[-1])
+    ctx = pl.layout.context_lens.astype(np.int64)
+    eq = ELEM_BYTES[cfg.q_dtype]
+    return int(prefill_kv_bytes(pcfg, pl) + 2 * N * cfg.num_heads * cfg.head_dim * eq
+               + 4 * int(np.sum(-(-ctx // cfg.block_size))) + 4 * (2 * cfg.num_seqs + 1))
