@@ -180,6 +180,52 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_sc
     return kc, vc
 
 
+def copy_blocks(dst_cache, src_cache, block_mapping, inplace: bool = False):
+    """Reference block copy; returns the destination pool as a CPU tensor.
+
+    For every pair (s, d) of ``block_mapping`` ([M, 2]), block d of the
+    destination pool becomes a byte copy of block s of the source pool.  This
+    is the copy that a write into a shared, partly filled block needs first
+    (page "vLLM框架中的KV cache优化与PagedAttention机制详解", section 5.1, step 4:
+    shared blocks are copied before they are modified), and the move of whole
+    blocks between GPU and CPU memory (page "Paged KVCache：大模型推理显存管理优化方案",
+    section 5, blocks migrating between memory tiers).  A pair with a negative
+    id is skipped.  Raises OracleError for an id past its pool, a destination
+    named twice, or -- when both pools are the same tensor -- a destination
+    that is also a source (the result would depend on the order of copies).
+    Pools are [num_blocks, ...] of any dtype; only bytes move."""
+    import torch
+
+    same = dst_cache is src_cache or (dst_cache.data_ptr() == src_cache.data_ptr()
+                                      and dst_cache.device == src_cache.device)
+    src = _host(src_cache)
+    if inplace:
+        dst = dst_cache
+        if dst.device.type != "cpu" or not dst.is_contiguous():
+            raise ValueError("inplace copy_blocks needs a contiguous CPU pool")
+    else:
+        dst = _host(dst_cache).clone()
+    if same:
+        src = dst
+    if tuple(src.shape[1:]) != tuple(dst.shape[1:]) or src.dtype != dst.dtype:
+        raise ValueError("pools differ in block shape or dtype")
+    pairs = [(int(a), int(b)) for a, b in _host(block_mapping, torch.int64).reshape(-1, 2).tolist()]
+    live = [(a, b) for a, b in pairs if a >= 0 and b >= 0]
+    for a, b in live:
+        if a >= src.shape[0] or b >= dst.shape[0]:
+            raise OracleError("copy_blocks: block id outside the pool")
+    dsts = [b for _, b in live]
+    if len(set(dsts)) != len(dsts):
+        raise OracleError("copy_blocks: a destination block is named twice")
+    if same and set(dsts) & {a for a, _ in live}:
+        raise OracleError("copy_blocks: a destination block is also a source")
+    sb = src.view(torch.uint8).reshape(src.shape[0], -1)
+    db = dst.view(torch.uint8).reshape(dst.shape[0], -1)
+    for a, b in live:
+        db[b] = sb[a]
+    return dst
+
+
 def f16_to_double(bits: int) -> float:
     return _load().oracle_f16_to_double(bits)
 
