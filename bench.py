@@ -4,7 +4,9 @@
 
 With a prefill workload as --config (prefill_7b, verify_gqa70b, prefill_small)
 a step is instead the cache write of every new token of the step followed by
-pa_prefill over all query rows, and the line reports attention TFLOP/s.
+pa_prefill over all query rows, and the line reports attention TFLOP/s.  With
+a block-copy workload (cow_llama7b, swap_out_gqa70b, swap_in_gqa70b) a step is
+one pa_copy_blocks launch, and the line reports bytes moved per second.
 
 A step is one pass of the whole hot path over one batch: the cache write of
 each sequence's new token, then paged decode (one launch: balanced
@@ -57,7 +59,9 @@ TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode": ["pa_sched.h", "pa_device.h", "pa_internal.h", "mfma_core.h", "decode_valu.hip", "decode_mfma.hip"],
     "prefill": ["pa_device.h", "pa_internal.h", "mfma_core.h", "prefill_mfma.hip"],
+    "blocks": ["pa_device.h", "pa_internal.h", "block_copy.hip"],
 }
+HOST_LINK_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction, GB/s
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, TFLOP/s
 
 
@@ -110,6 +114,11 @@ def main():
 
     if args.config in PREFILL_CONFIGS:
         print(json.dumps(bench_prefill(args, PREFILL_CONFIGS[args.config], dev)), flush=True)
+        return
+    from pa_workloads.blocks import BLOCK_CONFIGS
+
+    if args.config in BLOCK_CONFIGS:
+        print(json.dumps(bench_blocks(args, BLOCK_CONFIGS[args.config], dev)), flush=True)
         return
 
     cfg = get_config(args.config)
@@ -419,6 +428,127 @@ def bench_prefill(args, pcfg, dev) -> dict:
             "kind": "oracle",
             "sample": f"{reps} x the fp64 prefill of sequence 0 of {cfg.name} ({n0} query rows, context "
                       f"{int(ctx[0])}, all {cfg.num_heads} heads), {el:.1f} s wall, {nthreads} threads",
+        }
+    return result
+
+
+def bench_blocks(args, cfg, dev) -> dict:
+    """One step = one pa_copy_blocks launch over the workload's pairs, rotating
+    over independent pool sets; HIP events around each launch."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_447_amd as pa
+    from pa_workloads.blocks import block_mapping, pool_shapes, random_pool
+
+    src_shape, dst_shape, src_host, dst_host = pool_shapes(cfg)
+    m = torch.from_numpy(block_mapping(cfg)).to(dev)
+    dt = cfg.base.kv_dtype
+    moved = cfg.bytes_moved()  # K and V, read + written
+    nsets = 2
+    sets = []
+    for i in range(nsets):
+        base = 1000 * cfg.seed + 10 * i
+        sk = random_pool(src_shape, dt, base + 1, dev, pin=src_host)
+        sv = random_pool(src_shape, dt, base + 2, dev, pin=src_host)
+        if cfg.kind == "cow":
+            dk, dv = sk, sv
+        else:
+            dk = random_pool(dst_shape, dt, base + 3, dev, pin=dst_host)
+            dv = random_pool(dst_shape, dt, base + 4, dev, pin=dst_host)
+        sets.append((dk, dv, sk, sv))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step(i):
+        dk, dv, sk, sv = sets[i % nsets]
+        pa.copy_blocks(dk, dv, sk, sv, m, stream=sptr)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    value = moved / (ms_per_step * 1e-3) / 1e9
+    if cfg.kind == "cow":
+        ach = moved / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": moved}
+    else:
+        link = moved // 2  # the bytes that cross the host link, in one direction
+        ach = link / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "host-link", "achieved": round(ach, 2), "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HOST_LINK_PEAK_GBS, 4), "algorithmic_bytes_per_launch": link}
+    roof.update({"traffic": measured_traffic(cfg.name, "blocks") if cfg.kind == "cow" else None,
+                 "kernel": "copy_blocks (whole-block gather/scatter by a block mapping)",
+                 "kernel_ms": round(kernel_ms, 5)})
+    result = {
+        "metric": "paged block copy GB/s (K and V bytes read + written per step / step time) at 1 GPU",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic (seeded pools and block mapping)",
+        "config": {"workload": cfg.name, "kind": cfg.kind, "num_pairs": cfg.num_pairs,
+                   "block_bytes": cfg.block_bytes, "kv_dtype": dt, "device_blocks": cfg.base.num_blocks,
+                   "input_sets": nsets},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        dk, dv, sk, sv = sets[0]
+        hs_k, hs_v = sk.cpu(), sv.cpu()
+        hd_k = hs_k if cfg.kind == "cow" else dk.cpu()
+        hd_v = hs_v if cfg.kind == "cow" else dv.cpu()
+        mh = m.cpu()
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            oracle.copy_blocks(hd_k, hs_k, mh, inplace=True)
+            oracle.copy_blocks(hd_v, hs_v, mh, inplace=True)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {
+            "value": round(moved * reps / el / 1e9, 3),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} full {cfg.name} copies on host copies of the pools, {el:.1f} s wall, one thread",
         }
     return result
 

@@ -1,7 +1,7 @@
 /*
  * pa.h -- C ABI of the paged-KV attention library (libpa.so) for AMD gfx950.
  *
- * Three operations, all defined on the pages this library follows:
+ * Four operations, all defined on the pages this library follows:
  *
  *   pa_decode       attention of one query token per head over a KV cache kept
  *                   in fixed-size physical blocks, found through a per-sequence
@@ -21,6 +21,11 @@
  *   pa_cache_write  scatter of new tokens' K/V rows into physical slots
  *                   (slot = block * block_size + offset, the address rule of
  *                   page "Paged KVCache：大模型推理显存管理优化方案", section 2.3).
+ *   pa_copy_blocks  copies of whole blocks, between or within pools: the
+ *                   private copy a sequence takes of a shared block before
+ *                   writing into it (section 5.1, step 4, of the first page
+ *                   above), and the swap of blocks between GPU memory and host
+ *                   memory (section 5 of the page just cited).
  *
  * Conventions shared by every entry point
  *   - Every buffer is device memory owned by the caller.  No call allocates or
@@ -195,6 +200,35 @@ PA_API pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_te
  */
 PA_API pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor v_cache,
                                 pa_tensor slot_mapping, const pa_opts *opts);
+
+/*
+ * pa_copy_blocks -- copy whole blocks from one pool to another (or within one).
+ *
+ *   dst_k_cache, dst_v_cache  [dst_blocks, block_size, num_kv_heads, head_dim]
+ *   src_k_cache, src_v_cache  [src_blocks, block_size, num_kv_heads, head_dim]
+ *                             any one dtype for all four; the same block shape;
+ *                             each block one contiguous run of bytes (the cache
+ *                             layout of pa_decode); K and V pools of a side have
+ *                             the same number of blocks and block stride.  Each
+ *                             pool is device memory or pinned host memory
+ *                             (hipHostMalloc, torch pin_memory): a swap-out
+ *                             copies device -> host, a swap-in host -> device,
+ *                             copy-on-write device -> device in one pool (pass
+ *                             the same tensors as source and destination).
+ *   block_mapping             [num_pairs, 2] PA_I64 or PA_I32, device or pinned
+ *                             host memory: pair (s, d) makes K and V block d of
+ *                             the destination a byte copy of block s of the
+ *                             source.  Pairs with an id < 0 or past its pool are
+ *                             skipped.  Destinations must be distinct and, within
+ *                             one pool, no destination may also be a source;
+ *                             otherwise the result is unspecified (never a fault).
+ *   opts                      stream only (flags must be 0).
+ * Errors: PA_ERR_ARG if a pointer is neither device memory nor pinned host
+ * memory (pageable host memory is refused before anything is enqueued).
+ * Work: one launch, a workgroup per (pair, K or V, 16 KB of the block).
+ */
+PA_API pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor src_k_cache,
+                                pa_tensor src_v_cache, pa_tensor block_mapping, const pa_opts *opts);
 
 /* Static description of a status code. */
 PA_API const char *pa_status_string(pa_status s);

@@ -19,6 +19,7 @@ __all__ = [
     "decode",
     "prefill",
     "cache_write",
+    "copy_blocks",
     "workspace_size",
     "num_workers",
     "new_workspace",
@@ -96,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_prefill.restype = i32
     lib.pa_prefill.argtypes = [PaTensor] * 7 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_copy_blocks.restype = i32
+    lib.pa_copy_blocks.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
     lib.pa_cache_write.restype = i32
     lib.pa_cache_write.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -236,3 +239,28 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_sc
     if st != 0:
         _raise(lib, st)
     return k_cache, v_cache
+
+
+def copy_blocks(dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mapping, stream=None):
+    """pa_copy_blocks: for each pair (s, d) of block_mapping [M, 2], K and V block d
+    of the destination pools become copies of block s of the source pools.  Pools
+    and the mapping may be GPU tensors or pinned CPU tensors (swap out / in)."""
+    lib = load_library()
+    for t in (dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mapping):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("pools and mapping must be GPU tensors or pinned CPU tensors")
+    o = PaOpts()
+    dev = next((t for t in (dst_k_cache, src_k_cache, block_mapping) if t.is_cuda), None)
+    if stream is not None:
+        o.stream = stream
+    elif dev is not None:
+        o.stream = _current_stream(dev)
+    else:
+        import torch
+
+        o.stream = torch.cuda.current_stream().cuda_stream
+    st = lib.pa_copy_blocks(describe(dst_k_cache), describe(dst_v_cache), describe(src_k_cache),
+                            describe(src_v_cache), describe(block_mapping), ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return dst_k_cache, dst_v_cache

@@ -112,6 +112,29 @@ WsLayout workspace_layout(int64_t S, int64_t H, int64_t Hkv, int64_t D, int64_t 
   return l;
 }
 
+// The device address of memory the GPU can reach: device memory, or pinned
+// host memory mapped into the device's address space.  Pageable host memory
+// (or anything unknown to the runtime) is refused, so a kernel never touches it.
+pa_status device_address(const void *p, const char *name, void **dev) {
+  hipPointerAttribute_t at;
+  std::memset(&at, 0, sizeof at);
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_ARG, "%s: not device memory or pinned host memory", name);
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *dev = const_cast<void *>(p);
+    return PA_OK;
+  }
+  if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    // the mapped alias of this byte (the attributes describe the allocation's base)
+    const char *hbase = static_cast<const char *>(at.hostPointer ? at.hostPointer : p);
+    *dev = static_cast<char *>(at.devicePointer) + (static_cast<const char *>(p) - hbase);
+    return PA_OK;
+  }
+  return fail(PA_ERR_ARG, "%s: not device memory or pinned host memory", name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,6 +435,70 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   if (a.block_size <= 0) return fail(PA_ERR_SHAPE, "block_size must be positive");
   hipError_t e = pa::launch_cache_write(a, static_cast<hipStream_t>(o.stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache-write kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor src_k_cache, pa_tensor src_v_cache,
+                         pa_tensor block_mapping, const pa_opts *opts) {
+  pa_opts o;
+  std::memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  pa_status st;
+  const pa_tensor *pools[4] = {&dst_k_cache, &dst_v_cache, &src_k_cache, &src_v_cache};
+  const char *names[4] = {"dst_k_cache", "dst_v_cache", "src_k_cache", "src_v_cache"};
+  for (int i = 0; i < 4; ++i)
+    if ((st = check_tensor(*pools[i], names[i], 4, true))) return st;
+  if ((st = check_tensor(block_mapping, "block_mapping", 2, false))) return st;
+  if (block_mapping.dtype != PA_I64 && block_mapping.dtype != PA_I32)
+    return fail(PA_ERR_DTYPE, "block_mapping: dtype must be I64 or I32");
+  if (block_mapping.shape[1] != 2) return fail(PA_ERR_SHAPE, "block_mapping must be [num_pairs, 2]");
+  const int eb = elem_bytes(src_k_cache.dtype);
+  for (int i = 0; i < 4; ++i) {
+    const pa_tensor &t = *pools[i];
+    if (t.dtype != src_k_cache.dtype) return fail(PA_ERR_DTYPE, "%s: dtype differs from src_k_cache", names[i]);
+    for (int j = 1; j < 4; ++j)
+      if (t.shape[j] != src_k_cache.shape[j])
+        return fail(PA_ERR_SHAPE, "%s: block shape differs from src_k_cache in dim %d", names[i], j);
+    if (t.stride[2] != t.shape[3] || t.stride[1] != t.shape[2] * t.shape[3])
+      return fail(PA_ERR_LAYOUT, "%s: each block must be one contiguous run", names[i]);
+  }
+  if (dst_k_cache.shape[0] != dst_v_cache.shape[0] || src_k_cache.shape[0] != src_v_cache.shape[0])
+    return fail(PA_ERR_SHAPE, "K and V pools of one side must have the same number of blocks");
+  if (dst_k_cache.stride[0] != dst_v_cache.stride[0] || src_k_cache.stride[0] != src_v_cache.stride[0])
+    return fail(PA_ERR_LAYOUT, "K and V pools of one side must have the same block stride");
+  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  const int64_t M = block_mapping.shape[0];
+  const int64_t block_bytes = src_k_cache.shape[1] * src_k_cache.shape[2] * src_k_cache.shape[3] * eb;
+  if (M == 0 || block_bytes == 0 || src_k_cache.shape[0] == 0 || dst_k_cache.shape[0] == 0) return PA_OK;
+  if (block_bytes % 16) return fail(PA_ERR_LAYOUT, "a block of %lld bytes is not a whole number of 16-byte vectors",
+                                    (long long)block_bytes);
+  const int64_t pieces = pa::copy_blocks_pieces(block_bytes);
+  if (M * 2 * pieces > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many block pairs");
+  if (block_mapping.stride[1] != 1) return fail(PA_ERR_LAYOUT, "block_mapping: pairs must be contiguous");
+
+  pa::BlockCopyArgs a;
+  std::memset(&a, 0, sizeof a);
+  void *dev[5];
+  const void *ptrs[5] = {dst_k_cache.data, dst_v_cache.data, src_k_cache.data, src_v_cache.data, block_mapping.data};
+  const char *pnames[5] = {"dst_k_cache", "dst_v_cache", "src_k_cache", "src_v_cache", "block_mapping"};
+  for (int i = 0; i < 5; ++i)
+    if ((st = device_address(ptrs[i], pnames[i], &dev[i]))) return st;
+  a.dst_k = static_cast<char *>(dev[0]);
+  a.dst_v = static_cast<char *>(dev[1]);
+  a.src_k = static_cast<const char *>(dev[2]);
+  a.src_v = static_cast<const char *>(dev[3]);
+  a.mapping = dev[4];
+  a.map_i64 = block_mapping.dtype == PA_I64;
+  a.map_stride = block_mapping.stride[0];
+  a.num_pairs = M;
+  a.block_bytes = block_bytes;
+  a.src_stride = src_k_cache.stride[0] * eb;
+  a.dst_stride = dst_k_cache.stride[0] * eb;
+  a.src_blocks = src_k_cache.shape[0];
+  a.dst_blocks = dst_k_cache.shape[0];
+  a.pieces = (int32_t)pieces;
+  hipError_t e = pa::launch_copy_blocks(a, static_cast<hipStream_t>(o.stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "block-copy kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

@@ -73,6 +73,23 @@ struct PrefillArgs {
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype
 };
 
+// Whole-block copies between two pools (copy-on-write, swap): for every pair
+// (s, d) of the mapping, the K and V bytes of source block s become those of
+// destination block d.  Pointers are device addresses (of device memory or of
+// pinned, device-mapped host memory).
+struct BlockCopyArgs {
+  char *dst_k, *dst_v;
+  const char *src_k, *src_v;
+  const void *mapping;           // [num_pairs, 2] (source, destination)
+  int32_t map_i64;               // 1: int64 pairs, 0: int32
+  int64_t map_stride;            // elements between consecutive pairs
+  int64_t num_pairs;
+  int64_t block_bytes;           // bytes of one block, contiguous in both pools
+  int64_t src_stride, dst_stride;  // bytes between consecutive blocks
+  int64_t src_blocks, dst_blocks;
+  int32_t pieces;                // workgroups per (pair, K or V)
+};
+
 struct CacheWriteArgs {
   const void *k;
   const void *v;
@@ -105,6 +122,9 @@ hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 bool prefill_supported(int kv_kind, int head_dim);
 int prefill_tile_cols(int64_t num_rows, int64_t num_seqs, int group);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// whole-block copies (block_copy.hip)
+int64_t copy_blocks_pieces(int64_t block_bytes);
+hipError_t launch_copy_blocks(const BlockCopyArgs &a, hipStream_t stream);
 
 // Which (kv dtype, q dtype, head_dim, group size) the decode kernels were built for.
 bool decode_supported(int kv_kind, int q_kind, int head_dim, int group);

@@ -45,7 +45,7 @@ def lib():
 
 def test_header_declares_the_operations():
     syms = declared_symbols()
-    for s in ("pa_decode", "pa_prefill", "pa_cache_write", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
+    for s in ("pa_decode", "pa_prefill", "pa_cache_write", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
               "pa_last_error"):
         assert s in syms
 
@@ -266,3 +266,40 @@ def test_prefill_errors(lib):
     a = good_prefill()
     a[1] = T([40, 8, 128], pa.PA_F16, strides=[8 * 128, 128, 2])
     expect(lib, call_prefill(lib, a), -4)
+
+
+def good_copy(NB=64, bs=16, Hkv=2, D=128, M=4, dt=pa.PA_F16, mdt=pa.PA_I64):
+    return [T([NB, bs, Hkv, D], dt), T([NB, bs, Hkv, D], dt), T([NB, bs, Hkv, D], dt), T([NB, bs, Hkv, D], dt),
+            T([M, 2], mdt)]
+
+
+def call_copy(lib, args, opts=None):
+    return lib.pa_copy_blocks(*args, ctypes.byref(opts or pa.PaOpts()))
+
+
+def test_copy_blocks_errors(lib):
+    a = good_copy()
+    a[4] = T([4, 2], pa.PA_F32)
+    expect(lib, call_copy(lib, a), -2, "block_mapping")
+    a = good_copy()
+    a[4] = T([4, 3], pa.PA_I64)
+    expect(lib, call_copy(lib, a), -3, "block_mapping")
+    a = good_copy()
+    a[1] = T([64, 16, 2, 128], pa.PA_BF16)
+    expect(lib, call_copy(lib, a), -2)
+    a = good_copy()
+    a[2] = T([64, 32, 2, 128], pa.PA_F16)
+    expect(lib, call_copy(lib, a), -3)
+    a = good_copy()
+    a[0] = T([64, 16, 2, 128], pa.PA_F16, strides=[16 * 2 * 256, 2 * 256, 256, 1])  # padded rows
+    expect(lib, call_copy(lib, a), -4, "contiguous")
+    a = good_copy()
+    a[3] = T([65, 16, 2, 128], pa.PA_F16)
+    expect(lib, call_copy(lib, a), -3, "same number of blocks")
+    o = pa.PaOpts()
+    o.flags = 2
+    expect(lib, call_copy(lib, good_copy(), o), -7, "flags")
+    # memory the runtime does not know (here: no device at all) is refused before any launch
+    expect(lib, call_copy(lib, good_copy()), -7, "pinned host memory")
+    # nothing to copy: OK without looking at the pointers
+    assert call_copy(lib, good_copy(M=0)) == 0
