@@ -169,7 +169,10 @@ struct MfmaCore {
   // Online softmax for column c16 over the lane's 8 tokens of the chunk
   // starting at token cs (those past `last`, the column's last visible token,
   // masked), then across the 4 quarters; returns the weights as P^T operands
-  // split as P = hi + lo in the operand type.
+  // split as P = hi + lo in the operand type.  EMPTY_OK: the column may have
+  // seen no position yet and see none in this chunk either (its running max
+  // still -inf); its weights are then zeros instead of exp2(-inf - -inf).
+  template <bool EMPTY_OK = false>
   __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, float qk_scale_log2, u32x4 &phi,
                                           u32x4 &plo) {
     float p8[8];
@@ -188,13 +191,14 @@ struct MfmaCore {
     // accumulator rescale is skipped for almost every chunk
     if (__ballot(cm > m + kSlack)) {
       const float mn = fmaxf(m, cm);
-      const float alpha = fast_exp2(m - mn);
+      // (a column that has seen nothing yet rescales its zeros by 0, never by exp2(NaN))
+      const float alpha = EMPTY_OK && m == -INFINITY ? 0.0f : fast_exp2(m - mn);
       m = mn;
       l *= alpha;
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] *= alpha;
     }
-    const float mn = m;
+    const float mn = EMPTY_OK && m == -INFINITY ? 0.0f : m;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);

@@ -354,7 +354,10 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   a.num_blocks = (int32_t)NB;
   a.block_size = block_size;
   a.max_ctx = (int32_t)(W * block_size);
-  a.tile_cols = pa::prefill_tile_cols(N, S, (int)G);
+  int tile_cols = 0, key_split = 0;
+  pa::prefill_plan(N, S, (int)G, tile_cols, key_split);
+  a.tile_cols = tile_cols;
+  a.key_split = key_split;
   // every sequence's tiles: at most N * G / tile_cols whole ones plus one partial tile each
   const int64_t slots = (N * G + a.tile_cols - 1) / a.tile_cols + S;
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");

@@ -68,6 +68,7 @@ struct PrefillArgs {
   int32_t num_blocks, block_size, max_ctx;
   int32_t tile_slots;              // tile slots per kv head in the grid (>= the tiles of all sequences)
   int32_t tile_cols;               // columns per tile
+  int32_t key_split;               // 1: the four wavefronts split a tile's keys, 0: its columns
   float qk_scale_log2;             // scale * log2(e)
   int32_t kv_kind;                 // KvKind of the caches (= q's)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype
@@ -120,7 +121,7 @@ hipError_t launch_decode_mfma(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs &a, hipStream_t stream);
 // causal multi-token queries on the matrix cores (prefill_mfma.hip)
 bool prefill_supported(int kv_kind, int head_dim);
-int prefill_tile_cols(int64_t num_rows, int64_t num_seqs, int group);
+void prefill_plan(int64_t num_rows, int64_t num_seqs, int group, int &tile_cols, int &key_split);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // whole-block copies (block_copy.hip)
 int64_t copy_blocks_pieces(int64_t block_bytes);

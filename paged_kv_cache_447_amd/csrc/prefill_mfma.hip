@@ -80,7 +80,12 @@ __device__ bool locate_tile(const PrefillArgs &a, int t, int lane, int &seq, int
   return false;
 }
 
-template <typename MT, int D, int BS, int NC>
+// KSP (key split): for tiles of few columns (verification-sized steps), the
+// four wavefronts all compute the tile's 16 NC columns, each over every fourth
+// chunk, which it loads alone into a private two-slot ring; the four partial
+// softmax states are merged through LDS at the end.  Otherwise the four
+// wavefronts compute different columns over every chunk of one shared stream.
+template <typename MT, int D, int BS, int NC, bool KSP>
 struct PrefillTile {
   using Slot = RowSlot<D>;
   using Core = MfmaCore<MT, D>;
@@ -90,8 +95,12 @@ struct PrefillTile {
   static constexpr int HB = Slot::HB;                 // bytes of the K (or V) rows of a chunk
   static constexpr int PER = Slot::NLD / kWaves;      // DMA instructions per wavefront per K (or V) chunk
   static constexpr int CB = 2 * HB;                   // bytes of a ring slot: K rows, then V rows
-  static constexpr int R = kLdsPerWG / CB < 8 ? kLdsPerWG / CB : 8;  // ring slots
-  static constexpr int kLdsBytes = R * CB;
+  static constexpr int R = kLdsPerWG / CB < 8 ? kLdsPerWG / CB : 8;  // ring slots (shared stream)
+  // key split: two private slots per wavefront, reused for the partials' merge
+  static constexpr int kMergeBytes = kWaves * NC * 16 * (D + 2) * 4;
+  static constexpr int kLdsBytes = KSP ? kWaves * 2 * CB : R * CB;
+  static_assert(!KSP || kMergeBytes <= kLdsBytes, "the partials fit the ring");
+  static_assert(!KSP || 2 * Slot::NLD < 64, "wait counter range");
   static constexpr int LOG2BS = BS == 16 ? 4 : 5;
   static_assert(Slot::NLD % kWaves == 0, "every wavefront loads the same share of a chunk");
   static_assert(Slot::RPI * PER == 8, "a wavefront's share is 8 rows inside one 16-token tile");
@@ -138,7 +147,7 @@ struct PrefillTile {
     bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
     kbase = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * 2;
     vbase = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * 2;
-    const int w_lo = c_lo + 16 * NC * wave;
+    const int w_lo = KSP ? c_lo : c_lo + 16 * NC * wave;
     wlast = w_lo < c_hi ? pos0 + (min(w_lo + 16 * NC, c_hi) - 1) / a.group : -1;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
@@ -195,9 +204,8 @@ struct PrefillTile {
     }
   }
 
-  __device__ __forceinline__ void compute(int c, int slot) {
+  __device__ __forceinline__ void compute(int c, const char *ks) {
     const int cs = CT * c;
-    const char *ks = ring + slot * CB;
     u32x4 kop[2][KS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -208,7 +216,8 @@ struct PrefillTile {
     for (int ct = 0; ct < NC; ++ct) {
       f32x4 sc[2];
       core[ct].scores(qop[ct], [&](int tt, int kb) { return kop[tt][kb]; }, sc);
-      core[ct].weights(sc, cs, last[ct], a.qk_scale_log2, phi[ct], plo[ct]);
+      // with the keys split, a wavefront's first chunks may lie past a column's limit
+      core[ct].template weights<KSP>(sc, cs, last[ct], a.qk_scale_log2, phi[ct], plo[ct]);
     }
     accumulate_slot_n<NC>(core, phi, plo, ks + HB, [&](int n) { return voff[n]; });
   }
@@ -233,7 +242,7 @@ struct PrefillTile {
       issue(c + R - 1, nblk, islot);
       nblk = block_of(c + R);
       __builtin_amdgcn_sched_barrier(0);
-      if (CT * c <= wlast) compute(c, slot);
+      if (CT * c <= wlast) compute(c, ring + slot * CB);
       __builtin_amdgcn_sched_barrier(0);
       slot = slot + 1 == R ? 0 : slot + 1;
       islot = islot + 1 == R ? 0 : islot + 1;
@@ -241,6 +250,136 @@ struct PrefillTile {
     wait_vm<0>();  // no load may land after the workgroup's LDS is released
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) core[ct].finish();
+  }
+
+  // ---- key split --------------------------------------------------------
+
+  // physical blocks of chunk c's two 16-token tiles (rows past last_max read its row)
+  __device__ __forceinline__ void blocks_of(int c, int &b0, int &b1) const {
+    const int t0 = min(CT * c, last_max), t1 = min(CT * c + 16, last_max);
+    const int x0 = bt[t0 >> LOG2BS], x1 = bt[t1 >> LOG2BS];
+    b0 = x0 < 0 ? 0 : (x0 >= a.num_blocks ? a.num_blocks - 1 : x0);
+    b1 = x1 < 0 ? 0 : (x1 >= a.num_blocks ? a.num_blocks - 1 : x1);
+  }
+
+  // all of chunk c's K and V rows, by this wavefront alone, into `dst`
+  __device__ __forceinline__ void issue_all(int c, int b0, int b1, char *dst) {
+    const int cs = CT * c;
+#pragma unroll
+    for (int isv = 0; isv < 2; ++isv) {
+      const char *base = isv ? vbase : kbase;
+      const int64_t sb = isv ? a.v_sb : a.k_sb, st = isv ? a.v_st : a.k_st;
+#pragma unroll
+      for (int i = 0; i < Slot::NLD; ++i) {
+        int r, g;
+        Slot::dma_target(isv, i, lane, r, g);
+        const int t = min(cs + r, last_max);
+        const char *bb = base + (int64_t)((Slot::RPI * i) / 16 ? b1 : b0) * sb * 2;  // uniform block base
+        const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
+        __builtin_amdgcn_global_load_lds(gp, lds_addr(dst + isv * HB + 1024 * i), 16, 0, 0);
+      }
+    }
+  }
+
+  __device__ void run_split() {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].reset();
+    load_q();
+    const int nch = last_max / CT + 1;
+    char *mine = ring + wave * 2 * CB;
+    // chunks wave, wave + 4, ...: one in flight while the one before it is
+    // computed.  A chunk index past the end reloads the last rows into the
+    // slot nobody reads next, so exactly 2 NLD loads are outstanding behind
+    // the awaited chunk.
+    int b0, b1;
+    blocks_of(wave, b0, b1);
+    issue_all(wave, b0, b1, mine);
+    blocks_of(wave + kWaves, b0, b1);
+    int k = 0;
+    for (int c = wave; c < nch; c += kWaves, ++k) {
+      issue_all(c + kWaves, b0, b1, mine + ((k + 1) & 1) * CB);
+      blocks_of(c + 2 * kWaves, b0, b1);
+      wait_vm<2 * Slot::NLD>();  // chunk c (and the queries before it) has landed
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c, mine + (k & 1) * CB);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<0>();  // no load may land after the ring is reused or released
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].finish();
+  }
+
+  // Merge the four wavefronts' (max, sum, output) of every column by
+  // log-sum-exp through LDS and write the outputs: wavefront w writes the
+  // 16-dim tiles n = w, w + 4, ... of every column.
+  template <typename OT>
+  __device__ void merge_store() {
+    float *pacc = reinterpret_cast<float *>(ring);  // [wave][ct][column][D]
+    float *pml = pacc + kWaves * NC * 16 * D;       // [wave][ct][column][2]
+    __syncthreads();                                // every wavefront is done with the ring
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      float *dst = pacc + ((wave * NC + ct) * 16 + c16) * D + 4 * jq;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // copy the element out first: a bit cast applied directly to a
+          // vector element is lowered as a read of element 0
+          const float v = core[ct].acc[n][i];
+          w[i] = __builtin_bit_cast(uint32_t, v);
+        }
+        st16(dst + 16 * n, w);
+      }
+      if (jq == 0) {
+        pml[((wave * NC + ct) * 16 + c16) * 2] = core[ct].m;
+        pml[((wave * NC + ct) * 16 + c16) * 2 + 1] = core[ct].l;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      float m[kWaves], f[kWaves];
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        m[w] = pml[((w * NC + ct) * 16 + c16) * 2];
+        M = fmaxf(M, m[w]);
+      }
+      float L = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        f[w] = fast_exp2(m[w] - M);  // 0 for a wavefront that saw none of this column's positions
+        L += f[w] * pml[((w * NC + ct) * 16 + c16) * 2 + 1];
+      }
+      const bool z = last[ct] < 0;
+      const float inv = 1.0f / L;
+      const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
+#pragma unroll
+      for (int n = wave; n < NT; n += kWaves) {
+        float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const u32x4 x = ld16(pacc + ((w * NC + ct) * 16 + c16) * D + 16 * n + 4 * jq);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t xi = x[i];
+            o[i] += f[w] * __builtin_bit_cast(float, xi);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = z ? 0.0f : o[i] * inv;
+        if (valid[ct]) store4<OT>(a.out, off + 16 * n, o);
+      }
+    }
+  }
+
+  __device__ void merge_write() {
+    if (a.out_f32)
+      merge_store<f32_t>();
+    else
+      merge_store<MT>();
   }
 
   template <typename OT>
@@ -270,9 +409,9 @@ struct PrefillTile {
   }
 };
 
-template <typename MT, int D, int BS, int NC>
-__global__ void __launch_bounds__(64 * kWaves, 2) prefill_mfma(const PrefillArgs a) {
-  typedef PrefillTile<MT, D, BS, NC> Tile;
+template <typename MT, int D, int BS, int NC, bool KSP>
+__global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const PrefillArgs a) {
+  typedef PrefillTile<MT, D, BS, NC, KSP> Tile;
   __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -286,21 +425,33 @@ __global__ void __launch_bounds__(64 * kWaves, 2) prefill_mfma(const PrefillArgs
   if (!locate_tile(a, bx - kvh * a.tile_slots, lane, seq, tile)) return;  // the same for all four wavefronts
   Tile t(a, lds, lane, wave);
   if (!t.setup(seq, tile, kvh)) {
-    t.write_out(true);
+    if (!KSP || wave == 0) t.write_out(true);
     return;
   }
-  t.run();
-  t.write_out(false);
+  if constexpr (KSP) {
+    t.run_split();
+    t.merge_write();
+  } else {
+    t.run();
+    t.write_out(false);
+  }
 }
 
 template <typename MT, int D, int BS>
 hipError_t launch_nc(const PrefillArgs &a, hipStream_t stream) {
   const int64_t n = (int64_t)a.tile_slots * a.num_kv_heads;
   const dim3 grid((unsigned)((n + 7) / 8 * 8)), block(64 * kWaves);
-  if (a.tile_cols == 64 * kWaves / 2)
-    hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1>), grid, block, 0, stream, a);
+  if (a.key_split) {
+    if (a.tile_cols == 32)
+      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2, true>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1, true>), grid, block, 0, stream, a);
+  } else {
+    if (a.tile_cols == 32 * kWaves)
+      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2, false>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1, false>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -324,12 +475,18 @@ bool prefill_supported(int kv_kind, int head_dim) {
   return (kv_kind == KV_F16 || kv_kind == KV_BF16) && (head_dim == 64 || head_dim == 128);
 }
 
-// Columns per tile: 32 per wavefront when the sequences average at least two
-// such tiles' worth of columns (each K/V operand read from LDS then feeds
-// twice the arithmetic), else 16.
-int prefill_tile_cols(int64_t num_rows, int64_t num_seqs, int group) {
-  const int64_t wide = 32 * kWaves;
-  return num_rows * group >= 2 * wide * num_seqs ? (int)wide : 16 * kWaves;
+// Tile shape.  Steps that average at most 32 columns per sequence (a few
+// query rows, verification-sized) split the keys of a 16- or 32-column tile
+// over the four wavefronts; larger steps give each wavefront its own columns:
+// 32 when the sequences average at least two such tiles' worth (each K/V
+// operand read from LDS then feeds twice the arithmetic), else 16.
+void prefill_plan(int64_t num_rows, int64_t num_seqs, int group, int &tile_cols, int &key_split) {
+  const int64_t cols = num_rows * group;
+  key_split = cols <= 32 * num_seqs;
+  if (key_split)
+    tile_cols = cols <= 16 * num_seqs ? 16 : 32;
+  else
+    tile_cols = cols >= 2 * 32 * kWaves * num_seqs ? 32 * kWaves : 16 * kWaves;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {

@@ -46,6 +46,20 @@ CASES = {
                                 max_blocks_per_seq=48, ctx_kind="fixed", ctx_fixed=(50, 700, 9, 300, 64, 129),
                                 allocator="shuffled"),
                          (0, 40, 9, 1, 0, 77)),
+    # verification-sized steps, where the four wavefronts split each tile's keys:
+    # 16 heads per kv head at head_dim 64 in bf16 with 2 draft tokens (32 columns) ...
+    "verify_gqa16_d64_bf16": P("verify_gqa16_d64_bf16",
+                               scaled(get_config("gqa70b"), num_seqs=7, num_heads=32, num_kv_heads=2, head_dim=64,
+                                      block_size=16, kv_dtype="bf16", q_dtype="bf16", num_blocks=900,
+                                      max_blocks_per_seq=128, ctx_kind="fixed",
+                                      ctx_fixed=(2, 3, 33, 200, 1024, 1500, 2047), allocator="shuffled"),
+                               2),
+    # ... and 4 heads per kv head at block 16 with 3 draft tokens (12 of 16 columns)
+    "verify_gqa4_bs16": P("verify_gqa4_bs16",
+                          scaled(get_config("gqa70b"), num_seqs=9, num_heads=16, num_kv_heads=4, block_size=16,
+                                 num_blocks=1200, max_blocks_per_seq=120, ctx_kind="fixed",
+                                 ctx_fixed=(3, 4, 31, 32, 33, 127, 128, 129, 1900), allocator="shuffled"),
+                          3),
     # MHA f16 block 16, head_dim 128, uneven q_len straddling the 64-column tile
     "mha_f16_tiles": P("mha_f16_tiles",
                        scaled(get_config("llama7b"), num_seqs=4, num_heads=6, num_kv_heads=6, num_blocks=300,
