@@ -358,6 +358,7 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   pa::prefill_plan(N, S, (int)G, tile_cols, key_split);
   a.tile_cols = tile_cols;
   a.key_split = key_split;
+  a.persistent_wgs = device_default_workers() / kDefaultWorkersPerCU;  // one workgroup per CU
   // every sequence's tiles: at most N * G / tile_cols whole ones plus one partial tile each
   const int64_t slots = (N * G + a.tile_cols - 1) / a.tile_cols + S;
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");

@@ -69,6 +69,7 @@ struct PrefillArgs {
   int32_t tile_slots;              // tile slots per kv head in the grid (>= the tiles of all sequences)
   int32_t tile_cols;               // columns per tile
   int32_t key_split;               // 1: the four wavefronts split a tile's keys, 0: its columns
+  int32_t persistent_wgs;          // key split: workgroups of the persistent launch (one per CU)
   float qk_scale_log2;             // scale * log2(e)
   int32_t kv_kind;                 // KvKind of the caches (= q's)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype

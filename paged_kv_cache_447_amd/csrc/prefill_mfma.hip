@@ -53,32 +53,87 @@ __device__ __forceinline__ void seq_rows(const PrefillArgs &a, int i, int &lo, i
   hi = clampi(a.query_start_loc[i + 1], lo, a.num_rows);
 }
 
-// The sequence and tile of tile slot t: sequences in order, each cut into
-// ceil(rows * G / tile_cols) tiles, taken last tile first.  false if t is past
-// the last tile.  All results are wave-uniform.
-__device__ bool locate_tile(const PrefillArgs &a, int t, int lane, int &seq, int &tile) {
-  int carry = 0;
-  for (int base = 0; base < a.num_seqs; base += 64) {
-    const int i = base + lane;
-    int tiles = 0;
-    if (i < a.num_seqs) {
-      int lo, hi;
-      seq_rows(a, i, lo, hi);
-      tiles = (int)(((int64_t)(hi - lo) * a.group + a.tile_cols - 1) / a.tile_cols);
-    }
-    const int incl = wave_incl_scan(tiles, lane);
-    const int total = uniform(__shfl(incl, 63));
-    if (t < carry + total) {
-      const int k = uniform(__builtin_ctzll(__ballot(carry + incl > t)));
-      seq = base + k;
-      // a sequence's last tile (whose rows see the most positions) first
-      tile = uniform(__shfl(incl, k)) - 1 - (t - carry);
-      return true;
-    }
-    carry += total;
-  }
-  return false;
+__device__ __forceinline__ int seq_tiles(const PrefillArgs &a, int i) {
+  int lo, hi;
+  seq_rows(a, i, lo, hi);
+  return (int)(((int64_t)(hi - lo) * a.group + a.tile_cols - 1) / a.tile_cols);
 }
+
+// The order of the tiles.  Every sequence has ceil(rows * G / tile_cols)
+// tiles, its last tile (whose rows see the most positions) first.  Batches of
+// up to kRanked sequences take their sequences longest context first (ties in
+// sequence order), so that the longest work starts first: the lengths are
+// loaded once, in one round trip, and ranked in registers.  Larger batches
+// keep their own order and are scanned for each tile.  All results are
+// wave-uniform.
+struct TileOrder {
+  static constexpr int kWin = 4;
+  static constexpr int kRanked = 64 * kWin;
+  bool ranked;
+  int total;                      // tiles of all sequences (ranked batches)
+  int tiles[kWin], before[kWin];  // per lane: its sequence's tiles, and those of the sequences ranked before it
+
+  __device__ void init(const PrefillArgs &a, int lane) {
+    ranked = a.num_seqs <= kRanked;
+    total = 0;
+    if (!ranked) return;
+    int L[kWin];
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) {
+      const int i = 64 * w + lane;
+      tiles[w] = 0;
+      L[w] = -1;
+      before[w] = 0;
+      if (i < a.num_seqs) {
+        tiles[w] = seq_tiles(a, i);
+        L[w] = clamp_ctx(a.context_lens[i], a.max_ctx);
+      }
+    }
+#pragma unroll
+    for (int w2 = 0; w2 < kWin; ++w2) {
+      const int n = min(64, a.num_seqs - 64 * w2);
+      for (int k = 0; k < n; ++k) {
+        const int Lk = __builtin_amdgcn_readlane(L[w2], k), tk = __builtin_amdgcn_readlane(tiles[w2], k);
+        total += tk;
+#pragma unroll
+        for (int w = 0; w < kWin; ++w)
+          if (64 * w < a.num_seqs) before[w] += (Lk > L[w] || (Lk == L[w] && 64 * w2 + k < 64 * w + lane)) ? tk : 0;
+      }
+    }
+  }
+
+  // The sequence and tile of tile number t; false past the last tile.
+  __device__ bool find(const PrefillArgs &a, int t, int lane, int &seq, int &tile) const {
+    if (ranked) {
+#pragma unroll
+      for (int w = 0; w < kWin; ++w) {
+        const uint64_t hit = __ballot(tiles[w] > 0 && before[w] <= t && t < before[w] + tiles[w]);
+        if (hit) {
+          const int k = __builtin_ctzll(hit);
+          seq = 64 * w + k;
+          tile = __builtin_amdgcn_readlane(before[w] + tiles[w], k) - 1 - t;
+          return true;
+        }
+      }
+      return false;
+    }
+    int carry = 0;
+    for (int base = 0; base < a.num_seqs; base += 64) {
+      const int i = base + lane;
+      const int nt = i < a.num_seqs ? seq_tiles(a, i) : 0;
+      const int incl = wave_incl_scan(nt, lane);
+      const int tot = uniform(__shfl(incl, 63));
+      if (t < carry + tot) {
+        const int k = uniform(__builtin_ctzll(__ballot(carry + incl > t)));
+        seq = base + k;
+        tile = uniform(__shfl(incl, k)) - 1 - (t - carry);
+        return true;
+      }
+      carry += tot;
+    }
+    return false;
+  }
+};
 
 // KSP (key split): for tiles of few columns (verification-sized steps), the
 // four wavefronts all compute the tile's 16 NC columns, each over every fourth
@@ -415,32 +470,50 @@ __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const P
   __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
-  // workgroups are dealt to the 8 XCDs round-robin; number them so that the
-  // tiles of one kv head, which read the same K/V rows, share an XCD's L2
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  const int kvh = bx / a.tile_slots;
-  if (kvh >= a.num_kv_heads) return;
+  TileOrder order;
+  order.init(a, lane);
   int seq, tile;
-  if (!locate_tile(a, bx - kvh * a.tile_slots, lane, seq, tile)) return;  // the same for all four wavefronts
-  Tile t(a, lds, lane, wave);
-  if (!t.setup(seq, tile, kvh)) {
-    if (!KSP || wave == 0) t.write_out(true);
-    return;
-  }
   if constexpr (KSP) {
-    t.run_split();
-    t.merge_write();
+    // Key split (about one tile per sequence and kv head): persistent
+    // workgroups, one per CU, take the (tile, kv head) pairs round-robin in
+    // the tiles' order, all kv heads of a tile in a row, so that every
+    // workgroup gets a share of the longest contexts first.
+    const int64_t n = (int64_t)(order.ranked ? order.total : a.tile_slots) * a.num_kv_heads;
+    for (int64_t x = blockIdx.x; x < n; x += gridDim.x) {
+      const int t = (int)(x / a.num_kv_heads), kvh = (int)(x - (int64_t)t * a.num_kv_heads);
+      if (!order.find(a, t, lane, seq, tile)) break;  // unranked batches: past the last tile
+      Tile tl(a, lds, lane, wave);
+      if (!tl.setup(seq, tile, kvh)) {
+        if (wave == 0) tl.write_out(true);
+        continue;
+      }
+      tl.run_split();
+      tl.merge_write();
+      __syncthreads();  // the merge's reads of the ring are done before the next tile's loads
+    }
   } else {
-    t.run();
-    t.write_out(false);
+    // Workgroups are dealt to the 8 XCDs round-robin; number them so that the
+    // tiles of one kv head, which read the same K/V rows, share an XCD's L2.
+    const int nb = gridDim.x, b = blockIdx.x;
+    const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
+    const int kvh = bx / a.tile_slots;
+    if (kvh >= a.num_kv_heads) return;
+    if (!order.find(a, bx - kvh * a.tile_slots, lane, seq, tile)) return;  // the same for all four wavefronts
+    Tile tl(a, lds, lane, wave);
+    if (!tl.setup(seq, tile, kvh)) {
+      tl.write_out(true);
+      return;
+    }
+    tl.run();
+    tl.write_out(false);
   }
 }
 
 template <typename MT, int D, int BS>
 hipError_t launch_nc(const PrefillArgs &a, hipStream_t stream) {
   const int64_t n = (int64_t)a.tile_slots * a.num_kv_heads;
-  const dim3 grid((unsigned)((n + 7) / 8 * 8)), block(64 * kWaves);
+  const dim3 grid((unsigned)(a.key_split ? min((int64_t)a.persistent_wgs, n) : (n + 7) / 8 * 8)),
+      block(64 * kWaves);
   if (a.key_split) {
     if (a.tile_cols == 32)
       hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2, true>), grid, block, 0, stream, a);
