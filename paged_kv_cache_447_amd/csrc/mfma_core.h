@@ -184,8 +184,7 @@ struct MfmaCore {
       p8[i] = cs + tok <= last ? x : -INFINITY;
       cm = fmaxf(cm, p8[i]);
     }
-    cm = fmaxf(cm, __shfl_xor(cm, 16));
-    cm = fmaxf(cm, __shfl_xor(cm, 32));
+    cm = max_xor32(max_xor16(cm));
     // lazy rescale: the reference max moves only when a score exceeds it by
     // more than kSlack (log2 units), so weights stay below 2^kSlack and the
     // accumulator rescale is skipped for almost every chunk
@@ -225,10 +224,7 @@ struct MfmaCore {
   template <class VOff>
   __device__ __forceinline__ void accumulate_slot(u32x4 phi, u32x4 plo, const char *vs, VOff voff);
 
-  __device__ __forceinline__ void finish() {
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-  }
+  __device__ __forceinline__ void finish() { l = sum_xor32(sum_xor16(l)); }
 };
 
 // O^T += V^T P^T for NC cores (16 columns each) that share the chunk's V rows:
