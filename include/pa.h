@@ -1,7 +1,7 @@
 /*
  * pa.h -- C ABI of the paged-KV attention library (libpa.so) for AMD gfx950.
  *
- * Four operations, all defined on the pages this library follows:
+ * Five operations, all defined on the pages this library follows:
  *
  *   pa_decode       attention of one query token per head over a KV cache kept
  *                   in fixed-size physical blocks, found through a per-sequence
@@ -14,6 +14,8 @@
  *                   accumulates attention across blocks; the logical-to-physical
  *                   translation itself is section 5.1 of page
  *                   "vLLM框架中的KV cache优化与PagedAttention机制详解").
+ *   pa_decode_layers  pa_decode over several layers' caches in one launch,
+ *                   all layers sharing the block tables.
  *   pa_prefill      the same attention for several query tokens per sequence
  *                   (a prompt chunk, or draft tokens being verified), each
  *                   token seeing the context up to its own position; the
@@ -68,9 +70,9 @@ typedef enum pa_dtype {
 typedef struct pa_tensor {
   void *data;        /* device pointer */
   int32_t dtype;     /* pa_dtype */
-  int32_t ndim;      /* number of valid entries in shape/stride, 1..4 */
-  int64_t shape[4];
-  int64_t stride[4]; /* in elements */
+  int32_t ndim;      /* number of valid entries in shape/stride, 1..5 */
+  int64_t shape[5];
+  int64_t stride[5]; /* in elements */
 } pa_tensor;
 
 typedef enum pa_status {
@@ -146,6 +148,30 @@ PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int6
 PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
                            pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
                            const pa_opts *opts);
+
+/*
+ * pa_decode_layers -- pa_decode for several layers of the same batch in one
+ * launch (the translation of many lookups batched into one call, section 5.2
+ * of page "vLLM框架中的KV cache优化与PagedAttention机制详解").
+ *
+ *   out, q          [layers, num_seqs, num_heads, head_dim]
+ *   k_caches,
+ *   v_caches        [layers, num_blocks, block_size, num_kv_heads, head_dim]:
+ *                   one pool per layer, block b of every layer holding the same
+ *                   tokens, so that the block tables and context lengths --
+ *                   [num_seqs, max_blocks_per_seq] and [num_seqs], shared by all
+ *                   layers -- address every layer.
+ *   everything else as pa_decode; each layer's result is exactly pa_decode's
+ *   on that layer's q, caches and out.  The layer stride of each tensor must be
+ *   a multiple of 16 bytes.
+ *   opts->workspace: pa_decode_workspace_size(layers * num_seqs, ...) bytes.
+ * Work: one launch; the (layer, sequence) pairs are the items of pa_decode's
+ * split, so the launch's fixed cost and its finishing spread are paid once for
+ * all layers.
+ */
+PA_API pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches, pa_tensor v_caches,
+                                  pa_tensor block_tables, pa_tensor context_lens, int32_t block_size, float scale,
+                                  int32_t num_kv_heads, const pa_opts *opts);
 
 /*
  * pa_prefill -- paged attention for several causal query tokens per sequence.

@@ -123,6 +123,24 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
     return out
 
 
+def paged_decode_layers(q, k_caches, v_caches, block_tables, context_lens, scale: float, num_kv_heads: int,
+                        k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1):
+    """Reference decode of several layers of one batch: [L, S, H, D] float64.
+
+    Every layer has its own queries and caches ([L, ...] tensors) and they all
+    share one set of block tables and context lengths, since block b names the
+    same tokens in every layer's pool.  Layer l is exactly paged_decode on
+    layer l's tensors; batching the layers changes nothing in what is computed
+    (page "vLLM框架中的KV cache优化与PagedAttention机制详解", section 5.2, batches
+    the translation of many lookups into one call)."""
+    L = q.shape[0]
+    if k_caches.shape[0] != L or v_caches.shape[0] != L:
+        raise ValueError("q, k_caches and v_caches must have the same number of layers")
+    return np.stack([paged_decode(q[l], k_caches[l], v_caches[l], block_tables, context_lens, scale, num_kv_heads,
+                                  k_scale, v_scale, nthreads) for l in range(L)]) if L else \
+        np.zeros(tuple(q.shape), dtype=np.float64)
+
+
 def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
                   num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1) -> np.ndarray:
     """Reference prefill (causal, the query rows of sequence s being its newest

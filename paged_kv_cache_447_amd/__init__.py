@@ -17,6 +17,7 @@ __all__ = [
     "PaError",
     "load_library",
     "decode",
+    "decode_layers",
     "prefill",
     "cache_write",
     "copy_blocks",
@@ -48,8 +49,8 @@ class PaTensor(ctypes.Structure):
         ("data", ctypes.c_void_p),
         ("dtype", ctypes.c_int32),
         ("ndim", ctypes.c_int32),
-        ("shape", ctypes.c_int64 * 4),
-        ("stride", ctypes.c_int64 * 4),
+        ("shape", ctypes.c_int64 * 5),
+        ("stride", ctypes.c_int64 * 5),
     ]
 
 
@@ -95,6 +96,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_decode_layers.restype = i32
+    lib.pa_decode_layers.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_prefill.restype = i32
     lib.pa_prefill.argtypes = [PaTensor] * 7 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_copy_blocks.restype = i32
@@ -133,8 +136,8 @@ def _dtype_code(t) -> int:
 
 def describe(t) -> PaTensor:
     """pa_tensor view of a torch tensor (no copy; the tensor must stay alive)."""
-    if t.dim() > 4 or t.dim() < 1:
-        raise ValueError("tensors of rank 1..4 only")
+    if t.dim() > 5 or t.dim() < 1:
+        raise ValueError("tensors of rank 1..5 only")
     d = PaTensor()
     d.data = t.data_ptr()
     d.dtype = _dtype_code(t)
@@ -177,7 +180,10 @@ def new_workspace(q, num_kv_heads: int, num_workers: int = 0):
     number of calls of this shape, one at a time."""
     import torch
 
-    S, H, D = q.shape
+    *lead, H, D = q.shape  # [S, H, D], or [layers, S, H, D] for decode_layers
+    S = 1
+    for x in lead:
+        S *= x
     n = workspace_size(max(S, 1), H, num_kv_heads, D, num_workers)
     return torch.zeros(n, dtype=torch.uint8, device=q.device)
 
@@ -204,6 +210,32 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
     o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                        describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_size: int, scale: float,
+                  num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                  num_workers: int = 0, workspace=None, stream=None):
+    """pa_decode_layers: ``out`` [L, S, H, D] = pa_decode of every layer l on q[l],
+    k_caches[l], v_caches[l] ([L, NB, bs, Hkv, D]), with the block tables and
+    context lengths shared by all layers; returns ``out``."""
+    lib = load_library()
+    _check_device(out, q, k_caches, v_caches, block_tables, context_lens)
+    if workspace is None:
+        workspace = new_workspace(q, num_kv_heads, num_workers)
+    o = PaOpts()
+    o.k_scale = k_scale
+    o.v_scale = v_scale
+    o.partition_size = partition_size
+    o.num_workers = num_workers
+    o.workspace = workspace.data_ptr()
+    o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.stream = stream if stream is not None else _current_stream(q)
+    st = lib.pa_decode_layers(describe(out), describe(q), describe(k_caches), describe(v_caches),
+                              describe(block_tables), describe(context_lens), block_size, scale, num_kv_heads,
+                              ctypes.byref(o))
     if st != 0:
         _raise(lib, st)
     return out

@@ -96,7 +96,7 @@ struct MfmaMath : MfmaCore<MT, D> {
   __device__ void write_out(int s, int kvh) const {
     if (c16 >= G) return;
     const float inv = a.v_scale / l;
-    const int64_t row = (int64_t)s * a.o_ss + (int64_t)(kvh * G + c16) * a.o_sh;
+    const int64_t row = o_row(a, s) + (int64_t)(kvh * G + c16) * a.o_sh;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       float o[4];
@@ -216,15 +216,15 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
-    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
-    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;
-    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
+    p.bt = as_const(a.block_tables) + (int64_t)seq_of(a, g.s) * a.bt_ss;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, g.s) + (int64_t)g.kvh * a.k_sh) * EB;
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
     return p;
   }
   // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
   __device__ __forceinline__ void load_q(const SegInfo &g, u32x4 *dst) const {
-    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + (int64_t)g.s * a.q_ss +
+    const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + q_row(a, g.s) +
                            (int64_t)(g.kvh * G + (c16 < G ? c16 : 0)) * a.q_sh;
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) {
@@ -409,7 +409,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       const int b = 1024 * i + 16 * lane;
       const int h = b / RB < G ? b / RB : 0;
       const char *gp = reinterpret_cast<const char *>(a.q) +
-                       ((int64_t)g.s * a.q_ss + (int64_t)(g.kvh * G + h) * a.q_sh + (b % RB) / 2) * 2;
+                       (q_row(a, g.s) + (int64_t)(g.kvh * G + h) * a.q_sh + (b % RB) / 2) * 2;
       __builtin_amdgcn_global_load_lds(gp, lds_addr(slot + 1024 * i), 16, 0, 0);
     }
   }
@@ -419,7 +419,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       lhas = lw.next(ls);
     } while (lhas && ls.t_hi <= ls.t_lo);
     if (lhas) {
-      lbt = as_const(a.block_tables) + (int64_t)ls.s * a.bt_ss;
+      lbt = as_const(a.block_tables) + (int64_t)seq_of(a, ls.s) * a.bt_ss;
       lcs = ls.t_lo;
       llast = ls.t_hi - 1;
       fetch_blocks(lcs, llast, nblk);
@@ -435,10 +435,10 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
         dma_q(ls, ring + 4 * HB + (lord & 1) * QB);
         ++lord;
       }
-      const Src k{reinterpret_cast<const char *>(a.k_cache) + (int64_t)ls.kvh * a.k_sh * 2, nblk[0], nblk[1], lcs,
-                  llast};
-      vpend = Src{reinterpret_cast<const char *>(a.v_cache) + (int64_t)ls.kvh * a.v_sh * 2, nblk[0], nblk[1], lcs,
-                  llast};
+      const char *kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, ls.s) + (int64_t)ls.kvh * a.k_sh) * 2;
+      const char *vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, ls.s) + (int64_t)ls.kvh * a.v_sh) * 2;
+      const Src k{kb, nblk[0], nblk[1], lcs, llast};
+      vpend = Src{vb, nblk[0], nblk[1], lcs, llast};
       dma<false>(k, a.k_sb, a.k_st, slot);
       lcs += CT;
       if (lcs < ls.t_hi)

@@ -206,15 +206,16 @@ struct ValuSeg {
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
-    p.bt = as_const(a.block_tables) + (int64_t)g.s * a.bt_ss;
-    p.kb = reinterpret_cast<const char *>(a.k_cache) + (int64_t)g.kvh * a.k_sh * EB;  // uniform
-    p.vb = reinterpret_cast<const char *>(a.v_cache) + (int64_t)g.kvh * a.v_sh * EB;
+    p.bt = as_const(a.block_tables) + (int64_t)seq_of(a, g.s) * a.bt_ss;
+    p.kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, g.s) + (int64_t)g.kvh * a.k_sh) * EB;  // uniform
+    p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
     return p;
   }
   __device__ __forceinline__ void load_q(const SegInfo &g, QSlice<KVT, QT> *dst) const {
+    const int64_t qr = q_row(a, g.s);
 #pragma unroll
-    for (int h = 0; h < G; ++h) dst[h].load(a.q, (int64_t)g.s * a.q_ss + (int64_t)(g.kvh * G + h) * a.q_sh + r * VEC);
+    for (int h = 0; h < G; ++h) dst[h].load(a.q, qr + (int64_t)(g.kvh * G + h) * a.q_sh + r * VEC);
   }
 
   // pipeline state carried from one segment into the next
@@ -348,7 +349,7 @@ struct ValuSeg {
       const float inv = a.v_scale / l[h];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) o[v] = acc[h][v] * inv;
-      const int64_t off = (int64_t)s * a.o_ss + (int64_t)(kvh * G + h) * a.o_sh + r * VEC;
+      const int64_t off = o_row(a, s) + (int64_t)(kvh * G + h) * a.o_sh + r * VEC;
       if (a.out_f32)
         store_vec<f32_t, VEC>(a.out, off, o);
       else

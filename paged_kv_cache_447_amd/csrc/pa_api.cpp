@@ -147,9 +147,16 @@ size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num
   return workspace_layout(num_seqs, num_heads, num_kv_heads, head_dim, effective_workers(num_workers)).total;
 }
 
-pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
-                    pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
-                    const pa_opts *opts) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode over one layer (layers = 1, strides 0), or over several layers
+// whose per-layer views out/q/k_cache/v_cache are given with the layer
+// strides (elements) between consecutive layers.
+pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
+                      pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
+                      const pa_opts *opts, int64_t layers, int64_t q_sl, int64_t o_sl, int64_t k_sl, int64_t v_sl) {
   pa_opts o;
   std::memset(&o, 0, sizeof o);
   if (opts) o = *opts;
@@ -207,6 +214,7 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   if (S == 0 || H == 0) return PA_OK;
   if (NB == 0 || W == 0) return fail(PA_ERR_SHAPE, "empty cache or block table");
 
+  if (layers < 1 || S * layers > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 (layer, sequence) pairs");
   const int G = (int)(H / num_kv_heads);
   const int64_t max_ctx = W * block_size;
   int64_t part = o.partition_size;
@@ -217,10 +225,10 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
     return fail(PA_ERR_ARG, "partition_size %lld too small for a table of %lld tokens", (long long)part,
                 (long long)max_ctx);
   if (o.num_workers < 0) return fail(PA_ERR_ARG, "num_workers must be >= 0");
-  if (S * num_kv_heads * ((max_ctx + part - 1) / part) > ((int64_t)1 << 40))
+  if (layers * S * num_kv_heads * ((max_ctx + part - 1) / part) > ((int64_t)1 << 40))
     return fail(PA_ERR_UNSUPPORTED, "too many work units");
   const int32_t nw = effective_workers(o.num_workers);
-  const WsLayout ws = workspace_layout(S, H, num_kv_heads, D, nw);
+  const WsLayout ws = workspace_layout(layers * S, H, num_kv_heads, D, nw);
   if (!o.workspace || o.workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                 o.workspace ? o.workspace_bytes : (size_t)0);
@@ -249,7 +257,12 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   a.v_st = v_cache.stride[1];
   a.v_sh = v_cache.stride[2];
   a.bt_ss = block_tables.stride[0];
-  a.num_seqs = (int32_t)S;
+  a.num_seqs = (int32_t)(S * layers);
+  a.seqs_per_layer = (int32_t)S;
+  a.q_sl = q_sl;
+  a.o_sl = o_sl;
+  a.k_sl = k_sl;
+  a.v_sl = v_sl;
   a.num_heads = (int32_t)H;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = (int32_t)D;
@@ -268,6 +281,52 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
   hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(o.stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+// The view of one layer of a [layers, ...] tensor: the leading dimension dropped.
+pa_tensor layer_view(const pa_tensor &t) {
+  pa_tensor v;
+  std::memset(&v, 0, sizeof v);
+  v.data = t.data;
+  v.dtype = t.dtype;
+  v.ndim = t.ndim - 1;
+  for (int i = 1; i < t.ndim; ++i) {
+    v.shape[i - 1] = t.shape[i];
+    v.stride[i - 1] = t.stride[i];
+  }
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
+                    pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
+                    const pa_opts *opts) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale, num_kv_heads, opts, 1,
+                     0, 0, 0, 0);
+}
+
+pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches, pa_tensor v_caches,
+                           pa_tensor block_tables, pa_tensor context_lens, int32_t block_size, float scale,
+                           int32_t num_kv_heads, const pa_opts *opts) {
+  if (out.ndim != 4 || q.ndim != 4) return fail(PA_ERR_SHAPE, "out and q must be [layers, num_seqs, num_heads, head_dim]");
+  if (k_caches.ndim != 5 || v_caches.ndim != 5)
+    return fail(PA_ERR_SHAPE, "caches must be [layers, num_blocks, block_size, num_kv_heads, head_dim]");
+  const int64_t L = q.shape[0];
+  if (out.shape[0] != L || k_caches.shape[0] != L || v_caches.shape[0] != L)
+    return fail(PA_ERR_SHAPE, "out, q, k_caches and v_caches must have the same number of layers");
+  if (L < 0) return fail(PA_ERR_SHAPE, "negative layer count");
+  if (L == 0) return PA_OK;
+  const pa_tensor *ts[4] = {&out, &q, &k_caches, &v_caches};
+  for (const pa_tensor *t : ts) {
+    const int eb = elem_bytes(t->dtype);
+    if (eb && L > 1 && (t->stride[0] * eb) % 16) return fail(PA_ERR_LAYOUT, "layer stride not a multiple of 16 bytes");
+  }
+  return decode_impl(layer_view(out), layer_view(q), layer_view(k_caches), layer_view(v_caches), block_tables,
+                     context_lens, block_size, scale, num_kv_heads, opts, L, q.stride[0], out.stride[0],
+                     k_caches.stride[0], v_caches.stride[0]);
 }
 
 pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,

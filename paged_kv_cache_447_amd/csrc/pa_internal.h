@@ -43,6 +43,12 @@ struct DecodeArgs {
   int32_t kv_kind;              // KvKind
   int32_t q_kind;               // KV_F32 / KV_F16 / KV_BF16
   int32_t out_f32;              // 1: out is fp32, 0: out has q's dtype
+  // Several layers in one launch: sequence s of the launch is sequence
+  // s % seqs_per_layer of layer s / seqs_per_layer.  The layers share the block
+  // tables and context lengths; each has its own query, output and caches, at
+  // these strides (elements).  One layer: seqs_per_layer = num_seqs.
+  int32_t seqs_per_layer;
+  int64_t q_sl, o_sl, k_sl, v_sl;
 };
 
 // Everything a prefill launch needs, already validated; strides in elements.

@@ -36,6 +36,21 @@
 
 namespace pa {
 
+// A launch's sequence index as (layer, sequence of the layer), and where
+// that sequence's table row, context length, query, output and cache live.
+__device__ __forceinline__ int layer_of(const DecodeArgs &a, int s) { return s / a.seqs_per_layer; }
+__device__ __forceinline__ int seq_of(const DecodeArgs &a, int s) { return s - layer_of(a, s) * a.seqs_per_layer; }
+__device__ __forceinline__ int64_t q_row(const DecodeArgs &a, int s) {
+  const int l = layer_of(a, s);
+  return l * a.q_sl + (int64_t)(s - l * a.seqs_per_layer) * a.q_ss;
+}
+__device__ __forceinline__ int64_t o_row(const DecodeArgs &a, int s) {
+  const int l = layer_of(a, s);
+  return l * a.o_sl + (int64_t)(s - l * a.seqs_per_layer) * a.o_ss;
+}
+__device__ __forceinline__ int64_t k_layer(const DecodeArgs &a, int s) { return layer_of(a, s) * a.k_sl; }
+__device__ __forceinline__ int64_t v_layer(const DecodeArgs &a, int s) { return layer_of(a, s) * a.v_sl; }
+
 // The split of the unit order [0, T) into Ws = min(T, W) equal ranges, range
 // w worked by worker w (never more ranges than units, so none is empty).
 struct Split {
@@ -65,7 +80,7 @@ __device__ __forceinline__ SeqWindow load_window(const DecodeArgs &a, int s0, in
   SeqWindow win;
   win.s0 = s0;
   const int s = s0 + lane;
-  win.L = s < a.num_seqs ? clamp_ctx(a.context_lens[s], a.max_ctx) : 0;
+  win.L = s < a.num_seqs ? clamp_ctx(a.context_lens[seq_of(a, s)], a.max_ctx) : 0;
   win.n = (win.L + a.part_tokens - 1) / a.part_tokens;
   win.incl = wave_incl_scan(win.n, lane);
   win.total = uniform(__shfl(win.incl, 63));
@@ -85,7 +100,7 @@ __device__ __forceinline__ void load_windows(const DecodeArgs &a, int lane, Wind
 #pragma unroll
   for (int i = 0; i < kWin; ++i) {  // all loads in flight together
     const int s = 64 * i + lane;
-    L[i] = s < a.num_seqs ? clamp_ctx(a.context_lens[s], a.max_ctx) : 0;
+    L[i] = s < a.num_seqs ? clamp_ctx(a.context_lens[seq_of(a, s)], a.max_ctx) : 0;
   }
   ws.nw = 0;
 #pragma unroll
@@ -184,7 +199,7 @@ __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int6
   for (int k = 0; k < EPL; ++k) {
     const int e = lane + 64 * k;
     const int head = kvh * G + e / D;
-    store_elem<QT>(a, (int64_t)s * a.o_ss + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * a.v_scale);
+    store_elem<QT>(a, o_row(a, s) + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * a.v_scale);
   }
 }
 
@@ -230,7 +245,7 @@ __device__ __forceinline__ void zero_empty_sequences(const DecodeArgs &a, const 
     mask &= mask - 1;
     const int sz = win.s0 + l;
     for (int e = lane; e < a.num_heads * a.head_dim; e += 64)
-      store_elem<QT>(a, (int64_t)sz * a.o_ss + (int64_t)(e / a.head_dim) * a.o_sh + e % a.head_dim, 0.0f);
+      store_elem<QT>(a, o_row(a, sz) + (int64_t)(e / a.head_dim) * a.o_sh + e % a.head_dim, 0.0f);
   }
 }
 
@@ -364,7 +379,7 @@ struct Walker {
           stage = 3;
           return false;
         }
-        p.L = clamp_ctx(uniform(a.context_lens[p.s]), a.max_ctx);
+        p.L = clamp_ctx(uniform(a.context_lens[seq_of(a, p.s)]), a.max_ctx);
         p.n = (p.L + a.part_tokens - 1) / a.part_tokens;
       } while (p.n == 0);
     }
