@@ -6,7 +6,10 @@ With a prefill workload as --config (prefill_7b, verify_gqa70b, prefill_small)
 a step is instead the cache write of every new token of the step followed by
 pa_prefill over all query rows, and the line reports attention TFLOP/s.  With
 a block-copy workload (cow_llama7b, swap_out_gqa70b, swap_in_gqa70b) a step is
-one pa_copy_blocks launch, and the line reports bytes moved per second.
+one pa_copy_blocks launch, and the line reports bytes moved per second.  With
+a multi-layer workload (llama7b_x8, gqa70b_x8) a step writes every layer's new
+token (one cache-write launch over the flattened pools) and decodes all layers
+in one pa_decode_layers launch; the line reports K/V GB/s like decode.
 
 A step is one pass of the whole hot path over one batch: the cache write of
 each sequence's new token, then paged decode (one launch: balanced
@@ -114,6 +117,11 @@ def main():
 
     if args.config in PREFILL_CONFIGS:
         print(json.dumps(bench_prefill(args, PREFILL_CONFIGS[args.config], dev)), flush=True)
+        return
+    from pa_workloads.layers import LAYER_CONFIGS
+
+    if args.config in LAYER_CONFIGS:
+        print(json.dumps(bench_layers(args, LAYER_CONFIGS[args.config], dev)), flush=True)
         return
     from pa_workloads.blocks import BLOCK_CONFIGS
 
@@ -428,6 +436,137 @@ def bench_prefill(args, pcfg, dev) -> dict:
             "kind": "oracle",
             "sample": f"{reps} x the fp64 prefill of sequence 0 of {cfg.name} ({n0} query rows, context "
                       f"{int(ctx[0])}, all {cfg.num_heads} heads), {el:.1f} s wall, {nthreads} threads",
+        }
+    return result
+
+
+def bench_layers(args, lcfg, dev) -> dict:
+    """Decode of L layers sharing one layout: one step = the cache write of all
+    layers' new tokens plus one pa_decode_layers launch."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_447_amd as pa
+    from pa_workloads import algorithmic_bytes, kv_bytes, make_layout
+    from pa_workloads.layers import flat_slots, make_layer_inputs
+
+    cfg = lcfg.base
+    L = lcfg.num_layers
+    layout = make_layout(cfg)
+    ctx = layout.context_lens
+    step_kv = L * kv_bytes(cfg, ctx)
+    step_alg = L * algorithmic_bytes(cfg, ctx)
+    nsets = 2
+    sets = []
+    for i in range(nsets):
+        inp = make_layer_inputs(lcfg, layout, dev, seed_offset=i)
+        inp["out"] = torch.zeros_like(inp["q"])
+        inp["ws"] = pa.new_workspace(inp["q"], cfg.num_kv_heads)
+        NB = cfg.num_blocks
+        inp["kc_flat"] = inp["k_cache"].view((L * NB,) + tuple(inp["k_cache"].shape[2:]))
+        inp["vc_flat"] = inp["v_cache"].view((L * NB,) + tuple(inp["v_cache"].shape[2:]))
+        inp["kn_flat"] = inp["k_new"].reshape((-1,) + tuple(inp["k_new"].shape[2:]))
+        inp["vn_flat"] = inp["v_new"].reshape((-1,) + tuple(inp["v_new"].shape[2:]))
+        inp["slots_flat"] = flat_slots(inp["slot_mapping"], L, NB * cfg.block_size)
+        sets.append(inp)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def write(inp):
+        pa.cache_write(inp["kn_flat"], inp["vn_flat"], inp["kc_flat"], inp["vc_flat"], inp["slots_flat"],
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
+
+    def decode(inp):
+        pa.decode_layers(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"],
+                         inp["context_lens"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+                         k_scale=inp["k_scale"], v_scale=inp["v_scale"], workspace=inp["ws"], stream=sptr)
+
+    for i in range(args.warmup):
+        write(sets[i % nsets])
+        decode(sets[i % nsets])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        write(sets[i % nsets])
+        decode(sets[i % nsets])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        inp = sets[i % nsets]
+        write(inp)
+        evs[i][0].record(stream)
+        decode(inp)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    for inp in sets:
+        if not torch.isfinite(inp["out"]).all():
+            raise RuntimeError("non-finite decode output")
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float16, device=dev).fill_(1.0)  # 512 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    achieved = step_alg / (kernel_ms * 1e-3) / 1e9
+    value = step_kv / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.kv_dtype,
+        "data": "synthetic (seeded N(0,1) values, seeded block allocator)",
+        "config": {"workload": lcfg.name, "layers": L, "num_seqs": cfg.num_seqs, "num_heads": cfg.num_heads,
+                   "num_kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim, "block_size": cfg.block_size,
+                   "kv_dtype": cfg.kv_dtype, "mean_context": float(np.mean(ctx)), "input_sets": nsets,
+                   "kv_bytes_per_step": step_kv},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
+        "roofline": {"kernel": "decode_layers (paged decode of all layers in one launch)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 5),
+                     "algorithmic_bytes_per_launch": step_alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = len(os.sched_getaffinity(0))
+        nthreads = max(1, min(cores, 64))
+        h = {k: sets[0][k][0].cpu() for k in ("q", "k_cache", "v_cache")}
+        bt, cl = sets[0]["block_tables"].cpu(), sets[0]["context_lens"].cpu()
+        reps, t_start = 0, time.perf_counter()
+        while True:
+            oracle.paged_decode(h["q"], h["k_cache"], h["v_cache"], bt, cl, cfg.softmax_scale, cfg.num_kv_heads,
+                                nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t_start
+            if el >= args.cpu_seconds or reps >= 1000:
+                break
+        result["cpu_baseline"] = {
+            "value": round(kv_bytes(cfg, ctx) * reps / el / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{reps} fp64 decodes of layer 0 of {lcfg.name} (all {cfg.num_seqs} sequences), "
+                      f"{el:.1f} s wall, {nthreads} threads",
         }
     return result
 

@@ -362,6 +362,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   bool lhas;
   int lcs, llast;  // next chunk of ls to load; last token of ls
   const_i32 *lbt;
+  const char *lkb, *lvb;  // K / V rows of ls: its layer's cache at its kv head
   int nblk[2];  // block ids of chunk lcs
   int lord;     // non-empty segments whose query has been loaded
   Src vpend;    // the chunk whose V rows go out next
@@ -420,6 +421,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
     } while (lhas && ls.t_hi <= ls.t_lo);
     if (lhas) {
       lbt = as_const(a.block_tables) + (int64_t)seq_of(a, ls.s) * a.bt_ss;
+      lkb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, ls.s) + (int64_t)ls.kvh * a.k_sh) * 2;
+      lvb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, ls.s) + (int64_t)ls.kvh * a.v_sh) * 2;
       lcs = ls.t_lo;
       llast = ls.t_hi - 1;
       fetch_blocks(lcs, llast, nblk);
@@ -435,10 +438,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
         dma_q(ls, ring + 4 * HB + (lord & 1) * QB);
         ++lord;
       }
-      const char *kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, ls.s) + (int64_t)ls.kvh * a.k_sh) * 2;
-      const char *vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, ls.s) + (int64_t)ls.kvh * a.v_sh) * 2;
-      const Src k{kb, nblk[0], nblk[1], lcs, llast};
-      vpend = Src{vb, nblk[0], nblk[1], lcs, llast};
+      const Src k{lkb, nblk[0], nblk[1], lcs, llast};
+      vpend = Src{lvb, nblk[0], nblk[1], lcs, llast};
       dma<false>(k, a.k_sb, a.k_st, slot);
       lcs += CT;
       if (lcs < ls.t_hi)

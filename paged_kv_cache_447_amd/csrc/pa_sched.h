@@ -38,7 +38,9 @@ namespace pa {
 
 // A launch's sequence index as (layer, sequence of the layer), and where
 // that sequence's table row, context length, query, output and cache live.
-__device__ __forceinline__ int layer_of(const DecodeArgs &a, int s) { return s / a.seqs_per_layer; }
+__device__ __forceinline__ int layer_of(const DecodeArgs &a, int s) {
+  return a.seqs_per_layer == a.num_seqs ? 0 : s / a.seqs_per_layer;  // one layer: no division
+}
 __device__ __forceinline__ int seq_of(const DecodeArgs &a, int s) { return s - layer_of(a, s) * a.seqs_per_layer; }
 __device__ __forceinline__ int64_t q_row(const DecodeArgs &a, int s) {
   const int l = layer_of(a, s);

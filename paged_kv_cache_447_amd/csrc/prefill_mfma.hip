@@ -73,7 +73,7 @@ struct TileOrder {
   int total;                      // tiles of all sequences (ranked batches)
   int tiles[kWin], before[kWin];  // per lane: its sequence's tiles, and those of the sequences ranked before it
 
-  __device__ void init(const PrefillArgs &a, int lane) {
+  __device__ __forceinline__ void init(const PrefillArgs &a, int lane) {
     ranked = a.num_seqs <= kRanked;
     total = 0;
     if (!ranked) return;
@@ -89,34 +89,45 @@ struct TileOrder {
         L[w] = clamp_ctx(a.context_lens[i], a.max_ctx);
       }
     }
+    rank_against<0>(a, lane, L);
+    rank_against<1>(a, lane, L);
+    rank_against<2>(a, lane, L);
+    rank_against<3>(a, lane, L);
+    static_assert(kWin == 4, "one rank_against per window");
+  }
+
+  // Count, for every lane's sequence, the tiles of window W2's sequences that
+  // rank before it (a template per window keeps every array index static).
+  template <int W2>
+  __device__ __forceinline__ void rank_against(const PrefillArgs &a, int lane, const int *L) {
+    if (64 * W2 >= a.num_seqs) return;
+    const int n = min(64, a.num_seqs - 64 * W2);
+    const int Lw = L[W2], tw = tiles[W2];
+    for (int k = 0; k < n; ++k) {
+      const int Lk = __builtin_amdgcn_readlane(Lw, k), tk = __builtin_amdgcn_readlane(tw, k);
+      total += tk;
 #pragma unroll
-    for (int w2 = 0; w2 < kWin; ++w2) {
-      const int n = min(64, a.num_seqs - 64 * w2);
-      for (int k = 0; k < n; ++k) {
-        const int Lk = __builtin_amdgcn_readlane(L[w2], k), tk = __builtin_amdgcn_readlane(tiles[w2], k);
-        total += tk;
-#pragma unroll
-        for (int w = 0; w < kWin; ++w)
-          if (64 * w < a.num_seqs) before[w] += (Lk > L[w] || (Lk == L[w] && 64 * w2 + k < 64 * w + lane)) ? tk : 0;
-      }
+      for (int w = 0; w < kWin; ++w)
+        if (64 * w < a.num_seqs) before[w] += (Lk > L[w] || (Lk == L[w] && 64 * W2 + k < 64 * w + lane)) ? tk : 0;
     }
   }
 
+  // Tile number t among window W's sequences (ranked batches)
+  template <int W>
+  __device__ __forceinline__ bool find_in(int t, int &seq, int &tile) const {
+    const uint64_t hit = __ballot(tiles[W] > 0 && before[W] <= t && t < before[W] + tiles[W]);
+    if (!hit) return false;
+    const int k = __builtin_ctzll(hit);
+    seq = 64 * W + k;
+    tile = __builtin_amdgcn_readlane(before[W] + tiles[W], k) - 1 - t;
+    return true;
+  }
+
   // The sequence and tile of tile number t; false past the last tile.
-  __device__ bool find(const PrefillArgs &a, int t, int lane, int &seq, int &tile) const {
-    if (ranked) {
-#pragma unroll
-      for (int w = 0; w < kWin; ++w) {
-        const uint64_t hit = __ballot(tiles[w] > 0 && before[w] <= t && t < before[w] + tiles[w]);
-        if (hit) {
-          const int k = __builtin_ctzll(hit);
-          seq = 64 * w + k;
-          tile = __builtin_amdgcn_readlane(before[w] + tiles[w], k) - 1 - t;
-          return true;
-        }
-      }
-      return false;
-    }
+  __device__ __forceinline__ bool find(const PrefillArgs &a, int t, int lane, int &seq, int &tile) const {
+    if (ranked)
+      return find_in<0>(t, seq, tile) || find_in<1>(t, seq, tile) || find_in<2>(t, seq, tile) ||
+             find_in<3>(t, seq, tile);
     int carry = 0;
     for (int base = 0; base < a.num_seqs; base += 64) {
       const int i = base + lane;

@@ -45,7 +45,7 @@ def lib():
 
 def test_header_declares_the_operations():
     syms = declared_symbols()
-    for s in ("pa_decode", "pa_prefill", "pa_cache_write", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
+    for s in ("pa_decode", "pa_decode_layers", "pa_prefill", "pa_cache_write", "pa_copy_blocks", "pa_decode_workspace_size", "pa_decode_num_workers", "pa_status_string",
               "pa_last_error"):
         assert s in syms
 
@@ -303,3 +303,23 @@ def test_copy_blocks_errors(lib):
     expect(lib, call_copy(lib, good_copy()), -7, "pinned host memory")
     # nothing to copy: OK without looking at the pointers
     assert call_copy(lib, good_copy(M=0)) == 0
+
+
+def test_decode_layers_errors(lib):
+    L, S, H, Hkv, D, NB, bs, W = 3, 4, 8, 2, 128, 64, 16, 8
+
+    def args(qshape=(L, S, H, D), kshape=(L, NB, bs, Hkv, D), kstrides=None):
+        return [T(list(qshape), pa.PA_F16), T(list(qshape), pa.PA_F16), T(list(kshape), pa.PA_F16, strides=kstrides),
+                T(list(kshape), pa.PA_F16), T([S, W], pa.PA_I32), T([S], pa.PA_I32)]
+
+    def call(a, opts=None):
+        return lib.pa_decode_layers(*a, bs, 0.1, Hkv, ctypes.byref(opts or pa.PaOpts()))
+
+    expect(lib, call(args(qshape=(S, H, D))), -3, "layers")
+    expect(lib, call(args(kshape=(NB, bs, Hkv, D))), -3, "layers")
+    expect(lib, call(args(kshape=(L + 1, NB, bs, Hkv, D))), -3, "same number of layers")
+    odd = [NB * bs * Hkv * D + 4, bs * Hkv * D, Hkv * D, D, 1]  # layer stride of 8 bytes past a multiple of 16
+    expect(lib, call(args(kstrides=odd)), -4, "layer stride")
+    # the per-layer checks are pa_decode's: a workspace is required
+    expect(lib, call(args()), -6)
+    assert call(args(qshape=(0, S, H, D), kshape=(0, NB, bs, Hkv, D))) == 0  # no layers: nothing to do

@@ -1,11 +1,11 @@
-"""Checks on the gfx950 assembly of the matrix-core decode kernels (CPU only).
+"""Checks on the gfx950 assembly of the matrix-core kernels (CPU only).
 
 The transposed V reads are issued as inline assembly and their completion is
 awaited with an explicit lgkmcnt wait that names the destination registers.
 The compiler does not see the reads as asynchronous, so nothing but this test
 guarantees that it never reads, copies or overwrites a destination register
-between the read and its wait.  The test also checks that no decode kernel
-keeps anything in scratch memory.
+between the read and its wait.  The test also checks that no matrix-core
+kernel (decode, prefill) keeps anything in scratch memory.
 """
 
 import os
@@ -17,7 +17,7 @@ import pytest
 
 from paged_kv_cache_447_amd import build as B
 
-SRC = os.path.join(B.CSRC, "decode_mfma.hip")
+SOURCES = ["decode_mfma.hip", "prefill_mfma.hip"]
 
 
 @pytest.fixture(scope="module")
@@ -25,16 +25,24 @@ def asm(tmp_path_factory):
     hipcc = B.hipcc()
     if not (os.path.exists(hipcc) or shutil.which(hipcc)):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "decode_mfma.s"
-    cmd = [hipcc, "-x", "hip", *B.COMMON, *B.DEVICE, "--offload-device-only", "-S", SRC, "-o", str(out)]
-    proc = subprocess.run(cmd, capture_output=True, text=True)
-    assert proc.returncode == 0, proc.stderr[-2000:]
-    text = out.read_text()
+    d = tmp_path_factory.mktemp("asm")
+    procs = []
+    for src in SOURCES:  # both files compile at once
+        out = d / (src + ".s")
+        cmd = [hipcc, "-x", "hip", *B.COMMON, *B.DEVICE, "--offload-device-only", "-S", os.path.join(B.CSRC, src),
+               "-o", str(out)]
+        procs.append((src, out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     kernels = {}
-    for name in re.findall(r"^(_Z\S*decode_mfma\S*):", text, re.M):
-        i = text.index(name + ":")
-        kernels[name] = text[i:text.index(".Lfunc_end", i)].split("\n")
-    assert kernels, "no decode kernels found in the assembly"
+    for src, out, p in procs:
+        _, err = p.communicate()
+        assert p.returncode == 0, err[-2000:]
+        text = out.read_text()
+        stem = src.split(".")[0]
+        found = re.findall(r"^(_Z\S*" + stem + r"\S*):", text, re.M)
+        assert found, f"no {stem} kernels found in the assembly"
+        for name in found:
+            i = text.index(name + ":")
+            kernels[name] = text[i:text.index(".Lfunc_end", i)].split("\n")
     return kernels
 
 

@@ -1,0 +1,126 @@
+"""GPU parity of multi-layer decode (pa_decode_layers through the C ABI)
+against the multi-layer oracle: each step writes every layer's new token with
+one pa_cache_write over the flattened pools, then decodes all layers in one
+launch.  Run on an MI355X with ``pytest -m gpu``."""
+
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_447_amd as pa
+from pa_workloads import get_config, make_layout, scaled
+from pa_workloads.layers import LAYER_CONFIGS, LayerConfig, flat_slots, make_layer_inputs
+from tests.gpu_common import NTHREADS, TOL_F32, TOL_OUT, host_inputs, log, max_abs_err
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_layer_step(lcfg, inp, out_dtype=None, partition_size=0, num_workers=0, workspace=None):
+    cfg = lcfg.base
+    L = lcfg.num_layers
+    NB, bs = cfg.num_blocks, cfg.block_size
+    kc = inp["k_cache"].view((L * NB,) + tuple(inp["k_cache"].shape[2:]))
+    vc = inp["v_cache"].view((L * NB,) + tuple(inp["v_cache"].shape[2:]))
+    kn = inp["k_new"].reshape((-1,) + tuple(inp["k_new"].shape[2:]))
+    vn = inp["v_new"].reshape((-1,) + tuple(inp["v_new"].shape[2:]))
+    pa.cache_write(kn, vn, kc, vc, flat_slots(inp["slot_mapping"], L, NB * bs),
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    out = torch.empty(inp["q"].shape, dtype=out_dtype or inp["q"].dtype, device=inp["q"].device)
+    pa.decode_layers(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                     cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
+                     v_scale=inp["v_scale"], partition_size=partition_size, num_workers=num_workers,
+                     workspace=workspace)
+    return out
+
+
+def oracle_layer_step(lcfg, host, seqs=None):
+    cfg = lcfg.base
+    kc, vc = host["k_cache"].clone(), host["v_cache"].clone()
+    for l in range(lcfg.num_layers):
+        oracle.cache_write(host["k_new"][l], host["v_new"][l], kc[l], vc[l], host["slot_mapping"],
+                           host["k_scale"], host["v_scale"], inplace=True)
+    q, bt, ctx = host["q"], host["block_tables"], host["context_lens"]
+    if seqs is not None:
+        q, bt, ctx = q[:, seqs].contiguous(), bt[seqs].contiguous(), ctx[seqs].contiguous()
+    return oracle.paged_decode_layers(q, kc, vc, bt, ctx, cfg.softmax_scale, cfg.num_kv_heads, host["k_scale"],
+                                      host["v_scale"], nthreads=NTHREADS), kc, vc
+
+
+SMALL = {
+    "mha_f16": LayerConfig("mha_f16", scaled(get_config("llama7b"), num_seqs=7, num_heads=4, num_kv_heads=4,
+                                             num_blocks=200, max_blocks_per_seq=40, ctx_hi=600), 3),
+    "gqa8_bf16": LayerConfig("gqa8_bf16", scaled(get_config("gqa70b"), num_seqs=9, num_heads=16, num_kv_heads=2,
+                                                 kv_dtype="bf16", q_dtype="bf16", num_blocks=700,
+                                                 max_blocks_per_seq=48, ctx_hi=1500), 4),
+    "fp8_gqa4_d64": LayerConfig("fp8_gqa4_d64", scaled(get_config("fp8_long"), num_seqs=3, num_heads=8,
+                                                       num_kv_heads=2, head_dim=64, num_blocks=300,
+                                                       max_blocks_per_seq=96, ctx_lo=1, ctx_hi=1500,
+                                                       partition_size=0), 2),
+    "f32_tiny": LayerConfig("f32_tiny", get_config("tiny"), 5),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("split", [(0, 0), (64, 0), (0, 8)], ids=["default", "p64", "w8"])
+def test_small_layer_steps_match_oracle(case, split):
+    lcfg = SMALL[case]
+    cfg = lcfg.base
+    part = split[0] if split[0] % cfg.block_size == 0 else 0
+    log(f"[{case} p={part} w={split[1]}]")
+    layout = make_layout(cfg)
+    inp = make_layer_inputs(lcfg, layout, "cuda")
+    host = host_inputs(inp)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads, split[1])
+    out = gpu_layer_step(lcfg, inp, partition_size=part, num_workers=split[1], workspace=ws)
+    out32 = torch.empty(inp["q"].shape, dtype=torch.float32, device="cuda")
+    pa.decode_layers(out32, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                     cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
+                     v_scale=inp["v_scale"], partition_size=part, num_workers=split[1], workspace=ws)
+    torch.cuda.synchronize()
+    ref, kc, vc = oracle_layer_step(lcfg, host)
+    assert torch.equal(inp["k_cache"].cpu().view(torch.uint8), kc.view(torch.uint8))
+    assert torch.equal(inp["v_cache"].cpu().view(torch.uint8), vc.view(torch.uint8))
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    log(f"    err={err:.3e} err32={err32:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
+    assert int(ws[: 4 * lcfg.num_layers * cfg.num_seqs * cfg.num_kv_heads].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_CONFIGS))
+def test_full_size_layer_step_sampled_sequences(name):
+    """The benchmark's multi-layer workloads at full size: all outputs finite,
+    and 6 sequences of every layer against the oracle."""
+    lcfg = LAYER_CONFIGS[name]
+    cfg = lcfg.base
+    log(f"[{name}] generating")
+    layout = make_layout(cfg)
+    inp = make_layer_inputs(lcfg, layout, "cuda")
+    host = host_inputs(inp)
+    out = gpu_layer_step(lcfg, inp)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    seqs = torch.tensor(sorted({0, 1, cfg.num_seqs // 2, cfg.num_seqs - 2, cfg.num_seqs - 1,
+                                int(layout.context_lens.argmax())}))
+    log(f"[{name}] oracle on sequences {seqs.tolist()}")
+    ref, _, _ = oracle_layer_step(lcfg, host, seqs)
+    err = max_abs_err(out[:, seqs.cuda()], ref)
+    log(f"    err={err:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype]
+
+
+def test_each_layer_equals_a_single_layer_decode():
+    """Layer l of one multi-layer launch against pa_decode on layer l alone (the
+    two launches cut the contexts at different places, so they agree to fp32
+    rounding, not bit for bit)."""
+    lcfg = SMALL["gqa8_bf16"]
+    cfg = lcfg.base
+    layout = make_layout(cfg)
+    inp = make_layer_inputs(lcfg, layout, "cuda")
+    out = gpu_layer_step(lcfg, inp, out_dtype=torch.float32)
+    for l in range(lcfg.num_layers):
+        single = torch.empty(inp["q"][l].shape, dtype=torch.float32, device="cuda")
+        pa.decode(single, inp["q"][l], inp["k_cache"][l], inp["v_cache"][l], inp["block_tables"],
+                  inp["context_lens"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads)
+        torch.cuda.synchronize()
+        assert (single - out[l]).abs().max().item() <= 1e-5, l
