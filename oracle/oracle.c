@@ -24,7 +24,9 @@
  *     reading KV head h / (num_heads / num_kv_heads).
  *   - fp8 KV holds OCP e4m3fn codes; a stored value is code_value * scale with
  *     one fp32 scale per tensor (page "大模型推理KV Cache内存管理与PagedAttention分页
- *     显存实战", closing paragraph on FP8 KV caches).
+ *     显存实战", closing paragraph on FP8 KV caches), or one per kv head: the
+ *     scale of the head the element belongs to (precision set per attention
+ *     head, page "vLLM框架中的KV cache优化与PagedAttention机制详解", section 8.2).
  *   - The cache write puts the K/V row of new token n at slot_mapping[n], slot
  *     = block * block_size + offset, and skips negative slots.
  *   - Prefill (several query tokens per sequence): the query rows of sequence
@@ -165,6 +167,7 @@ typedef struct {
   const int32_t *block_tables, *context_lens;
   int64_t num_seqs, num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks;
   double scale, k_scale, v_scale;
+  const double *k_heads, *v_heads; /* fp8: one scale per kv head instead of k_scale / v_scale, or NULL */
   /* work distribution */
   int64_t next_item;
   pthread_mutex_t lock;
@@ -184,8 +187,11 @@ static int decode_item(decode_job *J, int64_t seq, int64_t kvh, double *Kc, doub
     return ORC_OK;
   }
   if ((L + bs - 1) / bs > J->max_blocks) return ORC_CTX_TOO_LONG;
-  const double ks = (J->kv_dtype == ORC_FP8) ? J->k_scale : 1.0;
-  const double vs = (J->kv_dtype == ORC_FP8) ? J->v_scale : 1.0;
+  double ks = 1.0, vs = 1.0;
+  if (J->kv_dtype == ORC_FP8) {
+    ks = J->k_heads ? J->k_heads[kvh] : J->k_scale;
+    vs = J->v_heads ? J->v_heads[kvh] : J->v_scale;
+  }
 
   for (int64_t t = 0; t < L; ++t) {
     int64_t blk = J->block_tables[seq * J->max_blocks + t / bs];
@@ -258,7 +264,8 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
                         int kv_dtype, const int32_t *block_tables, const int32_t *context_lens,
                         int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads, int64_t head_dim,
                         int64_t num_blocks, int64_t block_size, int64_t max_blocks_per_seq, double scale,
-                        double k_scale, double v_scale, int nthreads) {
+                        double k_scale, double v_scale, const double *k_head_scale, const double *v_head_scale,
+                        int nthreads) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return ORC_BAD_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0)
@@ -284,6 +291,9 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
   J.scale = scale;
   J.k_scale = k_scale;
   J.v_scale = v_scale;
+  if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
+  J.k_heads = k_head_scale;
+  J.v_heads = v_head_scale;
   J.status = ORC_OK;
   pthread_mutex_init(&J.lock, NULL);
   if (nthreads < 1) nthreads = 1;
@@ -458,11 +468,15 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
 
 /* k, v: [num_tokens, num_kv_heads, head_dim] in in_dtype; caches as above in
  * cache_dtype.  Same dtype: the bytes are copied.  fp8 cache: each element is
- * converted to fp32, divided by the tensor's fp32 scale in fp32, and encoded
- * with oracle_float_to_fp8.  Validates every slot before writing anything. */
+ * converted to fp32, divided in fp32 by its scale -- the tensor's fp32 scale,
+ * or its kv head's when k_head_scale / v_head_scale ([num_kv_heads]) are
+ * given -- and encoded with oracle_float_to_fp8.  Validates every slot before
+ * writing anything. */
 int oracle_cache_write(const void *k, const void *v, int in_dtype, void *k_cache, void *v_cache, int cache_dtype,
                        const int64_t *slot_mapping, int64_t num_tokens, int64_t num_kv_heads, int64_t head_dim,
-                       int64_t num_blocks, int64_t block_size, float k_scale, float v_scale) {
+                       int64_t num_blocks, int64_t block_size, float k_scale, float v_scale,
+                       const float *k_head_scale, const float *v_head_scale) {
+  if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return ORC_BAD_ARG;
   if (!elem_size(in_dtype) || !elem_size(cache_dtype)) return ORC_BAD_ARG;
   if (in_dtype != cache_dtype && !(cache_dtype == ORC_FP8 && in_dtype != ORC_FP8)) return ORC_BAD_ARG;
@@ -483,11 +497,12 @@ int oracle_cache_write(const void *k, const void *v, int in_dtype, void *k_cache
     for (int which = 0; which < 2; ++which) {
       const void *src = which ? v : k;
       char *cache = (char *)(which ? v_cache : k_cache);
-      const float sc = which ? v_scale : k_scale;
+      const float *heads = which ? v_head_scale : k_head_scale;
       if (in_dtype == cache_dtype) {
         memcpy(cache + dst * es_c, (const char *)src + n * row * es_in, (size_t)(row * es_c));
       } else {
         for (int64_t i = 0; i < row; ++i) {
+          const float sc = heads ? heads[i / head_dim] : (which ? v_scale : k_scale);
           float x = (float)load_elem(src, in_dtype, n * row + i);
           ((uint8_t *)cache)[dst + i] = oracle_float_to_fp8(x / sc);
         }

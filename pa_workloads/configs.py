@@ -46,6 +46,11 @@ class DecodeConfig:
     churn_band: Tuple[float, float] = (0.70, 0.90)
     partition_size: int = 0  # tokens per split-context partition, 0 = library choice
     scale: Optional[float] = None  # softmax scale, default 1/sqrt(head_dim)
+    # fp8 caches: "tensor" = one scale per K / V tensor, "head" = one per kv head
+    fp8_scales: str = "tensor"
+    # standard deviation of kv head h's K and V values, geometric from the first
+    # to the second number over the heads (heads of different magnitude)
+    head_std: Tuple[float, float] = (1.0, 1.0)
 
     @property
     def group_size(self) -> int:
@@ -98,6 +103,18 @@ CONFIGS = {
         block_size=16, num_blocks=20480, max_blocks_per_seq=2048, kv_dtype="fp8", q_dtype="f16",
         ctx_kind="uniform", ctx_lo=16384, ctx_hi=32768, allocator="shuffled",
         partition_size=512,
+    ),
+    # The 70B-shaped grouped-query step with an fp8-e4m3 cache and one scale per
+    # kv head (an fp8 KV cache on a 70B model, page "大模型推理KV Cache内存管理与
+    # PagedAttention分页显存实战"; precision chosen per head, page "vLLM框架中的KV
+    # cache优化与PagedAttention机制详解" section 8.2).  The kv heads' K/V values
+    # range from std 1/4 to std 4, so one scale per tensor would leave the
+    # quiet heads a few bits.
+    "gqa70b_fp8": DecodeConfig(
+        name="gqa70b_fp8", seed=6, num_seqs=128, num_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=32, num_blocks=40000, max_blocks_per_seq=256, kv_dtype="fp8", q_dtype="f16",
+        ctx_kind="lognormal", ctx_median=1024.0, ctx_sigma=1.0, ctx_lo=1, ctx_hi=8192,
+        allocator="churn", fp8_scales="head", head_std=(0.25, 4.0),
     ),
 }
 

@@ -244,21 +244,30 @@ def torch_dtype(name: str):
     }[name]
 
 
-def _pool_masked_amax(shape, gen_seed, mask_t, device, chunk_blocks):
+def head_stds(cfg: DecodeConfig) -> np.ndarray:
+    """float32 [num_kv_heads]: the standard deviation of each kv head's K and V
+    values (geometric from cfg.head_std[0] to cfg.head_std[1])."""
+    lo, hi = cfg.head_std
+    n = cfg.num_kv_heads
+    return np.geomspace(lo, hi, n).astype(np.float32) if n > 1 else np.array([lo], dtype=np.float32)
+
+
+def _pool_masked_amax(shape, gen_seed, mask_t, device, chunk_blocks, std_t):
+    """float32 [num_kv_heads]: the largest stored magnitude of each kv head."""
     import torch
 
     g = torch.Generator(device=device)
     g.manual_seed(gen_seed)
-    amax = torch.zeros((), dtype=torch.float32, device=device)
+    amax = torch.zeros((shape[2],), dtype=torch.float32, device=device)
     for b0 in range(0, shape[0], chunk_blocks):
         b1 = min(shape[0], b0 + chunk_blocks)
-        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32) * std_t
         m = mask_t[b0:b1, :, None, None]
-        amax = torch.maximum(amax, torch.where(m, x.abs(), torch.zeros_like(x)).amax())
-    return float(amax.item())
+        amax = torch.maximum(amax, torch.where(m, x.abs(), torch.zeros_like(x)).amax(dim=(0, 1, 3)))
+    return amax
 
 
-def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, quant_scale=None):
+def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, std_t, quant_scale=None):
     import torch
 
     g = torch.Generator(device=device)
@@ -266,7 +275,7 @@ def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, quant_
     out = torch.empty(shape, dtype=torch_dtype(dtype_name), device=device)
     for b0 in range(0, shape[0], chunk_blocks):
         b1 = min(shape[0], b0 + chunk_blocks)
-        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32)
+        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32) * std_t
         m = mask_t[b0:b1, :, None, None].expand_as(x)
         if dtype_name == "fp8":
             codes = (x / quant_scale).to(torch.float8_e4m3fn).view(torch.uint8)
@@ -283,9 +292,12 @@ def make_inputs(cfg: DecodeConfig, layout: Layout, device="cpu", seed_offset: in
 
     Returns torch tensors on ``device``: q [S,H,D]; k_cache/v_cache
     [num_blocks, block_size, Hkv, D]; k_new/v_new [S, Hkv, D]; int32
-    context_lens and block_tables; int64 slot_mapping; plus fp32 k_scale/v_scale
-    (per-tensor fp8 scales, 1.0 for other dtypes).  fp8 scales are chosen so the
-    largest stored magnitude (new tokens included) maps just under 448.
+    context_lens and block_tables; int64 slot_mapping; plus k_scale/v_scale:
+    per-tensor fp8 scales (floats; 1.0 for other dtypes), or for workloads with
+    per-head fp8 scales float32 tensors [Hkv] on ``device``.  fp8 scales are
+    chosen so the largest stored magnitude of the tensor (or of the kv head),
+    new tokens included, maps just under 448.  Kv head h's values are N(0, 1)
+    times head_stds(cfg)[h].
     """
     import torch
 
@@ -299,20 +311,37 @@ def make_inputs(cfg: DecodeConfig, layout: Layout, device="cpu", seed_offset: in
     gq.manual_seed(base + 1)
     q = torch.randn((S, H, D), generator=gq, device=device, dtype=torch.float32).to(torch_dtype(cfg.q_dtype))
     new_dtype = cfg.q_dtype if cfg.kv_dtype == "fp8" else cfg.kv_dtype
+    std_np = head_stds(cfg)
+    std_t = torch.from_numpy(std_np).to(device).reshape(1, 1, Hkv, 1)
     gn = torch.Generator(device=device)
     gn.manual_seed(base + 4)
-    k_new = torch.randn((S, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
-    v_new = torch.randn((S, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
+    k_new = (torch.randn((S, Hkv, D), generator=gn, device=device, dtype=torch.float32) * std_t[0]) \
+        .to(torch_dtype(new_dtype))
+    v_new = (torch.randn((S, Hkv, D), generator=gn, device=device, dtype=torch.float32) * std_t[0]) \
+        .to(torch_dtype(new_dtype))
 
     k_scale = v_scale = 1.0
+    k_q = v_q = None  # what the pool's values are divided by before encoding
     if cfg.kv_dtype == "fp8":
-        ka = max(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks), float(k_new.float().abs().max()))
-        va = max(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks), float(v_new.float().abs().max()))
+        ka = torch.maximum(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks, std_t),
+                           k_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
+        va = torch.maximum(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks, std_t),
+                           v_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
         # float32 scales, nudged up so that |x| / scale stays below 448 after rounding
-        k_scale = float(np.float32(ka / FP8_MAX * (1.0 + 2.0**-16)))
-        v_scale = float(np.float32(va / FP8_MAX * (1.0 + 2.0**-16)))
-    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, k_scale)
-    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, v_scale)
+        if cfg.fp8_scales == "head":
+            kh = (ka / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)
+            vh = (va / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)
+            k_scale = torch.from_numpy(kh).to(device)
+            v_scale = torch.from_numpy(vh).to(device)
+            k_q, v_q = k_scale.reshape(1, 1, Hkv, 1), v_scale.reshape(1, 1, Hkv, 1)
+        elif cfg.fp8_scales == "tensor":
+            k_scale = float(np.float32(ka.max() / FP8_MAX * (1.0 + 2.0**-16)))
+            v_scale = float(np.float32(va.max() / FP8_MAX * (1.0 + 2.0**-16)))
+            k_q, v_q = k_scale, v_scale
+        else:
+            raise ValueError(cfg.fp8_scales)
+    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, std_t, k_q)
+    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, std_t, v_q)
 
     return {
         "q": q,
@@ -343,5 +372,6 @@ def algorithmic_bytes(cfg: DecodeConfig, context_lens: np.ndarray, out_dtype: st
     out_dtype = out_dtype or cfg.q_dtype
     S, H, D = cfg.num_seqs, cfg.num_heads, cfg.head_dim
     table = 4 * int((-(-ctx // cfg.block_size)).sum())
+    head_scales = 2 * 4 * cfg.num_kv_heads if (cfg.kv_dtype == "fp8" and cfg.fp8_scales == "head") else 0
     return (kv_bytes(cfg, ctx) + S * H * D * (ELEM_BYTES[cfg.q_dtype] + ELEM_BYTES[out_dtype])
-            + table + 4 * S)
+            + table + 4 * S + head_scales)

@@ -132,13 +132,16 @@ def make_prefill_inputs(pcfg: PrefillConfig, pl: PrefillLayout, device="cpu", se
     k_new = torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
     v_new = torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
     k_scale = v_scale = 1.0
+    ones = torch.ones((1, 1, Hkv, 1), dtype=torch.float32, device=device)
     if cfg.kv_dtype == "fp8":
-        ka = max(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks), float(k_new.float().abs().max()))
-        va = max(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks), float(v_new.float().abs().max()))
+        ka = max(float(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks, ones).max()),
+                 float(k_new.float().abs().max()))
+        va = max(float(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks, ones).max()),
+                 float(v_new.float().abs().max()))
         k_scale = float(np.float32(ka / FP8_MAX * (1.0 + 2.0**-16)))
         v_scale = float(np.float32(va / FP8_MAX * (1.0 + 2.0**-16)))
-    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, k_scale)
-    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, v_scale)
+    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, ones, k_scale)
+    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, ones, v_scale)
     L = pl.layout
     return {
         "q": q,
