@@ -236,6 +236,7 @@ def main():
             "num_workers": pa.num_workers(args.num_workers),
             "input_sets": nsets,
             "kv_bytes_per_step": step_kv,
+            **({"fp8_scales": f"one per {cfg.fp8_scales}"} if cfg.kv_dtype == "fp8" else {}),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),

@@ -100,6 +100,17 @@ typedef struct pa_opts {
   void *workspace;        /* decode: device scratch of >= pa_decode_workspace_size() bytes */
   size_t workspace_bytes;
   void *stream;           /* hipStream_t the work is enqueued on; NULL = null stream */
+  /* fp8 caches, finer scales: NULL, or fp32 arrays with one scale per kv head
+   * (pa_decode_layers: [layers, num_kv_heads], layer-major), in device memory
+   * or pinned host memory.  The stored value of kv head h is then
+   * code * k_head_scales[h] (v_head_scales[h] for the value cache), so that
+   * heads of small magnitude keep their precision (the precision per attention
+   * head of section 8.2 of page "vLLM框架中的KV cache优化与PagedAttention机制详解";
+   * the fp8 KV cache of page "大模型推理KV Cache内存管理与PagedAttention分页显存实战").
+   * Both or neither; with them k_scale and v_scale must be 0.  The contents are
+   * trusted like the block tables: finite and > 0, else results are unspecified. */
+  const float *k_head_scales;
+  const float *v_head_scales;
 } pa_opts;
 
 /* Number of workers pa_decode launches for this request (0 = the library's
@@ -130,7 +141,8 @@ PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int6
  *   k_cache,
  *   v_cache      [num_blocks, block_size, num_kv_heads, head_dim], same shape and
  *                dtype: PA_F32 / PA_F16 / PA_BF16 equal to q's dtype, or PA_FP8_E4M3
- *                with an F16 or BF16 q (values are code * opts->k_scale / v_scale).
+ *                with an F16 or BF16 q (values are code * opts->k_scale / v_scale,
+ *                or code * the kv head's entry of opts->k_head_scales / v_head_scales).
  *   block_tables [num_seqs, max_blocks_per_seq] PA_I32; only the first
  *                ceil(context_lens[s] / block_size) entries of row s are read.
  *   context_lens [num_seqs] PA_I32.
@@ -165,6 +177,7 @@ PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
  *   on that layer's q, caches and out.  The layer stride of each tensor must be
  *   a multiple of 16 bytes.
  *   opts->workspace: pa_decode_workspace_size(layers * num_seqs, ...) bytes.
+ *   opts->k_head_scales / v_head_scales (fp8 caches): [layers, num_kv_heads].
  * Work: one launch; the (layer, sequence) pairs are the items of pa_decode's
  * split, so the launch's fixed cost and its finishing spread are paid once for
  * all layers.
@@ -222,7 +235,10 @@ PA_API pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_te
  *                 sequences share is the caller's responsibility.
  * Same-dtype writes copy the bytes.  fp8 writes store
  * round-to-nearest-even(x / scale) saturated to +-448 (NaN stays NaN), the
- * division done in fp32, with scale = opts->k_scale / v_scale.
+ * division done in fp32, with scale = opts->k_scale / v_scale, or the scale of
+ * the row's kv head when opts->k_head_scales / v_head_scales are given
+ * ([num_kv_heads] each; ignored, like the per-tensor scales, when k is itself
+ * FP8_E4M3 and its codes are copied).
  */
 PA_API pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor v_cache,
                                 pa_tensor slot_mapping, const pa_opts *opts);

@@ -65,6 +65,8 @@ class PaOpts(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("k_head_scales", ctypes.c_void_p),
+        ("v_head_scales", ctypes.c_void_p),
     ]
 
 
@@ -164,6 +166,28 @@ def _raise(lib, status: int):
     raise PaError(status, lib.pa_last_error().decode(errors="replace"))
 
 
+def _set_scales(o: PaOpts, k_scale, v_scale, count: int) -> None:
+    """fp8 scales into the options: floats are per-tensor scales; fp32 tensors
+    of ``count`` elements (one scale per kv head, [num_kv_heads] or [layers,
+    num_kv_heads], on the device or in pinned host memory) are per-head
+    scales."""
+    import torch
+
+    if torch.is_tensor(k_scale) or torch.is_tensor(v_scale):
+        if not (torch.is_tensor(k_scale) and torch.is_tensor(v_scale)):
+            raise ValueError("k_scale and v_scale: both per-head tensors or both floats")
+        for t in (k_scale, v_scale):
+            if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != count:
+                raise ValueError(f"per-head scales must be contiguous float32 tensors of {count} elements")
+        o.k_scale = 0.0
+        o.v_scale = 0.0
+        o.k_head_scales = k_scale.data_ptr()
+        o.v_head_scales = v_scale.data_ptr()
+    else:
+        o.k_scale = float(k_scale)
+        o.v_scale = float(v_scale)
+
+
 def num_workers(requested: int = 0) -> int:
     """Workers pa_decode launches for this request (0 = the library's choice for the current device)."""
     return int(load_library().pa_decode_num_workers(requested))
@@ -189,20 +213,21 @@ def new_workspace(q, num_kv_heads: int, num_workers: int = 0):
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float, num_kv_heads: int,
-           k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0, num_workers: int = 0, workspace=None,
+           k_scale=1.0, v_scale=1.0, partition_size: int = 0, num_workers: int = 0, workspace=None,
            stream=None):
     """pa_decode: fill ``out`` [S, H, D] with paged attention over the cache; returns ``out``.
 
     ``workspace`` is a zero-filled device tensor from new_workspace() (made
     here, once per call, if not given; pass one to avoid that allocation).
+    ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale per tensor, or
+    float32 tensors [num_kv_heads], one scale per kv head.
     """
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
     if workspace is None:
         workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
-    o.k_scale = k_scale
-    o.v_scale = v_scale
+    _set_scales(o, k_scale, v_scale, num_kv_heads)
     o.partition_size = partition_size
     o.num_workers = num_workers
     o.workspace = workspace.data_ptr()
@@ -216,7 +241,7 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
 
 
 def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_size: int, scale: float,
-                  num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, partition_size: int = 0,
+                  num_kv_heads: int, k_scale=1.0, v_scale=1.0, partition_size: int = 0,
                   num_workers: int = 0, workspace=None, stream=None):
     """pa_decode_layers: ``out`` [L, S, H, D] = pa_decode of every layer l on q[l],
     k_caches[l], v_caches[l] ([L, NB, bs, Hkv, D]), with the block tables and
@@ -226,8 +251,7 @@ def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_
     if workspace is None:
         workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
-    o.k_scale = k_scale
-    o.v_scale = v_scale
+    _set_scales(o, k_scale, v_scale, q.shape[0] * num_kv_heads)
     o.partition_size = partition_size
     o.num_workers = num_workers
     o.workspace = workspace.data_ptr()
@@ -258,13 +282,12 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     return out
 
 
-def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale: float = 1.0, v_scale: float = 1.0, stream=None):
+def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None):
     """pa_cache_write: scatter rows of k, v [N, Hkv, D] into the caches at slot_mapping [N]."""
     lib = load_library()
     _check_device(k, v, k_cache, v_cache, slot_mapping)
     o = PaOpts()
-    o.k_scale = k_scale
-    o.v_scale = v_scale
+    _set_scales(o, k_scale, v_scale, k.shape[1])
     o.stream = stream if stream is not None else _current_stream(k)
     st = lib.pa_cache_write(describe(k), describe(v), describe(k_cache), describe(v_cache), describe(slot_mapping),
                             ctypes.byref(o))

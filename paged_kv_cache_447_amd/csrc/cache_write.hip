@@ -88,11 +88,13 @@ __global__ void __launch_bounds__(kThreads) cache_quant_kernel(const CacheWriteA
   char *dst = reinterpret_cast<char *>(is_v ? a.v_cache : a.k_cache);
   const int64_t s_n = is_v ? a.v_sn : a.k_sn, s_h = is_v ? a.v_sh : a.k_sh;
   const int64_t c_b = is_v ? a.vc_sb : a.kc_sb, c_t = is_v ? a.vc_st : a.kc_st, c_h = is_v ? a.vc_sh : a.kc_sh;
-  const float scale = is_v ? a.v_scale : a.k_scale;
+  const float *head_scale = is_v ? a.v_head_scale : a.k_head_scale;  // null: one scale for the tensor
+  const float tensor_scale = is_v ? a.v_scale : a.k_scale;
   const int per_head = a.head_dim / 16;
   const int total = a.num_kv_heads * per_head;
   for (int i = threadIdx.x; i < total; i += kThreads) {
     const int h = i / per_head, c = (i % per_head) * 16;
+    const float scale = head_scale ? head_scale[h] : tensor_scale;
     const int64_t sb = (int64_t)n * s_n + (int64_t)h * s_h + c;
     constexpr int IVEC = Elem<InT>::kPer16;
     float x[16];

@@ -85,17 +85,18 @@ struct MfmaMath : MfmaCore<MT, D> {
   static_assert(G >= 2 && G <= 16, "group must fit the 16 columns");
 
   const DecodeArgs &a;
+  ItemScale isc;  // the segment's scales (the launch's, or its fp8 kv head's)
 
-  __device__ MfmaMath(const DecodeArgs &args, int lane) : Core(lane), a(args) {}
+  __device__ MfmaMath(const DecodeArgs &args, int lane) : Core(lane), a(args), isc{args.qk_scale_log2, args.v_scale} {}
 
   // online softmax for head c16 (tokens past `last` masked)
   __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, u32x4 &phi, u32x4 &plo) {
-    Core::weights(sc, cs, last, a.qk_scale_log2, phi, plo);
+    Core::weights(sc, cs, last, isc.qk, phi, plo);
   }
 
   __device__ void write_out(int s, int kvh) const {
     if (c16 >= G) return;
-    const float inv = a.v_scale / l;
+    const float inv = isc.v / l;
     const int64_t row = o_row(a, s) + (int64_t)(kvh * G + c16) * a.o_sh;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
@@ -261,6 +262,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
       if (has) begin(nx);
       return;
     }
+    Math::isc = seg_scale<KVT>(a, g.s, g.kvh);
     const Ptrs p = ptrs(g);
     // the chunk after this segment's last one: the next segment's first (or,
     // for the range's last segment, this last chunk again -- a cache hit, unused)

@@ -168,6 +168,7 @@ struct ValuSeg {
   const DecodeArgs &a;
   const int lane, r, tg;  // lane, 16-byte slice of the row, token of a wave-wide load
   float m[G], l[G], acc[G][VEC];
+  float vsc;              // the segment's output scale (fp8 value scale)
 
   __device__ ValuSeg(const DecodeArgs &args, int ln) : a(args), lane(ln), r(ln % LPR), tg(ln / LPR) {}
 
@@ -255,6 +256,8 @@ struct ValuSeg {
       return;
     }
     const Ptrs p = ptrs(g);
+    const ItemScale isc = seg_scale<KVT>(a, g.s, g.kvh);
+    vsc = isc.v;
     // the chunk after this segment's last one: the next segment's first (or,
     // for the range's last segment, this last chunk again -- a cache hit, unused)
     const Ptrs pn = has ? ptrs(nx) : p;
@@ -286,7 +289,7 @@ struct ValuSeg {
       for (int i = 0; i < NL; ++i) {
         const bool valid = cs + i * TPW + tg <= p.last;
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * a.qk_scale_log2 : -INFINITY;
+        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * isc.qk : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
       issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
@@ -346,7 +349,7 @@ struct ValuSeg {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float o[VEC];
-      const float inv = a.v_scale / l[h];
+      const float inv = vsc / l[h];
 #pragma unroll
       for (int v = 0; v < VEC; ++v) o[v] = acc[h][v] * inv;
       const int64_t off = o_row(a, s) + (int64_t)(kvh * G + h) * a.o_sh + r * VEC;

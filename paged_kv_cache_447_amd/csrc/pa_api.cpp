@@ -135,6 +135,26 @@ pa_status device_address(const void *p, const char *name, void **dev) {
   return fail(PA_ERR_ARG, "%s: not device memory or pinned host memory", name);
 }
 
+// Per-kv-head fp8 scales of opts (both or neither, fp8 caches only, not
+// together with per-tensor scales), as device addresses; null when not given.
+pa_status head_scales(const pa_opts &o, int cache_kind, const float **ks, const float **vs) {
+  *ks = *vs = nullptr;
+  if (!o.k_head_scales && !o.v_head_scales) return PA_OK;
+  if (!o.k_head_scales || !o.v_head_scales) return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
+  if (cache_kind != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  if (o.k_scale != 0.0f || o.v_scale != 0.0f)
+    return fail(PA_ERR_ARG, "per-tensor and per-head scales exclude each other: leave k_scale and v_scale at 0");
+  if (reinterpret_cast<uintptr_t>(o.k_head_scales) % 4 || reinterpret_cast<uintptr_t>(o.v_head_scales) % 4)
+    return fail(PA_ERR_LAYOUT, "per-head scales must be 4-byte aligned");
+  void *dk = nullptr, *dv = nullptr;
+  pa_status st;
+  if ((st = device_address(o.k_head_scales, "k_head_scales", &dk))) return st;
+  if ((st = device_address(o.v_head_scales, "v_head_scales", &dv))) return st;
+  *ks = static_cast<const float *>(dk);
+  *vs = static_cast<const float *>(dv);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -207,6 +227,9 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
+    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
+  if (o.k_head_scales && kvk != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
   const int64_t W = block_tables.shape[1];
   if (S > 65535 || num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 sequences or kv heads");
   if (W * block_size > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "table width too large");
@@ -233,6 +256,9 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                 o.workspace ? o.workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+
+  const float *khs = nullptr, *vhs = nullptr;
+  if ((st = head_scales(o, kvk, &khs, &vhs))) return st;
 
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
@@ -274,6 +300,8 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   a.num_workers = nw;
   a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)ks);
   a.v_scale = vs;
+  a.k_head_scale = khs;
+  a.v_head_scale = vhs;
   a.kv_kind = kvk;
   a.q_kind = kv_kind(q.dtype);
   a.out_f32 = out.dtype == PA_F32 && q.dtype != PA_F32;
@@ -376,6 +404,7 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if (o.k_head_scales || o.v_head_scales) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
   const int64_t W = block_tables.shape[1];
   const int64_t G = num_kv_heads > 0 ? H / num_kv_heads : 0;
   if (S > INT32_MAX - 1 || N * G > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many sequences or query rows");
@@ -466,7 +495,12 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
+    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
+  if (o.k_head_scales && ck != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
   if (N == 0 || Hkv == 0 || D == 0) return PA_OK;
+  const float *khs = nullptr, *vhs = nullptr;
+  if ((st = head_scales(o, ck, &khs, &vhs))) return st;
 
   pa::CacheWriteArgs a;
   std::memset(&a, 0, sizeof a);
@@ -495,6 +529,8 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   a.cache_kind = ck;
   a.k_scale = ks;
   a.v_scale = vs;
+  a.k_head_scale = khs;
+  a.v_head_scale = vhs;
   if (a.block_size <= 0) return fail(PA_ERR_SHAPE, "block_size must be positive");
   hipError_t e = pa::launch_cache_write(a, static_cast<hipStream_t>(o.stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache-write kernel launch: %s", hipGetErrorString(e));

@@ -53,6 +53,29 @@ __device__ __forceinline__ int64_t o_row(const DecodeArgs &a, int s) {
 __device__ __forceinline__ int64_t k_layer(const DecodeArgs &a, int s) { return layer_of(a, s) * a.k_sl; }
 __device__ __forceinline__ int64_t v_layer(const DecodeArgs &a, int s) { return layer_of(a, s) * a.v_sl; }
 
+// The scales of item (s, kvh): qk multiplies its scores into log2 units, v
+// its normalised output.  With one fp8 scale per (layer, kv head) they are
+// the launch's scale * log2(e) and 1 times that head's key and value scales;
+// otherwise the launch's own (per-tensor fp8 scales already folded in).
+struct ItemScale {
+  float qk, v;
+};
+__device__ __forceinline__ ItemScale item_scale(const DecodeArgs &a, int s, int kvh) {
+  ItemScale r{a.qk_scale_log2, a.v_scale};
+  if (a.k_head_scale != nullptr) {
+    const int64_t i = (int64_t)layer_of(a, s) * a.num_kv_heads + kvh;
+    r.qk *= a.k_head_scale[i];
+    r.v *= a.v_head_scale[i];
+  }
+  return r;
+}
+// Only fp8 caches carry per-head scales: other kernels keep the launch's.
+template <typename KVT>
+__device__ __forceinline__ ItemScale seg_scale(const DecodeArgs &a, int s, int kvh) {
+  if constexpr (__is_same(KVT, fp8_t)) return item_scale(a, s, kvh);
+  return ItemScale{a.qk_scale_log2, a.v_scale};
+}
+
 // The split of the unit order [0, T) into Ws = min(T, W) equal ranges, range
 // w worked by worker w (never more ranges than units, so none is empty).
 struct Split {
@@ -197,11 +220,12 @@ __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int6
       }
     }
   }
+  const float vsc = item_scale(a, s, kvh).v;
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
     const int e = lane + 64 * k;
     const int head = kvh * G + e / D;
-    store_elem<QT>(a, o_row(a, s) + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * a.v_scale);
+    store_elem<QT>(a, o_row(a, s) + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * vsc);
   }
 }
 

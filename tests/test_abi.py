@@ -323,3 +323,34 @@ def test_decode_layers_errors(lib):
     # the per-layer checks are pa_decode's: a workspace is required
     expect(lib, call(args()), -6)
     assert call(args(qshape=(0, S, H, D), kshape=(0, NB, bs, Hkv, D))) == 0  # no layers: nothing to do
+
+
+def test_head_scale_errors(lib):
+    """Per-kv-head fp8 scales: both or neither, fp8 caches only, never together
+    with per-tensor scales, 4-byte aligned; prefill takes none."""
+    fp8 = dict(kv=pa.PA_FP8_E4M3, q=pa.PA_F16)
+    o = with_workspace()
+    o.k_head_scales = FAKE
+    expect(lib, call_decode(lib, good_decode(**fp8), o), -1, "together")
+    o = with_workspace()
+    o.k_head_scales = o.v_head_scales = FAKE
+    expect(lib, call_decode(lib, good_decode(), o), -7, "FP8")  # 16-bit cache
+    o = with_workspace()
+    o.k_head_scales = o.v_head_scales = FAKE
+    o.k_scale = 0.5
+    expect(lib, call_decode(lib, good_decode(**fp8), o), -7, "exclude")
+    o = with_workspace()
+    o.k_head_scales = FAKE + 2
+    o.v_head_scales = FAKE
+    expect(lib, call_decode(lib, good_decode(**fp8), o), -4, "aligned")
+    w = pa.PaOpts()
+    w.v_head_scales = FAKE
+    expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), w), -1, "together")
+    w = pa.PaOpts()
+    w.k_head_scales = w.v_head_scales = FAKE
+    expect(lib, call_write(lib, good_write(), w), -7, "FP8")
+    w.v_scale = 2.0
+    expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), w), -7, "exclude")
+    p = pa.PaOpts()
+    p.k_head_scales = p.v_head_scales = FAKE
+    expect(lib, call_prefill(lib, good_prefill(), opts=p), -7, "FP8")

@@ -1,0 +1,144 @@
+"""GPU parity of fp8 caches with one scale per kv head, through the C ABI,
+against the fp64 oracle: the cache write (bit-exact over the whole pool),
+single-layer decode on both kernels (vector ALU for groups of 1-2, matrix
+cores for 4-16) across work splits, and multi-layer decode with a row of
+scales per layer."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_447_amd as pa
+from pa_workloads import get_config, scaled
+from pa_workloads.layers import LayerConfig, make_layer_inputs
+from tests.gpu_common import (NTHREADS, TOL_F32, TOL_OUT, gpu_cache_write, gpu_decode, host_inputs, log,
+                              max_abs_err, max_err_beyond_rounding, oracle_step, setup)
+
+pytestmark = pytest.mark.gpu
+
+
+def _bytes(t):
+    return t.detach().cpu().contiguous().view(torch.uint8)
+
+
+def test_full_size_gqa70b_fp8_step_matches_oracle():
+    cfg = get_config("gqa70b_fp8")
+    log(f"[{cfg.name}] generating")
+    layout, inp = setup(cfg)
+    assert torch.is_tensor(inp["k_scale"]) and inp["k_scale"].numel() == cfg.num_kv_heads
+    host = host_inputs(inp)
+    log(f"[{cfg.name}] gpu step")
+    gpu_cache_write(cfg, inp)
+    out = gpu_decode(cfg, inp)
+    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    log(f"[{cfg.name}] oracle")
+    ref, kc, vc = oracle_step(cfg, host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8)), "k_cache differs from the oracle's write"
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8)), "v_cache differs from the oracle's write"
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    log(f"[{cfg.name}] max|err| out={err:.3e} fp32-out={err32:.3e} max|ref|={np.abs(ref).max():.3f}")
+    assert err <= TOL_OUT["fp8"]
+    assert err32 <= TOL_F32["fp8"]
+
+
+_BASE = get_config("gqa70b_fp8")
+SMALL = {
+    "mha_f16q_bs16": scaled(_BASE, num_seqs=6, num_heads=8, num_kv_heads=8, block_size=16, num_blocks=1500,
+                            max_blocks_per_seq=160, ctx_hi=2500, allocator="shuffled"),
+    "gqa2_bf16q_d64": scaled(_BASE, num_seqs=7, num_heads=8, num_kv_heads=4, head_dim=64, q_dtype="bf16",
+                             num_blocks=900, max_blocks_per_seq=80, ctx_hi=2500),
+    "gqa4_f16q_d64_bs16": scaled(_BASE, num_seqs=5, num_heads=16, num_kv_heads=4, head_dim=64, block_size=16,
+                                 num_blocks=1200, max_blocks_per_seq=128, ctx_hi=2000, allocator="shuffled"),
+    "gqa8_f16q": scaled(_BASE, num_seqs=9, num_blocks=1500, max_blocks_per_seq=64, ctx_hi=2048),
+    "gqa16_bf16q": scaled(_BASE, num_seqs=5, num_heads=32, num_kv_heads=2, q_dtype="bf16", num_blocks=700,
+                          max_blocks_per_seq=64, ctx_hi=2048),
+}
+SPLITS = [(0, 0), (256, 0), (0, 7), (32, 65536)]
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+@pytest.mark.parametrize("split", SPLITS, ids=[f"p{p}w{w}" for p, w in SPLITS])
+def test_small_head_scale_cases_match_oracle(case, split):
+    cfg = SMALL[case]
+    part, workers = split
+    log(f"[{case} p={part} w={workers}]")
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    gpu_cache_write(cfg, inp)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads, workers)
+    out = gpu_decode(cfg, inp, partition_size=part, num_workers=workers, workspace=ws)
+    out32 = gpu_decode(cfg, inp, out_dtype=torch.float32, partition_size=part, num_workers=workers, workspace=ws)
+    torch.cuda.synchronize()
+    ref, kc, vc = oracle_step(cfg, host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8))
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8))
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    beyond = max_err_beyond_rounding(out, ref)
+    log(f"    err={err:.3e} (beyond output rounding {beyond:.3e}) err32={err32:.3e} max|ref|={np.abs(ref).max():.3f}")
+    # the loud heads (std 4) reach |out| ~ 13, where a bf16 half-ulp alone is
+    # 0.03: stored 16-bit outputs are held to the bound beyond their own rounding
+    assert beyond <= TOL_OUT["fp8"]
+    assert err32 <= TOL_F32["fp8"]
+
+
+def test_head_scales_select_their_own_head():
+    """Scaling one kv head's value scale by 2 scales exactly its query group's
+    outputs by 2 (fp32 output; powers of two are exact) and changes no other."""
+    cfg = SMALL["gqa8_f16q"]
+    layout, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)
+    base = gpu_decode(cfg, inp, out_dtype=torch.float32)
+    G = cfg.group_size
+    for h in (0, cfg.num_kv_heads - 1):
+        v2 = inp["v_scale"].clone()
+        v2[h] *= 2.0
+        out = torch.empty_like(base)
+        pa.decode(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                  cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"], v_scale=v2,
+                  partition_size=cfg.partition_size)
+        torch.cuda.synchronize()
+        mine = slice(h * G, (h + 1) * G)
+        assert torch.equal(out[:, mine], 2.0 * base[:, mine])
+        others = torch.ones(cfg.num_heads, dtype=torch.bool)
+        others[mine] = False
+        assert torch.equal(out[:, others], base[:, others])
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_layers_with_head_scales_match_oracle(G):
+    base = scaled(_BASE, num_seqs=6, num_heads=8 * G, num_kv_heads=8, num_blocks=900, max_blocks_per_seq=48,
+                  ctx_hi=1500)
+    lcfg = LayerConfig(f"heads_x3_g{G}", base, 3)
+    from pa_workloads import make_layout
+
+    layout = make_layout(base)
+    inp = make_layer_inputs(lcfg, layout, "cuda")
+    # make_layer_inputs keeps the first layer's scales: give each layer its own row
+    L, Hkv = lcfg.num_layers, base.num_kv_heads
+    ks = torch.stack([inp["k_scale"] * (1.0 + 0.25 * l) for l in range(L)]).contiguous()
+    vs = torch.stack([inp["v_scale"] * (1.0 - 0.125 * l) for l in range(L)]).contiguous()
+    host = host_inputs(inp)
+    # each layer's new rows, written with that layer's scales
+    for l in range(L):
+        pa.cache_write(inp["k_new"][l], inp["v_new"][l], inp["k_cache"][l], inp["v_cache"][l],
+                       inp["slot_mapping"], k_scale=ks[l].contiguous(), v_scale=vs[l].contiguous())
+    out = torch.empty(inp["q"].shape, dtype=torch.float32, device="cuda")
+    pa.decode_layers(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                     base.block_size, base.softmax_scale, Hkv, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    kcs, vcs = [], []
+    for l in range(L):
+        kc, vc = oracle.cache_write(host["k_new"][l], host["v_new"][l], host["k_cache"][l], host["v_cache"][l],
+                                    host["slot_mapping"], ks[l].cpu(), vs[l].cpu())
+        kcs.append(kc)
+        vcs.append(vc)
+    assert torch.equal(_bytes(inp["k_cache"]), torch.stack(kcs).view(torch.uint8))
+    assert torch.equal(_bytes(inp["v_cache"]), torch.stack(vcs).view(torch.uint8))
+    ref = oracle.paged_decode_layers(host["q"], torch.stack(kcs), torch.stack(vcs), host["block_tables"],
+                                     host["context_lens"], base.softmax_scale, Hkv, ks.cpu(), vs.cpu(),
+                                     nthreads=NTHREADS)
+    err = max_abs_err(out, ref)
+    log(f"[layers G={G}] err32={err:.3e}")
+    assert err <= TOL_F32["fp8"]
