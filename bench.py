@@ -542,7 +542,7 @@ def bench_layers(args, lcfg, dev) -> dict:
         "tokens_per_s": round(cfg.num_seqs / (ms_per_step * 1e-3), 1),
         "roofline": {"kernel": "decode_layers (paged decode of all layers in one launch)", "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel_ms": round(kernel_ms, 5),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(lcfg.name), "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes_per_launch": step_alg},
         "cpu_baseline": None,
     }
