@@ -309,10 +309,11 @@ def bench_prefill(args, pcfg, dev) -> dict:
     for i in range(nsets):
         inp = make_prefill_inputs(pcfg, pl, dev, seed_offset=i)
         inp["out"] = torch.zeros_like(inp["q"])  # sets that a short run never reaches stay finite
+        inp["ws"] = pa.new_prefill_workspace(dev)
         sets.append(inp)
     host0 = None
     if not args.no_cpu_baseline:
-        host0 = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in sets[0].items() if k != "out"}
+        host0 = {k: (v.cpu() if torch.is_tensor(v) else v) for k, v in sets[0].items() if k not in ("out", "ws")}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
@@ -322,7 +323,8 @@ def bench_prefill(args, pcfg, dev) -> dict:
 
     def prefill(inp):
         pa.prefill(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, stream=sptr)
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, workspace=inp["ws"],
+                   stream=sptr)
 
     for i in range(args.warmup):
         write(sets[i % nsets])

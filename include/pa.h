@@ -210,16 +210,30 @@ PA_API pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches
  *   v_cache         [num_blocks, block_size, num_kv_heads, head_dim], q's dtype.
  *   block_tables    [num_seqs, max_blocks_per_seq] PA_I32, as in pa_decode.
  *   block_size      16 or 32; num_kv_heads divides num_heads; head_dim 64 or 128.
- *   opts            stream only (no workspace; scales, partition_size and
+ *   opts            stream; optional workspace (scales, partition_size and
  *                   num_workers are ignored; flags must be 0).
+ *   opts->workspace NULL, or device memory of pa_prefill_workspace_size()
+ *                   bytes, 256-byte aligned, zero-filled before its first use
+ *                   and left at zero by every call.  With it, steps of few
+ *                   query rows per sequence hand their (tile, kv head) pairs to
+ *                   workgroups as they free up, longest context first; without
+ *                   it the pairs are dealt round-robin.  The results are the
+ *                   same either way, bit for bit.  One workspace serves one
+ *                   call at a time.
  * The contents of query_start_loc are trusted like the block tables: values
  * outside [0, num_tokens] are clamped, never followed out of bounds.
- * Work: one launch; a workgroup per (sequence, kv head, tile of 64 or 128
- * (query row, query head) pairs), streaming the positions its last row sees.
+ * Work: one launch.  Steps averaging more than 32 (query row, query head)
+ * pairs per sequence: a workgroup per (sequence, kv head, tile of 64 or 128
+ * such pairs), streaming the positions its last row sees.  Smaller steps
+ * (speculative verification): one persistent workgroup per compute unit; the
+ * four wavefronts of a workgroup split one tile's keys.
  */
 PA_API pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
                             pa_tensor block_tables, pa_tensor context_lens, pa_tensor query_start_loc,
                             int32_t block_size, float scale, int32_t num_kv_heads, const pa_opts *opts);
+
+/* Bytes of the optional pa_prefill workspace (one pair counter, padded). */
+PA_API size_t pa_prefill_workspace_size(void);
 
 /*
  * pa_cache_write -- scatter new tokens into the paged cache.

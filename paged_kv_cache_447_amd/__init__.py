@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_num_workers.restype = i32
     lib.pa_decode_num_workers.argtypes = [i32]
     lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.pa_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.pa_prefill_workspace_size.argtypes = []
     lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
@@ -265,14 +267,33 @@ def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_
     return out
 
 
+def prefill_workspace_size() -> int:
+    return int(load_library().pa_prefill_workspace_size())
+
+
+def new_prefill_workspace(device):
+    """A zero-filled workspace for pa_prefill (the pair counter of its key-split mode)."""
+    import torch
+
+    return torch.zeros(prefill_workspace_size(), dtype=torch.uint8, device=device)
+
+
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, block_size: int, scale: float,
-            num_kv_heads: int, stream=None):
+            num_kv_heads: int, workspace=None, stream=None):
     """pa_prefill: fill ``out`` [N, H, D] with causal paged attention of the
     query rows of every sequence (rows query_start_loc[s] .. [s+1]-1 are the
-    newest tokens of sequence s); returns ``out``."""
+    newest tokens of sequence s); returns ``out``.
+
+    ``workspace``: a tensor from new_prefill_workspace() (made here, once per
+    call, if None), or False for none (pairs dealt round-robin)."""
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
+    if workspace is None:
+        workspace = new_prefill_workspace(q.device)
     o = PaOpts()
+    if workspace is not False:
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
     o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_prefill(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                         describe(context_lens), describe(query_start_loc), block_size, scale, num_kv_heads,

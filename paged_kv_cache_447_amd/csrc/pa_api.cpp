@@ -161,6 +161,8 @@ extern "C" {
 
 int32_t pa_decode_num_workers(int32_t requested) { return effective_workers(requested); }
 
+size_t pa_prefill_workspace_size(void) { return 256; }
+
 size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads, int64_t head_dim,
                                 int32_t num_workers) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_heads % num_kv_heads) return 0;
@@ -451,6 +453,13 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   const int64_t slots = (N * G + a.tile_cols - 1) / a.tile_cols + S;
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");
   a.tile_slots = (int32_t)slots;
+  if (o.workspace) {  // the key split's pair counter
+    if (o.workspace_bytes < pa_prefill_workspace_size())
+      return fail(PA_ERR_WORKSPACE, "prefill workspace of %zu bytes needed, %zu given", pa_prefill_workspace_size(),
+                  o.workspace_bytes);
+    if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+    a.pair_counter = static_cast<int32_t *>(o.workspace);
+  }
   a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
   a.kv_kind = kv_kind(k_cache.dtype);
   a.out_f32 = out.dtype == PA_F32;

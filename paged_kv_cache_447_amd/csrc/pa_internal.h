@@ -79,6 +79,8 @@ struct PrefillArgs {
   int32_t tile_cols;               // columns per tile
   int32_t key_split;               // 1: the four wavefronts split a tile's keys, 0: its columns
   int32_t persistent_wgs;          // key split: workgroups of the persistent launch (one per CU)
+  int32_t *pair_counter;           // key split: pairs handed out so far (zero between calls), or null:
+                                   // the pairs are then dealt round-robin
   float qk_scale_log2;             // scale * log2(e)
   int32_t kv_kind;                 // KvKind of the caches (= q's)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype

@@ -163,10 +163,13 @@ struct PrefillTile {
   static constexpr int CB = 2 * HB;                   // bytes of a ring slot: K rows, then V rows
   static constexpr int R = kLdsPerWG / CB < 8 ? kLdsPerWG / CB : 8;  // ring slots (shared stream)
   // key split: two private slots per wavefront, reused for the partials' merge
-  static constexpr int kMergeBytes = kWaves * NC * 16 * (D + 2) * 4;
+  // merge buffer: a column's D outputs padded to PD floats, so that the 16
+  // columns of one 16-byte access fall on 16 different bank groups
+  static constexpr int PD = D + 4;
+  static constexpr int kMergeBytes = kWaves * NC * 16 * (PD + 2) * 4;
   static constexpr int kLdsBytes = KSP ? kWaves * 2 * CB : R * CB;
   static_assert(!KSP || kMergeBytes <= kLdsBytes, "the partials fit the ring");
-  static_assert(!KSP || 2 * Slot::NLD < 64, "wait counter range");
+  static_assert(!KSP || 3 * Slot::NLD < 64, "wait counter range");
   static constexpr int LOG2BS = BS == 16 ? 4 : 5;
   static_assert(Slot::NLD % kWaves == 0, "every wavefront loads the same share of a chunk");
   static_assert(Slot::RPI * PER == 8, "a wavefront's share is 8 rows inside one 16-token tile");
@@ -270,14 +273,14 @@ struct PrefillTile {
     }
   }
 
-  __device__ __forceinline__ void compute(int c, const char *ks) {
+  // scores and softmax weights of chunk c from the K rows at ks
+  __device__ __forceinline__ void qk(int c, const char *ks, u32x4 *phi, u32x4 *plo) {
     const int cs = CT * c;
     u32x4 kop[2][KS];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int kb = 0; kb < KS; ++kb) kop[tt][kb] = ld16(ks + koff[kb] + tt * 16 * RB);
-    u32x4 phi[NC], plo[NC];
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
       f32x4 sc[2];
@@ -285,7 +288,15 @@ struct PrefillTile {
       // with the keys split, a wavefront's first chunks may lie past a column's limit
       core[ct].template weights<KSP>(sc, cs, last[ct], a.qk_scale_log2, phi[ct], plo[ct]);
     }
-    accumulate_slot_n<NC>(core, phi, plo, ks + HB, [&](int n) { return voff[n]; });
+  }
+  // output update from the V rows at vs
+  __device__ __forceinline__ void pv(const char *vs, const u32x4 *phi, const u32x4 *plo) {
+    accumulate_slot_n<NC>(core, phi, plo, vs, [&](int n) { return voff[n]; });
+  }
+  __device__ __forceinline__ void compute(int c, const char *ks) {
+    u32x4 phi[NC], plo[NC];
+    qk(c, ks, phi, plo);
+    pv(ks + HB, phi, plo);
   }
 
   __device__ void run() {
@@ -328,46 +339,62 @@ struct PrefillTile {
     b1 = x1 < 0 ? 0 : (x1 >= a.num_blocks ? a.num_blocks - 1 : x1);
   }
 
-  // all of chunk c's K and V rows, by this wavefront alone, into `dst`
-  __device__ __forceinline__ void issue_all(int c, int b0, int b1, char *dst) {
+  // chunk c's K rows (ISV = 0) or V rows (ISV = 1), by this wavefront alone,
+  // into the slot at `dst` (K rows at its start, V rows HB bytes in)
+  template <int ISV>
+  __device__ __forceinline__ void issue_rows(int c, int b0, int b1, char *dst) {
     const int cs = CT * c;
+    const char *base = ISV ? vbase : kbase;
+    const int64_t sb = ISV ? a.v_sb : a.k_sb, st = ISV ? a.v_st : a.k_st;
 #pragma unroll
-    for (int isv = 0; isv < 2; ++isv) {
-      const char *base = isv ? vbase : kbase;
-      const int64_t sb = isv ? a.v_sb : a.k_sb, st = isv ? a.v_st : a.k_st;
-#pragma unroll
-      for (int i = 0; i < Slot::NLD; ++i) {
-        int r, g;
-        Slot::dma_target(isv, i, lane, r, g);
-        const int t = min(cs + r, last_max);
-        const char *bb = base + (int64_t)((Slot::RPI * i) / 16 ? b1 : b0) * sb * 2;  // uniform block base
-        const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
-        __builtin_amdgcn_global_load_lds(gp, lds_addr(dst + isv * HB + 1024 * i), 16, 0, 0);
-      }
+    for (int i = 0; i < Slot::NLD; ++i) {
+      int r, g;
+      Slot::dma_target(ISV, i, lane, r, g);
+      const int t = min(cs + r, last_max);
+      const char *bb = base + (int64_t)((Slot::RPI * i) / 16 ? b1 : b0) * sb * 2;  // uniform block base
+      const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
+      __builtin_amdgcn_global_load_lds(gp, lds_addr(dst + ISV * HB + 1024 * i), 16, 0, 0);
     }
   }
 
+  // The wavefront's chunks are wave, wave + 4, ...; two slots, chunk c and
+  // chunk c + 4 in the other.  As soon as chunk c's scores are done its K rows
+  // take chunk c + 8's, and once its output update is done its V rows do, so
+  // about two chunks are in flight at every wait.  Loads are issued in the
+  // order K(c), V(c), K(c + 4), V(c + 4), K(c + 8), ...; a chunk index past
+  // the end reloads the last rows into a slot nobody reads again, so each wait
+  // for K(c) or V(c) has exactly three halves (3 NLD loads) issued after it.
   __device__ void run_split() {
+    constexpr int NLD = Slot::NLD;
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) core[ct].reset();
     load_q();
     const int nch = last_max / CT + 1;
     char *mine = ring + wave * 2 * CB;
-    // chunks wave, wave + 4, ...: one in flight while the one before it is
-    // computed.  A chunk index past the end reloads the last rows into the
-    // slot nobody reads next, so exactly 2 NLD loads are outstanding behind
-    // the awaited chunk.
     int b0, b1;
     blocks_of(wave, b0, b1);
-    issue_all(wave, b0, b1, mine);
+    issue_rows<0>(wave, b0, b1, mine);
+    issue_rows<1>(wave, b0, b1, mine);
     blocks_of(wave + kWaves, b0, b1);
+    issue_rows<0>(wave + kWaves, b0, b1, mine + CB);
+    issue_rows<1>(wave + kWaves, b0, b1, mine + CB);
+    blocks_of(wave + 2 * kWaves, b0, b1);  // block ids of chunk c + 8
     int k = 0;
     for (int c = wave; c < nch; c += kWaves, ++k) {
-      issue_all(c + kWaves, b0, b1, mine + ((k + 1) & 1) * CB);
-      blocks_of(c + 2 * kWaves, b0, b1);
-      wait_vm<2 * Slot::NLD>();  // chunk c (and the queries before it) has landed
+      char *slot = mine + (k & 1) * CB;
+      wait_vm<3 * NLD>();  // K(c) (and the queries before it) has landed
       __builtin_amdgcn_sched_barrier(0);
-      compute(c, mine + (k & 1) * CB);
+      u32x4 phi[NC], plo[NC];
+      qk(c, slot, phi, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_rows<0>(c + 2 * kWaves, b0, b1, slot);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<3 * NLD>();  // V(c) has landed
+      __builtin_amdgcn_sched_barrier(0);
+      pv(slot + HB, phi, plo);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_rows<1>(c + 2 * kWaves, b0, b1, slot);
+      blocks_of(c + 3 * kWaves, b0, b1);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vm<0>();  // no load may land after the ring is reused or released
@@ -380,12 +407,12 @@ struct PrefillTile {
   // 16-dim tiles n = w, w + 4, ... of every column.
   template <typename OT>
   __device__ void merge_store() {
-    float *pacc = reinterpret_cast<float *>(ring);  // [wave][ct][column][D]
-    float *pml = pacc + kWaves * NC * 16 * D;       // [wave][ct][column][2]
+    float *pacc = reinterpret_cast<float *>(ring);  // [wave][ct][column][PD]
+    float *pml = pacc + kWaves * NC * 16 * PD;      // [wave][ct][column][2]
     __syncthreads();                                // every wavefront is done with the ring
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
-      float *dst = pacc + ((wave * NC + ct) * 16 + c16) * D + 4 * jq;
+      float *dst = pacc + ((wave * NC + ct) * 16 + c16) * PD + 4 * jq;
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
         u32x4 w;
@@ -427,7 +454,7 @@ struct PrefillTile {
         float o[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const u32x4 x = ld16(pacc + ((w * NC + ct) * 16 + c16) * D + 16 * n + 4 * jq);
+          const u32x4 x = ld16(pacc + ((w * NC + ct) * 16 + c16) * PD + 16 * n + 4 * jq);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const uint32_t xi = x[i];
@@ -486,21 +513,41 @@ __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const P
   int seq, tile;
   if constexpr (KSP) {
     // Key split (about one tile per sequence and kv head): persistent
-    // workgroups, one per CU, take the (tile, kv head) pairs round-robin in
-    // the tiles' order, all kv heads of a tile in a row, so that every
-    // workgroup gets a share of the longest contexts first.
-    const int64_t n = (int64_t)(order.ranked ? order.total : a.tile_slots) * a.num_kv_heads;
-    for (int64_t x = blockIdx.x; x < n; x += gridDim.x) {
-      const int t = (int)(x / a.num_kv_heads), kvh = (int)(x - (int64_t)t * a.num_kv_heads);
-      if (!order.find(a, t, lane, seq, tile)) break;  // unranked batches: past the last tile
-      Tile tl(a, lds, lane, wave);
-      if (!tl.setup(seq, tile, kvh)) {
-        if (wave == 0) tl.write_out(true);
+    // workgroups, one per CU, take the (tile, kv head) pairs in the tiles'
+    // order, all kv heads of a tile in a row, longest contexts first.  The
+    // first pairs are dealt one per workgroup; with a pair counter each
+    // workgroup then takes the next pair as it frees up (longest processing
+    // time first), else it takes every gridDim.x-th pair.  Every workgroup's
+    // last take returns a pair past the end, so the takes number exactly n
+    // (the grid never exceeds n) and the one that returns n - 1 is the last:
+    // it resets the counter for the next call.
+    const int n = (order.ranked ? order.total : a.tile_slots) * a.num_kv_heads;
+    __shared__ int next_pair;
+    for (int x = blockIdx.x; x < n;) {
+      const int t = x / a.num_kv_heads, kvh = x - t * a.num_kv_heads;
+      const bool found = order.find(a, t, lane, seq, tile);  // unranked batches: none past the last tile
+      if (!found && a.pair_counter == nullptr) break;      // (with a counter, keep taking to the end)
+      if (found) {
+        Tile tl(a, lds, lane, wave);
+        if (tl.setup(seq, tile, kvh)) {
+          tl.run_split();
+          tl.merge_write();
+        } else if (wave == 0) {
+          tl.write_out(true);
+        }
+      }
+      __syncthreads();  // the merge's reads of the ring are done before the next tile's loads
+      if (a.pair_counter == nullptr) {
+        x += gridDim.x;
         continue;
       }
-      tl.run_split();
-      tl.merge_write();
-      __syncthreads();  // the merge's reads of the ring are done before the next tile's loads
+      if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(a.pair_counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == n - 1) __hip_atomic_store(a.pair_counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next_pair = (int)gridDim.x + old;
+      }
+      __syncthreads();
+      x = next_pair;
     }
   } else {
     // Workgroups are dealt to the 8 XCDs round-robin; number them so that the

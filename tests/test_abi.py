@@ -354,3 +354,14 @@ def test_head_scale_errors(lib):
     p = pa.PaOpts()
     p.k_head_scales = p.v_head_scales = FAKE
     expect(lib, call_prefill(lib, good_prefill(), opts=p), -7, "FP8")
+
+
+def test_prefill_workspace_errors(lib):
+    assert lib.pa_prefill_workspace_size() >= 4
+    p = pa.PaOpts()
+    p.workspace = FAKE
+    p.workspace_bytes = 4  # too small
+    expect(lib, call_prefill(lib, good_prefill(), opts=p), -6, "workspace")
+    p.workspace = FAKE + 16  # misaligned
+    p.workspace_bytes = 1 << 20
+    expect(lib, call_prefill(lib, good_prefill(), opts=p), -6, "aligned")

@@ -232,3 +232,27 @@ def test_prefill_repeats_bit_identically_and_on_a_side_stream():
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("case", ["verify_gqa8", "verify_gqa16_d64_bf16", "verify_gqa4_bs16"])
+def test_pair_hand_out_matches_round_robin_bitwise(case):
+    """Key-split steps: pairs handed out through the workspace counter as
+    workgroups free up give the same bits as pairs dealt round-robin (each
+    pair is computed whole by one workgroup), and every call leaves the
+    counter at zero, over repeated calls on one workspace."""
+    pcfg = CASES[case]
+    cfg = pcfg.base
+    pl, inp = setup(pcfg)
+    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"])
+    ws = pa.new_prefill_workspace(inp["q"].device)
+    outs = []
+    for w in (False, ws, ws, ws):
+        out = torch.empty_like(inp["q"])
+        pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, workspace=w)
+        torch.cuda.synchronize()
+        if w is not False:
+            assert int(ws.view(torch.int32)[0]) == 0, "the pair counter is left at zero"
+        outs.append(out)
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
