@@ -319,12 +319,13 @@ def bench_prefill(args, pcfg, dev) -> dict:
     sptr = stream.cuda_stream
 
     def write(inp):
-        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"], stream=sptr)
+        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=sptr)
 
     def prefill(inp):
         pa.prefill(inp["out"], inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, workspace=inp["ws"],
-                   stream=sptr)
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"], workspace=inp["ws"], stream=sptr)
 
     for i in range(args.warmup):
         write(sets[i % nsets])
@@ -418,7 +419,7 @@ def bench_prefill(args, pcfg, dev) -> dict:
         cores = len(os.sched_getaffinity(0))
         nthreads = max(1, min(cores, 64))
         kc, vc = oracle.cache_write(host0["k_new"], host0["v_new"], host0["k_cache"], host0["v_cache"],
-                                    host0["slot_mapping"], inplace=True)
+                                    host0["slot_mapping"], host0["k_scale"], host0["v_scale"], inplace=True)
         # the sample: the step's first sequence (all of its query rows), repeated
         qsl = host0["query_start_loc"]
         n0 = int(qsl[1])
@@ -427,7 +428,8 @@ def bench_prefill(args, pcfg, dev) -> dict:
         reps, t_start = 0, time.perf_counter()
         while True:
             oracle.paged_prefill(q0, kc, vc, host0["block_tables"][:1], host0["context_lens"][:1],
-                                 qsl[:2].contiguous(), cfg.softmax_scale, cfg.num_kv_heads, nthreads=nthreads)
+                                 qsl[:2].contiguous(), cfg.softmax_scale, cfg.num_kv_heads, host0["k_scale"],
+                                 host0["v_scale"], nthreads=nthreads)
             reps += 1
             el = time.perf_counter() - t_start
             if el >= args.cpu_seconds or reps >= 1000:

@@ -66,6 +66,27 @@ PREFILL_CONFIGS: Dict[str, PrefillConfig] = {
         ),
         q_len=4,
     ),
+    # The same two steps over fp8 e4m3fn caches with per-tensor scales (the fp8
+    # KV cache of page "大模型推理KV Cache内存管理与PagedAttention分页显存实战"),
+    # f16 queries: half the cache bytes of the 16-bit steps.
+    "prefill_7b_fp8": PrefillConfig(
+        name="prefill_7b_fp8",
+        base=DecodeConfig(
+            name="prefill_7b_fp8", seed=14, num_seqs=8, num_heads=32, num_kv_heads=32, head_dim=128,
+            block_size=16, num_blocks=5000, max_blocks_per_seq=256, kv_dtype="fp8", q_dtype="f16",
+            ctx_kind="uniform", ctx_lo=1024, ctx_hi=4096, allocator="shuffled",
+        ),
+        q_len=512,
+    ),
+    "verify_gqa70b_fp8": PrefillConfig(
+        name="verify_gqa70b_fp8",
+        base=DecodeConfig(
+            name="verify_gqa70b_fp8", seed=15, num_seqs=128, num_heads=64, num_kv_heads=8, head_dim=128,
+            block_size=32, num_blocks=40000, max_blocks_per_seq=256, kv_dtype="fp8", q_dtype="f16",
+            ctx_kind="lognormal", ctx_median=1024.0, ctx_sigma=1.0, ctx_lo=4, ctx_hi=8192, allocator="churn",
+        ),
+        q_len=4,
+    ),
 }
 
 

@@ -375,8 +375,9 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   if ((st = check_tensor(query_start_loc, "query_start_loc", 1, false))) return st;
 
   if (q.dtype != PA_F16 && q.dtype != PA_BF16) return fail(PA_ERR_DTYPE, "q: dtype must be F16 or BF16");
-  if (k_cache.dtype != q.dtype || v_cache.dtype != q.dtype)
-    return fail(PA_ERR_DTYPE, "k_cache and v_cache must have q's dtype");
+  if (k_cache.dtype != v_cache.dtype) return fail(PA_ERR_DTYPE, "k_cache and v_cache dtypes differ");
+  if (k_cache.dtype != q.dtype && k_cache.dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "k_cache and v_cache must have q's dtype or FP8_E4M3");
   if (out.dtype != q.dtype && out.dtype != PA_F32) return fail(PA_ERR_DTYPE, "out: dtype must be q's dtype or F32");
   if (block_tables.dtype != PA_I32) return fail(PA_ERR_DTYPE, "block_tables: dtype must be I32");
   if (context_lens.dtype != PA_I32) return fail(PA_ERR_DTYPE, "context_lens: dtype must be I32");
@@ -406,7 +407,11 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
-  if (o.k_head_scales || o.v_head_scales) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  if (o.k_head_scales || o.v_head_scales) return fail(PA_ERR_ARG, "pa_prefill takes per-tensor scales only");
+  float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
+  if (k_cache.dtype != PA_FP8_E4M3) ks = vs = 1.0f;
+  if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
+    return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
   const int64_t W = block_tables.shape[1];
   const int64_t G = num_kv_heads > 0 ? H / num_kv_heads : 0;
   if (S > INT32_MAX - 1 || N * G > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many sequences or query rows");
@@ -460,8 +465,10 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
     a.pair_counter = static_cast<int32_t *>(o.workspace);
   }
-  a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)ks);
+  a.v_scale = vs;
   a.kv_kind = kv_kind(k_cache.dtype);
+  a.q_kind = kv_kind(q.dtype);
   a.out_f32 = out.dtype == PA_F32;
 
   hipError_t e = pa::launch_prefill(a, static_cast<hipStream_t>(o.stream));

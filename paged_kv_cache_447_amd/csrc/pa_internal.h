@@ -81,8 +81,10 @@ struct PrefillArgs {
   int32_t persistent_wgs;          // key split: workgroups of the persistent launch (one per CU)
   int32_t *pair_counter;           // key split: pairs handed out so far (zero between calls), or null:
                                    // the pairs are then dealt round-robin
-  float qk_scale_log2;             // scale * log2(e)
-  int32_t kv_kind;                 // KvKind of the caches (= q's)
+  float qk_scale_log2;             // scale * log2(e) (* k_scale for fp8)
+  float v_scale;                   // 1, or the fp8 value-cache scale
+  int32_t kv_kind;                 // KvKind of the caches: q's, or KV_FP8
+  int32_t q_kind;                  // KvKind of q (and of the matrix-core operands)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype
 };
 

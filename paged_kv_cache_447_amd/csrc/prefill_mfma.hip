@@ -151,9 +151,12 @@ struct TileOrder {
 // chunk, which it loads alone into a private two-slot ring; the four partial
 // softmax states are merged through LDS at the end.  Otherwise the four
 // wavefronts compute different columns over every chunk of one shared stream.
-template <typename MT, int D, int BS, int NC, bool KSP>
+template <typename MT, typename KVT, int D, int BS, int NC, bool KSP>
 struct PrefillTile {
   using Slot = RowSlot<D>;
+  static constexpr bool kFp8 = __is_same(KVT, fp8_t);
+  static constexpr int EB = kFp8 ? 1 : 2;             // bytes per cache element
+  static constexpr int PPR = D * EB / 16;             // 16-byte pieces per cache row
   using Core = MfmaCore<MT, D>;
   static constexpr int KS = D / 32;
   static constexpr int NT = D / 16;
@@ -214,8 +217,8 @@ struct PrefillTile {
     c_hi = min(c_lo + a.tile_cols, nq * a.group);
     last_max = pos0 + (c_hi - 1) / a.group;
     bt = as_const(a.block_tables) + (int64_t)s * a.bt_ss;
-    kbase = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * 2;
-    vbase = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * 2;
+    kbase = reinterpret_cast<const char *>(a.k_cache) + (int64_t)kvh * a.k_sh * EB;
+    vbase = reinterpret_cast<const char *>(a.v_cache) + (int64_t)kvh * a.v_sh * EB;
     const int w_lo = KSP ? c_lo : c_lo + 16 * NC * wave;
     wlast = w_lo < c_hi ? pos0 + (min(w_lo + 16 * NC, c_hi) - 1) / a.group : -1;
 #pragma unroll
@@ -325,6 +328,113 @@ struct PrefillTile {
       islot = islot + 1 == R ? 0 : islot + 1;
     }
     wait_vm<0>();  // no load may land after the workgroup's LDS is released
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].finish();
+  }
+
+  // ---- fp8 caches --------------------------------------------------------
+  // Rows come through registers: each 16-byte piece (16 codes) is decoded
+  // exactly into two 16-byte granules of the operand type and stored where
+  // the 16-bit kernel's DMA would have put them, so the operand reads and the
+  // arithmetic are the same.
+
+  // the pieces of rows r0 .. r0 + ROWS - 1 of chunk c, K then V, lane by
+  // lane: FP8N<ROWS> pieces per lane; rows of 16-token tile 0 read block b0,
+  // those of tile 1 block b1 (rows past last_max read its row)
+  template <int ROWS>
+  static constexpr int fp8n() { return 2 * ROWS * PPR / 64; }
+  template <int ROWS>
+  __device__ __forceinline__ void load_fp8(int c, int r0, int b0, int b1, u32x4 *dst) const {
+    static_assert((2 * ROWS * PPR) % 64 == 0, "whole pieces per lane");
+#pragma unroll
+    for (int k = 0; k < fp8n<ROWS>(); ++k) {
+      const int idx = lane + 64 * k;
+      const int isv = idx / (ROWS * PPR), rem = idx - isv * (ROWS * PPR);
+      const int r = r0 + rem / PPR, piece = rem % PPR;
+      const int t = min(CT * c + r, last_max);
+      const char *base = isv ? vbase : kbase;
+      const int64_t sb = isv ? a.v_sb : a.k_sb, st = isv ? a.v_st : a.k_st;
+      const int blk = (r & 16) ? b1 : b0;
+      const char *gp = base + (int64_t)blk * sb + (uint32_t)((t & (BS - 1)) * (uint32_t)st + 16 * piece);
+      // column mode: the tiles of one kv head read the same rows, from L2
+      // after the first; the key split reads each row once
+      dst[k] = KSP ? ld16_stream(gp) : ld16(gp);
+    }
+  }
+  template <int ROWS>
+  __device__ __forceinline__ void stage_fp8(int r0, char *slot, const u32x4 *src) const {
+#pragma unroll
+    for (int k = 0; k < fp8n<ROWS>(); ++k) {
+      const int idx = lane + 64 * k;
+      const int isv = idx / (ROWS * PPR), rem = idx - isv * (ROWS * PPR);
+      const int r = r0 + rem / PPR, piece = rem % PPR;
+      u32x4 o[2];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // codes 4w .. 4w+3 become operand elements 4w .. 4w+3 (exact conversions)
+        const uint32_t lo = __is_same(MT, f16_t) ? fp8x2_to_f16x2<false>(src[k][w]) : fp8x2_to_bf16x2<false>(src[k][w]);
+        const uint32_t hi = __is_same(MT, f16_t) ? fp8x2_to_f16x2<true>(src[k][w]) : fp8x2_to_bf16x2<true>(src[k][w]);
+        o[w >> 1][2 * (w & 1)] = lo;
+        o[w >> 1][2 * (w & 1) + 1] = hi;
+      }
+      char *dst = slot + isv * HB;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) st16(dst + 16 * Slot::phys(isv, r, 2 * piece + h), o[h]);
+    }
+  }
+
+  // Column mode, fp8: every wavefront stages its 8 rows of chunk c into the
+  // shared ring, a workgroup barrier publishes the chunk (and tells that every
+  // wavefront is done with chunk c - 1, so slot c - 1 + R is free), then the
+  // wavefront issues its rows of chunk c + 1 and computes chunk c.
+  __device__ void run_fp8() {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].reset();
+    load_q();
+    const int nch = last_max / CT + 1;
+    u32x4 rows[fp8n<8>()];
+    int blk = block_of(0);
+    load_fp8<8>(0, 8 * wave, blk, blk, rows);
+    int slot = 0;
+    for (int c = 0; c < nch; ++c) {
+      stage_fp8<8>(8 * wave, ring + slot * CB, rows);
+      __syncthreads();  // chunk c staged by every wavefront
+      if (c + 1 < nch) {
+        blk = block_of(c + 1);
+        load_fp8<8>(c + 1, 8 * wave, blk, blk, rows);
+      }
+      if (CT * c <= wlast) compute(c, ring + slot * CB);
+      slot = slot + 1 == R ? 0 : slot + 1;
+    }
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].finish();
+  }
+
+  // Key split, fp8: the wavefront's chunks wave, wave + 4, ... alternate
+  // between its two private slots; the next one is loaded into registers
+  // while the current one is computed.
+  __device__ void run_split_fp8() {
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) core[ct].reset();
+    load_q();
+    const int nch = last_max / CT + 1;
+    char *mine = ring + wave * 2 * CB;
+    u32x4 rows[fp8n<32>()];
+    int b0, b1;
+    blocks_of(wave, b0, b1);
+    load_fp8<32>(wave, 0, b0, b1, rows);
+    int k = 0;
+    for (int c = wave; c < nch; c += kWaves, ++k) {
+      char *slot = mine + (k & 1) * CB;
+      stage_fp8<32>(0, slot, rows);
+      blocks_of(c + kWaves, b0, b1);
+      load_fp8<32>(c + kWaves, 0, b0, b1, rows);  // past the end: the last rows again, unused
+      // the transposed reads are inline assembly: keep them after the stores
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      compute(c, slot);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) core[ct].finish();
   }
@@ -447,7 +557,7 @@ struct PrefillTile {
         L += f[w] * pml[((w * NC + ct) * 16 + c16) * 2 + 1];
       }
       const bool z = last[ct] < 0;
-      const float inv = 1.0f / L;
+      const float inv = a.v_scale / L;
       const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
 #pragma unroll
       for (int n = wave; n < NT; n += kWaves) {
@@ -477,7 +587,7 @@ struct PrefillTile {
 
   template <typename OT>
   __device__ __forceinline__ void store(int ct, bool zero) const {
-    const float inv = 1.0f / core[ct].l;
+    const float inv = a.v_scale / core[ct].l;
     const bool z = zero || last[ct] < 0;
     const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
 #pragma unroll
@@ -502,9 +612,9 @@ struct PrefillTile {
   }
 };
 
-template <typename MT, int D, int BS, int NC, bool KSP>
+template <typename MT, typename KVT, int D, int BS, int NC, bool KSP>
 __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const PrefillArgs a) {
-  typedef PrefillTile<MT, D, BS, NC, KSP> Tile;
+  typedef PrefillTile<MT, KVT, D, BS, NC, KSP> Tile;
   __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -530,7 +640,10 @@ __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const P
       if (found) {
         Tile tl(a, lds, lane, wave);
         if (tl.setup(seq, tile, kvh)) {
-          tl.run_split();
+          if constexpr (Tile::kFp8)
+            tl.run_split_fp8();
+          else
+            tl.run_split();
           tl.merge_write();
         } else if (wave == 0) {
           tl.write_out(true);
@@ -562,40 +675,43 @@ __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const P
       tl.write_out(true);
       return;
     }
-    tl.run();
+    if constexpr (Tile::kFp8)
+      tl.run_fp8();
+    else
+      tl.run();
     tl.write_out(false);
   }
 }
 
-template <typename MT, int D, int BS>
+template <typename MT, typename KVT, int D, int BS>
 hipError_t launch_nc(const PrefillArgs &a, hipStream_t stream) {
   const int64_t n = (int64_t)a.tile_slots * a.num_kv_heads;
   const dim3 grid((unsigned)(a.key_split ? min((int64_t)a.persistent_wgs, n) : (n + 7) / 8 * 8)),
       block(64 * kWaves);
   if (a.key_split) {
     if (a.tile_cols == 32)
-      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, true>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, true>), grid, block, 0, stream, a);
   } else {
     if (a.tile_cols == 32 * kWaves)
-      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 2, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, false>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_mfma<MT, D, BS, 1, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <typename MT, int D>
+template <typename MT, typename KVT, int D>
 hipError_t launch_bs(const PrefillArgs &a, hipStream_t stream) {
-  return a.block_size == 16 ? launch_nc<MT, D, 16>(a, stream) : launch_nc<MT, D, 32>(a, stream);
+  return a.block_size == 16 ? launch_nc<MT, KVT, D, 16>(a, stream) : launch_nc<MT, KVT, D, 32>(a, stream);
 }
 
-template <typename MT>
+template <typename MT, typename KVT>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return launch_bs<MT, 64>(a, stream);
-    case 128: return launch_bs<MT, 128>(a, stream);
+    case 64: return launch_bs<MT, KVT, 64>(a, stream);
+    case 128: return launch_bs<MT, KVT, 128>(a, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -603,7 +719,7 @@ hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
 }  // namespace
 
 bool prefill_supported(int kv_kind, int head_dim) {
-  return (kv_kind == KV_F16 || kv_kind == KV_BF16) && (head_dim == 64 || head_dim == 128);
+  return (kv_kind == KV_F16 || kv_kind == KV_BF16 || kv_kind == KV_FP8) && (head_dim == 64 || head_dim == 128);
 }
 
 // Tile shape.  Steps that average at most 32 columns per sequence (a few
@@ -622,8 +738,12 @@ void prefill_plan(int64_t num_rows, int64_t num_seqs, int group, int &tile_cols,
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   switch (a.kv_kind) {
-    case KV_F16: return launch_d<f16_t>(a, stream);
-    case KV_BF16: return launch_d<bf16_t>(a, stream);
+    case KV_F16: return launch_d<f16_t, f16_t>(a, stream);
+    case KV_BF16: return launch_d<bf16_t, bf16_t>(a, stream);
+    case KV_FP8:
+      if (a.q_kind == KV_F16) return launch_d<f16_t, fp8_t>(a, stream);
+      if (a.q_kind == KV_BF16) return launch_d<bf16_t, fp8_t>(a, stream);
+      break;
   }
   return hipErrorInvalidValue;
 }

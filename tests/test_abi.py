@@ -239,7 +239,7 @@ def call_prefill(lib, args, bs=16, scale=0.1, Hkv=2, opts=None):
 
 def test_prefill_errors(lib):
     expect(lib, call_prefill(lib, good_prefill(q=pa.PA_F32, kv=pa.PA_F32)), -2, "q")
-    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3)), -2)
+    expect(lib, call_prefill(lib, good_prefill(q=pa.PA_F32, kv=pa.PA_FP8_E4M3)), -2, "q")  # fp8 takes 16-bit q
     expect(lib, call_prefill(lib, good_prefill(q=pa.PA_BF16, kv=pa.PA_F16)), -2)
     expect(lib, call_prefill(lib, good_prefill(out=pa.PA_BF16)), -2, "out")
     a = good_prefill()
@@ -353,7 +353,10 @@ def test_head_scale_errors(lib):
     expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), w), -7, "exclude")
     p = pa.PaOpts()
     p.k_head_scales = p.v_head_scales = FAKE
-    expect(lib, call_prefill(lib, good_prefill(), opts=p), -7, "FP8")
+    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -7, "per-tensor")
+    p = pa.PaOpts()
+    p.k_scale = float("inf")
+    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -7, "scale")
 
 
 def test_prefill_workspace_errors(lib):

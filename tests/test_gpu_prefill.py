@@ -65,6 +65,30 @@ CASES = {
                        scaled(get_config("llama7b"), num_seqs=4, num_heads=6, num_kv_heads=6, num_blocks=300,
                               max_blocks_per_seq=40, ctx_kind="fixed", ctx_fixed=(63, 64, 65, 600)),
                        (63, 64, 65, 129)),
+    # fp8 e4m3fn caches (per-tensor scales), rows decoded into the query's type on the way into LDS:
+    # column mode, MHA, f16 q, block 32 ...
+    "fp8_mha_bs32": P("fp8_mha_bs32",
+                      scaled(get_config("fp8_long"), num_seqs=3, num_heads=4, num_kv_heads=4, block_size=32,
+                             num_blocks=200, max_blocks_per_seq=40, ctx_kind="fixed", ctx_fixed=(300, 700, 1000),
+                             partition_size=0),
+                      (300, 290, 333)),
+    # ... column mode, G = 4, head_dim 64, bf16 q, block 16 ...
+    "fp8_gqa4_d64_bf16q": P("fp8_gqa4_d64_bf16q",
+                            scaled(get_config("fp8_long"), num_seqs=4, num_heads=16, num_kv_heads=4, head_dim=64,
+                                   q_dtype="bf16", num_blocks=300, max_blocks_per_seq=64, ctx_kind="fixed",
+                                   ctx_fixed=(5, 100, 600, 1000), partition_size=0),
+                            (5, 64, 130, 200)),
+    # ... key split: 4 draft tokens, G = 8, block 32 ...
+    "fp8_verify_gqa8": P("fp8_verify_gqa8",
+                         scaled(get_config("gqa70b"), kv_dtype="fp8", num_seqs=12, num_blocks=2000,
+                                max_blocks_per_seq=64, ctx_lo=4, ctx_hi=2048), 4),
+    # ... key split, G = 16, head_dim 64, bf16 q, block 16, 2 draft tokens
+    "fp8_verify_gqa16_d64_bf16q": P("fp8_verify_gqa16_d64_bf16q",
+                                    scaled(get_config("gqa70b"), kv_dtype="fp8", q_dtype="bf16", num_seqs=7,
+                                           num_heads=32, num_kv_heads=2, head_dim=64, block_size=16,
+                                           num_blocks=900, max_blocks_per_seq=128, ctx_kind="fixed",
+                                           ctx_fixed=(2, 3, 33, 200, 1024, 1500, 2047), allocator="shuffled"),
+                                    2),
 }
 
 
@@ -76,10 +100,12 @@ def setup(pcfg, device="cuda"):
 
 def gpu_step(pcfg, inp, out_dtype=None, stream=None):
     cfg = pcfg.base
-    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"])
+    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     out = torch.empty(inp["q"].shape, dtype=out_dtype or inp["q"].dtype, device=inp["q"].device)
     pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, stream=stream)
+               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+               k_scale=inp["k_scale"], v_scale=inp["v_scale"], stream=stream)
     return out
 
 
@@ -87,13 +113,14 @@ def gpu_prefill(pcfg, inp, out_dtype=None):
     cfg = pcfg.base
     out = torch.empty(inp["q"].shape, dtype=out_dtype or inp["q"].dtype, device=inp["q"].device)
     pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads)
+               inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+               k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     return out
 
 
 def oracle_write(host):
     return oracle.cache_write(host["k_new"], host["v_new"], host["k_cache"], host["v_cache"], host["slot_mapping"],
-                              inplace=True)
+                              host["k_scale"], host["v_scale"], inplace=True)
 
 
 def _bytes(t):
@@ -114,7 +141,8 @@ def test_small_prefill_matches_oracle(case):
     assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8))
     assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8))
     ref = oracle.paged_prefill(host["q"], kc, vc, host["block_tables"], host["context_lens"],
-                               host["query_start_loc"], cfg.softmax_scale, cfg.num_kv_heads, nthreads=NTHREADS)
+                               host["query_start_loc"], cfg.softmax_scale, cfg.num_kv_heads, host["k_scale"],
+                               host["v_scale"], nthreads=NTHREADS)
     raw, err, err32 = max_abs_err(out, ref), max_err_beyond_rounding(out, ref), max_abs_err(out32, ref)
     log(f"    rows={out.shape[0]} err={raw:.3e} (beyond output rounding {err:.3e}) err32={err32:.3e}")
     assert err <= TOL_OUT[cfg.kv_dtype]
@@ -142,10 +170,11 @@ def oracle_rows(pcfg, host, kc, vc, picks):
     q = host["q"][rows].contiguous()
     bt = host["block_tables"][seqs].contiguous()
     lens = torch.tensor([p + 1 for _, _, p in picks], dtype=torch.int32)
-    return oracle.paged_decode(q, kc, vc, bt, lens, cfg.softmax_scale, cfg.num_kv_heads, nthreads=NTHREADS)
+    return oracle.paged_decode(q, kc, vc, bt, lens, cfg.softmax_scale, cfg.num_kv_heads, host["k_scale"],
+                               host["v_scale"], nthreads=NTHREADS)
 
 
-@pytest.mark.parametrize("name", ["prefill_7b", "verify_gqa70b"])
+@pytest.mark.parametrize("name", ["prefill_7b", "verify_gqa70b", "prefill_7b_fp8", "verify_gqa70b_fp8"])
 def test_full_size_prefill_sampled_rows(name):
     """Full-size workloads in the launch configuration the benchmark times:
     every output finite, and rows at tile edges of every sequence equal to the
@@ -234,7 +263,7 @@ def test_prefill_repeats_bit_identically_and_on_a_side_stream():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
-@pytest.mark.parametrize("case", ["verify_gqa8", "verify_gqa16_d64_bf16", "verify_gqa4_bs16"])
+@pytest.mark.parametrize("case", ["verify_gqa8", "verify_gqa16_d64_bf16", "verify_gqa4_bs16", "fp8_verify_gqa8"])
 def test_pair_hand_out_matches_round_robin_bitwise(case):
     """Key-split steps: pairs handed out through the workspace counter as
     workgroups free up give the same bits as pairs dealt round-robin (each
@@ -243,13 +272,15 @@ def test_pair_hand_out_matches_round_robin_bitwise(case):
     pcfg = CASES[case]
     cfg = pcfg.base
     pl, inp = setup(pcfg)
-    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"])
+    pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     ws = pa.new_prefill_workspace(inp["q"].device)
     outs = []
     for w in (False, ws, ws, ws):
         out = torch.empty_like(inp["q"])
         pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
-                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, workspace=w)
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"], workspace=w)
         torch.cuda.synchronize()
         if w is not False:
             assert int(ws.view(torch.int32)[0]) == 0, "the pair counter is left at zero"
