@@ -65,6 +65,17 @@ CASES = {
                        scaled(get_config("llama7b"), num_seqs=4, num_heads=6, num_kv_heads=6, num_blocks=300,
                               max_blocks_per_seq=40, ctx_kind="fixed", ctx_fixed=(63, 64, 65, 600)),
                        (63, 64, 65, 129)),
+    # wide prompt chunks (1600 columns per sequence, 128-column tiles): G = 8 ...
+    "gqa8_wide256": P("gqa8_wide256",
+                      scaled(get_config("gqa70b"), num_seqs=2, num_blocks=200, max_blocks_per_seq=40,
+                             ctx_kind="fixed", ctx_fixed=(300, 800), allocator="shuffled"),
+                      (200, 200)),
+    # ... and over an fp8 cache, head_dim 64, bf16 q, block 16
+    "fp8_gqa8_d64_wide256": P("fp8_gqa8_d64_wide256",
+                              scaled(get_config("gqa70b"), kv_dtype="fp8", q_dtype="bf16", head_dim=64,
+                                     block_size=16, num_seqs=2, num_blocks=200, max_blocks_per_seq=64,
+                                     ctx_kind="fixed", ctx_fixed=(257, 900), allocator="shuffled"),
+                              (257, 140)),
     # fp8 e4m3fn caches (per-tensor scales), rows decoded into the query's type on the way into LDS:
     # column mode, MHA, f16 q, block 32 ...
     "fp8_mha_bs32": P("fp8_mha_bs32",
