@@ -62,7 +62,8 @@ def _load():
             lib.oracle_paged_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp] + [i64] * 7 + [dbl] * 3 + \
                 [vp, vp, i32]
             lib.oracle_paged_prefill.restype = i32
-            lib.oracle_paged_prefill.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp] + [i64] * 7 + [dbl] * 3 + [i32]
+            lib.oracle_paged_prefill.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp] + [i64] * 7 + [dbl] * 3 + \
+                [vp, vp, i32]
             lib.oracle_cache_write.restype = i32
             lib.oracle_cache_write.argtypes = [vp, vp, i32, vp, vp, i32, vp] + [i64] * 5 + [ctypes.c_float] * 2 + \
                 [vp, vp]
@@ -173,7 +174,7 @@ def paged_decode_layers(q, k_caches, v_caches, block_tables, context_lens, scale
 
 
 def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
-                  num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, nthreads: int = 1) -> np.ndarray:
+                  num_kv_heads: int, k_scale=1.0, v_scale=1.0, nthreads: int = 1) -> np.ndarray:
     """Reference prefill (causal, the query rows of sequence s being its newest
     query_start_loc[s+1] - query_start_loc[s] tokens); returns float64
     [num_query_rows, num_heads, head_dim]."""
@@ -194,10 +195,12 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_l
     if qsl.shape[0] != S + 1 or int(qsl[-1]) != N:
         raise ValueError("query_start_loc must have num_seqs + 1 entries ending at the query row count")
     W = bt.shape[1] if bt.dim() == 2 else 0
+    ks, vs, kh, vh = _scales(k_scale, v_scale, Hkv, np.float64)
     out = np.empty((N, H, D), dtype=np.float64)
     rc = lib.oracle_paged_prefill(out.ctypes.data, q.data_ptr(), _code(q), k_cache.data_ptr(), v_cache.data_ptr(),
                                   _code(k_cache), bt.data_ptr(), cl.data_ptr(), qsl.data_ptr(), S, H, Hkv, D, NB,
-                                  bs, W, float(scale), float(k_scale), float(v_scale), int(nthreads))
+                                  bs, W, float(scale), ks, vs, None if kh is None else kh.ctypes.data,
+                                  None if vh is None else vh.ctypes.data, int(nthreads))
     if rc != 0:
         raise OracleError(f"oracle_paged_prefill: {STATUS.get(rc, rc)}")
     return out

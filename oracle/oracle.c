@@ -325,6 +325,7 @@ typedef struct {
   const int32_t *block_tables, *context_lens, *query_start_loc;
   int64_t num_seqs, num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks;
   double scale, k_scale, v_scale;
+  const double *k_heads, *v_heads; /* fp8: one scale per kv head instead of k_scale / v_scale, or NULL */
   int64_t next_item;
   pthread_mutex_t lock;
   int status;
@@ -342,8 +343,11 @@ static int prefill_item(prefill_job *J, int64_t seq, int64_t kvh, double *Kc, do
   if (L < 0 || nq < 0 || nq > L) return ORC_BAD_ARG;
   if (nq == 0) return ORC_OK;
   if ((L + bs - 1) / bs > J->max_blocks) return ORC_CTX_TOO_LONG;
-  const double ks = (J->kv_dtype == ORC_FP8) ? J->k_scale : 1.0;
-  const double vs = (J->kv_dtype == ORC_FP8) ? J->v_scale : 1.0;
+  double ks = 1.0, vs = 1.0;
+  if (J->kv_dtype == ORC_FP8) {
+    ks = J->k_heads ? J->k_heads[kvh] : J->k_scale;
+    vs = J->v_heads ? J->v_heads[kvh] : J->v_scale;
+  }
   for (int64_t t = 0; t < L; ++t) {
     const int64_t blk = J->block_tables[seq * J->max_blocks + t / bs];
     if (blk < 0 || blk >= J->num_blocks) return ORC_BAD_BLOCK;
@@ -414,7 +418,8 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
                          int kv_dtype, const int32_t *block_tables, const int32_t *context_lens,
                          const int32_t *query_start_loc, int64_t num_seqs, int64_t num_heads,
                          int64_t num_kv_heads, int64_t head_dim, int64_t num_blocks, int64_t block_size,
-                         int64_t max_blocks_per_seq, double scale, double k_scale, double v_scale, int nthreads) {
+                         int64_t max_blocks_per_seq, double scale, double k_scale, double v_scale,
+                         const double *k_head_scale, const double *v_head_scale, int nthreads) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc) return ORC_BAD_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0)
@@ -444,6 +449,9 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
   J.scale = scale;
   J.k_scale = k_scale;
   J.v_scale = v_scale;
+  if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
+  J.k_heads = k_head_scale;
+  J.v_heads = v_head_scale;
   J.status = ORC_OK;
   pthread_mutex_init(&J.lock, NULL);
   if (nthreads < 1) nthreads = 1;

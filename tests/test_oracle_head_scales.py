@@ -145,3 +145,49 @@ def test_head_scale_errors():
     k = torch.zeros((1, Hkv, 64), dtype=torch.float16)
     with pytest.raises(ValueError):
         oracle.cache_write(k, k, kc, vc, torch.tensor([0]), k_sc, v_sc[:2])
+
+
+def _prefill_setup(G, seed):
+    q_unused, rows, kc, vc, bt, ctx, k_sc, v_sc, Hkv = _setup(G, seed=seed)
+    g = torch.Generator().manual_seed(seed + 100)
+    lens = [int(x) for x in ctx]
+    n = [min(L, r) for L, r in zip(lens, (1, 5, 16, 3, 20, 40))]
+    qsl = torch.tensor([0] + list(np.cumsum(n)), dtype=torch.int32)
+    q = torch.randn((int(qsl[-1]), Hkv * G, 64), generator=g).to(torch.float16)
+    return q, rows, kc, vc, bt, ctx, qsl, n, k_sc, v_sc, Hkv
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_prefill_with_head_scales_is_textbook_causal_attention(G):
+    """Identity tables: query row j of a sequence with n rows and context L
+    attends to positions 0 .. L - n + j of K, V decoded by torch's fp8 cast,
+    each kv head times its own scale."""
+    q, rows, kc, vc, bt, ctx, qsl, n, k_sc, v_sc, Hkv = _prefill_setup(G, 21)
+    got = oracle.paged_prefill(q, kc, vc, bt, ctx, qsl, SM_SCALE, Hkv, k_sc, v_sc)
+    ks = k_sc.double().numpy()[None, :, None]
+    vs = v_sc.double().numpy()[None, :, None]
+    for i, (K, V) in enumerate(rows):
+        L = K.shape[0]
+        for j in range(n[i]):
+            r = int(qsl[i]) + j
+            p = L - n[i] + j
+            want = attention(to_f64(q[r]), to_f64(K[: p + 1]) * ks, to_f64(V[: p + 1]) * vs, SM_SCALE)
+            np.testing.assert_allclose(got[r], want, rtol=0, atol=1e-12)
+
+
+def test_prefill_rows_are_head_scaled_decodes_bitwise():
+    """Each prefill row equals the per-head decode oracle over the context cut
+    after its position, bit for bit; equal per-head scales equal the
+    per-tensor prefill bit for bit."""
+    q, rows, kc, vc, bt, ctx, qsl, n, k_sc, v_sc, Hkv = _prefill_setup(2, 22)
+    got = oracle.paged_prefill(q, kc, vc, bt, ctx, qsl, SM_SCALE, Hkv, k_sc, v_sc)
+    for i in range(len(n)):
+        for j in range(n[i]):
+            r = int(qsl[i]) + j
+            cut = torch.tensor([int(ctx[i]) - n[i] + j + 1], dtype=torch.int32)
+            dec = oracle.paged_decode(q[r:r + 1], kc, vc, bt[i:i + 1], cut, SM_SCALE, Hkv, k_sc, v_sc)
+            assert np.array_equal(got[r], dec[0])
+    ks, vs = 0.0213, 0.0377
+    a = oracle.paged_prefill(q, kc, vc, bt, ctx, qsl, SM_SCALE, Hkv, ks, vs)
+    b = oracle.paged_prefill(q, kc, vc, bt, ctx, qsl, SM_SCALE, Hkv, np.full(Hkv, ks), np.full(Hkv, vs))
+    assert np.array_equal(a, b)
