@@ -101,7 +101,8 @@ typedef struct pa_opts {
   size_t workspace_bytes;
   void *stream;           /* hipStream_t the work is enqueued on; NULL = null stream */
   /* fp8 caches, finer scales: NULL, or fp32 arrays with one scale per kv head
-   * (pa_decode_layers: [layers, num_kv_heads], layer-major), in device memory
+   * (pa_decode_layers: [layers, num_kv_heads], layer-major; pa_decode,
+   * pa_prefill, pa_cache_write: [num_kv_heads]), in device memory
    * or pinned host memory.  The stored value of kv head h is then
    * code * k_head_scales[h] (v_head_scales[h] for the value cache), so that
    * heads of small magnitude keep their precision (the precision per attention
@@ -207,10 +208,13 @@ PA_API pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches
  *                   n = L is causal attention over a whole prompt.  Requires
  *                   n <= L; a row whose position would be negative gets zeros.
  *   k_cache,
- *   v_cache         [num_blocks, block_size, num_kv_heads, head_dim], q's dtype.
+ *   v_cache         [num_blocks, block_size, num_kv_heads, head_dim]: q's dtype,
+ *                   or PA_FP8_E4M3 (values code * opts->k_scale / v_scale, or
+ *                   code * the kv head's entry of opts->k_head_scales /
+ *                   v_head_scales, as in pa_decode).
  *   block_tables    [num_seqs, max_blocks_per_seq] PA_I32, as in pa_decode.
  *   block_size      16 or 32; num_kv_heads divides num_heads; head_dim 64 or 128.
- *   opts            stream; optional workspace (scales, partition_size and
+ *   opts            stream, fp8 scales, optional workspace (partition_size and
  *                   num_workers are ignored; flags must be 0).
  *   opts->workspace NULL, or device memory of pa_prefill_workspace_size()
  *                   bytes, 256-byte aligned, zero-filled before its first use

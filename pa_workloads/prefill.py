@@ -15,7 +15,7 @@ from typing import Dict, Tuple, Union
 import numpy as np
 
 from .configs import DecodeConfig
-from .generate import ELEM_BYTES, FP8_MAX, Layout, _fill_pool, _pool_masked_amax, make_layout, torch_dtype
+from .generate import ELEM_BYTES, FP8_MAX, Layout, _fill_pool, _pool_masked_amax, head_stds, make_layout, torch_dtype
 
 
 @dataclass(frozen=True)
@@ -134,7 +134,8 @@ def make_prefill_inputs(pcfg: PrefillConfig, pl: PrefillLayout, device="cpu", se
     """q [N, H, D]; k_cache/v_cache with every position before the new tokens
     stored (the rest NaN, code 0x7F for fp8); k_new/v_new [N, Hkv, D]; int32
     context_lens, block_tables, query_start_loc; int64 slot_mapping [N];
-    fp32 k_scale/v_scale (fp8 only, else 1.0)."""
+    k_scale/v_scale: fp8 scales per tensor (floats; 1.0 for other dtypes) or
+    per kv head (float32 tensors [Hkv]), as make_inputs draws them."""
     import torch
 
     cfg = pcfg.base
@@ -148,21 +149,30 @@ def make_prefill_inputs(pcfg: PrefillConfig, pl: PrefillLayout, device="cpu", se
     gq.manual_seed(base + 1)
     q = torch.randn((N, H, D), generator=gq, device=device, dtype=torch.float32).to(torch_dtype(cfg.q_dtype))
     new_dtype = cfg.q_dtype if cfg.kv_dtype == "fp8" else cfg.kv_dtype
+    std_t = torch.from_numpy(head_stds(cfg)).to(device).reshape(1, 1, Hkv, 1)
     gn = torch.Generator(device=device)
     gn.manual_seed(base + 4)
-    k_new = torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
-    v_new = torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32).to(torch_dtype(new_dtype))
+    k_new = (torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32) * std_t[0]) \
+        .to(torch_dtype(new_dtype))
+    v_new = (torch.randn((N, Hkv, D), generator=gn, device=device, dtype=torch.float32) * std_t[0]) \
+        .to(torch_dtype(new_dtype))
     k_scale = v_scale = 1.0
-    ones = torch.ones((1, 1, Hkv, 1), dtype=torch.float32, device=device)
+    k_q = v_q = None
     if cfg.kv_dtype == "fp8":
-        ka = max(float(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks, ones).max()),
-                 float(k_new.float().abs().max()))
-        va = max(float(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks, ones).max()),
-                 float(v_new.float().abs().max()))
-        k_scale = float(np.float32(ka / FP8_MAX * (1.0 + 2.0**-16)))
-        v_scale = float(np.float32(va / FP8_MAX * (1.0 + 2.0**-16)))
-    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, ones, k_scale)
-    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, ones, v_scale)
+        ka = torch.maximum(_pool_masked_amax(shape, base + 2, mask_t, device, chunk_blocks, std_t),
+                           k_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
+        va = torch.maximum(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks, std_t),
+                           v_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
+        if cfg.fp8_scales == "head":  # one scale per kv head, float32 tensors [Hkv]
+            k_scale = torch.from_numpy((ka / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)).to(device)
+            v_scale = torch.from_numpy((va / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)).to(device)
+            k_q, v_q = k_scale.reshape(1, 1, Hkv, 1), v_scale.reshape(1, 1, Hkv, 1)
+        else:
+            k_scale = float(np.float32(ka.max() / FP8_MAX * (1.0 + 2.0**-16)))
+            v_scale = float(np.float32(va.max() / FP8_MAX * (1.0 + 2.0**-16)))
+            k_q, v_q = k_scale, v_scale
+    k_cache = _fill_pool(shape, cfg.kv_dtype, base + 2, mask_t, device, chunk_blocks, std_t, k_q)
+    v_cache = _fill_pool(shape, cfg.kv_dtype, base + 3, mask_t, device, chunk_blocks, std_t, v_q)
     L = pl.layout
     return {
         "q": q,

@@ -279,12 +279,13 @@ def new_prefill_workspace(device):
 
 
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, block_size: int, scale: float,
-            num_kv_heads: int, k_scale: float = 1.0, v_scale: float = 1.0, workspace=None, stream=None):
+            num_kv_heads: int, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
     """pa_prefill: fill ``out`` [N, H, D] with causal paged attention of the
     query rows of every sequence (rows query_start_loc[s] .. [s+1]-1 are the
     newest tokens of sequence s); returns ``out``.
 
-    ``k_scale`` / ``v_scale``: per-tensor scales of fp8 caches.
+    ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale per tensor, or
+    float32 tensors [num_kv_heads], one scale per kv head.
     ``workspace``: a tensor from new_prefill_workspace() (made here, once per
     call, if None), or False for none (pairs dealt round-robin)."""
     lib = load_library()
@@ -292,8 +293,7 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     if workspace is None:
         workspace = new_prefill_workspace(q.device)
     o = PaOpts()
-    o.k_scale = float(k_scale)
-    o.v_scale = float(v_scale)
+    _set_scales(o, k_scale, v_scale, num_kv_heads)
     if workspace is not False:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()

@@ -407,7 +407,10 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
-  if (o.k_head_scales || o.v_head_scales) return fail(PA_ERR_ARG, "pa_prefill takes per-tensor scales only");
+  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
+    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
+  if (o.k_head_scales && k_cache.dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (k_cache.dtype != PA_FP8_E4M3) ks = vs = 1.0f;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
@@ -458,6 +461,7 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   const int64_t slots = (N * G + a.tile_cols - 1) / a.tile_cols + S;
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");
   a.tile_slots = (int32_t)slots;
+  if ((st = head_scales(o, kv_kind(k_cache.dtype), &a.k_head_scale, &a.v_head_scale))) return st;
   if (o.workspace) {  // the key split's pair counter
     if (o.workspace_bytes < pa_prefill_workspace_size())
       return fail(PA_ERR_WORKSPACE, "prefill workspace of %zu bytes needed, %zu given", pa_prefill_workspace_size(),

@@ -83,6 +83,9 @@ struct PrefillArgs {
                                    // the pairs are then dealt round-robin
   float qk_scale_log2;             // scale * log2(e) (* k_scale for fp8)
   float v_scale;                   // 1, or the fp8 value-cache scale
+  // fp8 caches with one scale per kv head: [num_kv_heads] each, multiplied
+  // into the two above (then scale * log2(e) and 1); or null
+  const float *k_head_scale, *v_head_scale;
   int32_t kv_kind;                 // KvKind of the caches: q's, or KV_FP8
   int32_t q_kind;                  // KvKind of q (and of the matrix-core operands)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype

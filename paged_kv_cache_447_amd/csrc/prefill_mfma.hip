@@ -184,6 +184,7 @@ struct PrefillTile {
 
   // the workgroup's tile
   int s, kvh, q0, pos0, c_hi, last_max;
+  float qk_sc, v_sc;  // its score scale (log2 units) and output scale: the launch's, or its fp8 kv head's
   const_i32 *bt;
   const char *kbase, *vbase;
   // this wavefront's columns
@@ -208,6 +209,14 @@ struct PrefillTile {
   __device__ bool setup(int seq, int tile, int kh) {
     s = seq;
     kvh = kh;
+    qk_sc = a.qk_scale_log2;
+    v_sc = a.v_scale;
+    if constexpr (kFp8) {
+      if (a.k_head_scale != nullptr) {
+        qk_sc *= a.k_head_scale[kvh];
+        v_sc *= a.v_head_scale[kvh];
+      }
+    }
     int q1;
     seq_rows(a, s, q0, q1);
     const int nq = q1 - q0;
@@ -289,7 +298,7 @@ struct PrefillTile {
       f32x4 sc[2];
       core[ct].scores(qop[ct], [&](int tt, int kb) { return kop[tt][kb]; }, sc);
       // with the keys split, a wavefront's first chunks may lie past a column's limit
-      core[ct].template weights<KSP>(sc, cs, last[ct], a.qk_scale_log2, phi[ct], plo[ct]);
+      core[ct].template weights<KSP>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct]);
     }
   }
   // output update from the V rows at vs
@@ -557,7 +566,7 @@ struct PrefillTile {
         L += f[w] * pml[((w * NC + ct) * 16 + c16) * 2 + 1];
       }
       const bool z = last[ct] < 0;
-      const float inv = a.v_scale / L;
+      const float inv = v_sc / L;
       const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
 #pragma unroll
       for (int n = wave; n < NT; n += kWaves) {
@@ -587,7 +596,7 @@ struct PrefillTile {
 
   template <typename OT>
   __device__ __forceinline__ void store(int ct, bool zero) const {
-    const float inv = a.v_scale / core[ct].l;
+    const float inv = v_sc / core[ct].l;
     const bool z = zero || last[ct] < 0;
     const int64_t off = (int64_t)row[ct] * a.o_sn + (int64_t)head[ct] * a.o_sh + 4 * jq;
 #pragma unroll

@@ -353,7 +353,12 @@ def test_head_scale_errors(lib):
     expect(lib, call_write(lib, good_write(kc=pa.PA_FP8_E4M3), w), -7, "exclude")
     p = pa.PaOpts()
     p.k_head_scales = p.v_head_scales = FAKE
-    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -7, "per-tensor")
+    expect(lib, call_prefill(lib, good_prefill(), opts=p), -7, "FP8")  # 16-bit cache
+    p.k_scale = 0.5
+    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -7, "exclude")
+    p = pa.PaOpts()
+    p.v_head_scales = FAKE
+    expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -1, "together")
     p = pa.PaOpts()
     p.k_scale = float("inf")
     expect(lib, call_prefill(lib, good_prefill(kv=pa.PA_FP8_E4M3), opts=p), -7, "scale")

@@ -76,6 +76,17 @@ CASES = {
                                      block_size=16, num_seqs=2, num_blocks=200, max_blocks_per_seq=64,
                                      ctx_kind="fixed", ctx_fixed=(257, 900), allocator="shuffled"),
                               (257, 140)),
+    # fp8 caches with one scale per kv head (head magnitudes 1/4 .. 4): column mode, G = 4, head_dim 64 ...
+    "fp8_heads_gqa4_d64": P("fp8_heads_gqa4_d64",
+                            scaled(get_config("fp8_long"), num_seqs=4, num_heads=16, num_kv_heads=4, head_dim=64,
+                                   q_dtype="bf16", num_blocks=300, max_blocks_per_seq=64, ctx_kind="fixed",
+                                   ctx_fixed=(5, 100, 600, 1000), partition_size=0, fp8_scales="head",
+                                   head_std=(0.25, 4.0)),
+                            (5, 64, 130, 200)),
+    # ... and the key split on the 70B grouped-query shape
+    "fp8_heads_verify_gqa8": P("fp8_heads_verify_gqa8",
+                               scaled(get_config("gqa70b_fp8"), num_seqs=12, num_blocks=2000, max_blocks_per_seq=64,
+                                      ctx_lo=4, ctx_hi=2048), 4),
     # fp8 e4m3fn caches (per-tensor scales), rows decoded into the query's type on the way into LDS:
     # column mode, MHA, f16 q, block 32 ...
     "fp8_mha_bs32": P("fp8_mha_bs32",
@@ -274,7 +285,8 @@ def test_prefill_repeats_bit_identically_and_on_a_side_stream():
     assert torch.equal(a, b) and torch.equal(a, c)
 
 
-@pytest.mark.parametrize("case", ["verify_gqa8", "verify_gqa16_d64_bf16", "verify_gqa4_bs16", "fp8_verify_gqa8"])
+@pytest.mark.parametrize("case", ["verify_gqa8", "verify_gqa16_d64_bf16", "verify_gqa4_bs16", "fp8_verify_gqa8",
+                                  "fp8_heads_verify_gqa8"])
 def test_pair_hand_out_matches_round_robin_bitwise(case):
     """Key-split steps: pairs handed out through the workspace counter as
     workgroups free up give the same bits as pairs dealt round-robin (each
