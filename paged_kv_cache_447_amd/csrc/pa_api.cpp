@@ -135,19 +135,27 @@ pa_status device_address(const void *p, const char *name, void **dev) {
   return fail(PA_ERR_ARG, "%s: not device memory or pinned host memory", name);
 }
 
-// Per-kv-head fp8 scales of opts (both or neither, fp8 caches only, not
-// together with per-tensor scales), as device addresses; null when not given.
-pa_status head_scales(const pa_opts &o, int cache_kind, const float **ks, const float **vs) {
-  *ks = *vs = nullptr;
+// The argument checks of per-kv-head fp8 scales that need no device: both or
+// neither, fp8 caches only.
+pa_status check_head_scale_args(const pa_opts &o, int cache_kind) {
   if (!o.k_head_scales && !o.v_head_scales) return PA_OK;
   if (!o.k_head_scales || !o.v_head_scales) return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
   if (cache_kind != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  return PA_OK;
+}
+
+// Per-kv-head fp8 scales of opts (as above, and not together with per-tensor
+// scales), as device addresses; null when not given.
+pa_status head_scales(const pa_opts &o, int cache_kind, const float **ks, const float **vs) {
+  *ks = *vs = nullptr;
+  pa_status st;
+  if ((st = check_head_scale_args(o, cache_kind))) return st;
+  if (!o.k_head_scales) return PA_OK;
   if (o.k_scale != 0.0f || o.v_scale != 0.0f)
     return fail(PA_ERR_ARG, "per-tensor and per-head scales exclude each other: leave k_scale and v_scale at 0");
   if (reinterpret_cast<uintptr_t>(o.k_head_scales) % 4 || reinterpret_cast<uintptr_t>(o.v_head_scales) % 4)
     return fail(PA_ERR_LAYOUT, "per-head scales must be 4-byte aligned");
   void *dk = nullptr, *dv = nullptr;
-  pa_status st;
   if ((st = device_address(o.k_head_scales, "k_head_scales", &dk))) return st;
   if ((st = device_address(o.v_head_scales, "v_head_scales", &dv))) return st;
   *ks = static_cast<const float *>(dk);
@@ -229,9 +237,7 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
-  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
-    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
-  if (o.k_head_scales && kvk != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  if ((st = check_head_scale_args(o, kvk))) return st;
   const int64_t W = block_tables.shape[1];
   if (S > 65535 || num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 sequences or kv heads");
   if (W * block_size > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "table width too large");
@@ -407,10 +413,7 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
-  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
-    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
-  if (o.k_head_scales && k_cache.dtype != PA_FP8_E4M3)
-    return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  if ((st = check_head_scale_args(o, kv_kind(k_cache.dtype)))) return st;
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (k_cache.dtype != PA_FP8_E4M3) ks = vs = 1.0f;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
@@ -515,9 +518,7 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
   if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
-  if ((o.k_head_scales || o.v_head_scales) && (!o.k_head_scales || !o.v_head_scales))
-    return fail(PA_ERR_NULL, "k_head_scales and v_head_scales go together");
-  if (o.k_head_scales && ck != pa::KV_FP8) return fail(PA_ERR_ARG, "per-head scales apply to FP8_E4M3 caches only");
+  if ((st = check_head_scale_args(o, ck))) return st;
   if (N == 0 || Hkv == 0 || D == 0) return PA_OK;
   const float *khs = nullptr, *vhs = nullptr;
   if ((st = head_scales(o, ck, &khs, &vhs))) return st;
