@@ -142,3 +142,25 @@ def test_layers_with_head_scales_match_oracle(G):
     err = max_abs_err(out, ref)
     log(f"[layers G={G}] err32={err:.3e}")
     assert err <= TOL_F32["fp8"]
+
+
+def test_head_scales_in_pinned_host_memory():
+    """Per-head scales may live in pinned host memory (read over the link
+    through its device alias): same bits as device-resident scales.  Pageable
+    host memory is refused by the library before anything is enqueued."""
+    cfg = SMALL["gqa4_f16q_d64_bs16"]
+    layout, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)
+    dev = gpu_decode(cfg, inp, out_dtype=torch.float32)
+    ks_host = inp["k_scale"].cpu().pin_memory()
+    vs_host = inp["v_scale"].cpu().pin_memory()
+    out = torch.empty_like(dev)
+    pa.decode(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+              cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=ks_host, v_scale=vs_host,
+              partition_size=cfg.partition_size)
+    torch.cuda.synchronize()
+    assert torch.equal(out, dev)
+    with pytest.raises(pa.PaError, match="pinned host memory"):
+        pa.decode(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                  cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"].cpu(),
+                  v_scale=inp["v_scale"].cpu(), partition_size=cfg.partition_size)
