@@ -33,6 +33,10 @@
  *   - Every buffer is device memory owned by the caller.  No call allocates or
  *     frees device memory, and no call synchronises with the host: work is
  *     enqueued on opts->stream (NULL = the null stream) and the call returns.
+ *     A call enqueues kernel launches only (no memset, no copy), and every
+ *     kernel leaves its workspace counters at zero, so calls may be captured
+ *     into a HIP graph on a capturing stream and the graph replayed on the
+ *     same buffers.
  *   - Tensors are described by pa_tensor: a device pointer, a pa_dtype, a rank
  *     and per-dimension sizes and strides counted in ELEMENTS.  The last
  *     dimension must be contiguous (stride 1); the data pointer and every

@@ -1,0 +1,123 @@
+"""A serving step captured in a HIP graph (torch.cuda.graph) and replayed.
+
+The cache write followed by decode, or by prefill, goes through the C ABI into
+caller-owned workspaces and outputs, so the graph holds kernel launches only:
+no allocation and no memset.  The kernels leave their merge and hand-out
+counters at zero, so the same workspace serves every replay.  Each replay,
+with eager calls, in-place input changes and synchronisations between
+replays, must give the same bits as the eager calls on the same inputs."""
+
+import pytest
+import torch
+
+import paged_kv_cache_447_amd as pa
+from tests.gpu_common import gpu_cache_write, gpu_decode, log, setup
+from tests.test_gpu_head_scales import SMALL as HEAD_SCALE_CASES
+from tests.test_gpu_parity import SMALL as DECODE_CASES, assert_counters_zero
+from tests.test_gpu_prefill import CASES as PREFILL_CASES, setup as prefill_setup
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 4
+
+DECODE = {
+    "mha_f16_edges": DECODE_CASES["mha_f16_edges"],          # vector-ALU kernel, G = 1
+    "gqa8_f16": DECODE_CASES["gqa8_f16"],                    # matrix-core kernel, LDS ring
+    "fp8_heads_gqa4_d64": HEAD_SCALE_CASES["gqa4_f16q_d64_bs16"],  # fp8, one scale per kv head
+}
+
+
+def _other_q(q):
+    """A second query of the same shape (the first one reversed along the
+    sequences and negated), so replays can be told apart."""
+    return (-q.flip(0)).contiguous()
+
+
+@pytest.mark.parametrize("case", sorted(DECODE))
+def test_decode_step_replays_in_a_graph(case):
+    cfg = DECODE[case]
+    log(f"[graph decode {case}]")
+    _, inp = setup(cfg)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads)
+    q_a = inp["q"].clone()
+    q_b = _other_q(q_a)
+
+    # eager results on both queries (the write is idempotent: same slots, same values)
+    gpu_cache_write(cfg, inp)
+    ref_a = gpu_decode(cfg, inp, workspace=ws).clone()
+    inp["q"].copy_(q_b)
+    ref_b = gpu_decode(cfg, inp, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert not torch.equal(ref_a, ref_b)
+
+    out = torch.empty_like(ref_a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gpu_cache_write(cfg, inp)
+        gpu_decode(cfg, inp, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
+
+    for r in range(REPLAYS):
+        use_a = r % 2 == 0
+        inp["q"].copy_(q_a if use_a else q_b)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
+        assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
+        # eager work on the same workspace between replays
+        eager = gpu_decode(cfg, inp, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref_a if use_a else ref_b)
+    log(f"    {REPLAYS} replays bit-identical to the eager calls")
+
+
+@pytest.mark.parametrize("case", ["small_gqa4_d64", "verify_gqa8", "fp8_heads_verify_gqa8"])
+def test_prefill_step_replays_in_a_graph(case):
+    """Column mode (prompt chunks) and key-split mode (verification, pairs
+    handed out through the workspace counter)."""
+    pcfg = PREFILL_CASES[case]
+    cfg = pcfg.base
+    log(f"[graph prefill {case}]")
+    _, inp = prefill_setup(pcfg)
+    ws = pa.new_prefill_workspace(inp["q"].device)
+    q_a = inp["q"].clone()
+    q_b = _other_q(q_a)
+
+    def write():
+        pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+
+    def prefill(out):
+        pa.prefill(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                   inp["query_start_loc"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+                   k_scale=inp["k_scale"], v_scale=inp["v_scale"], workspace=ws)
+        return out
+
+    write()
+    ref_a = prefill(torch.empty_like(q_a))
+    inp["q"].copy_(q_b)
+    ref_b = prefill(torch.empty_like(q_a))
+    torch.cuda.synchronize()
+    assert not torch.equal(ref_a, ref_b)
+
+    out = torch.empty_like(q_a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        write()
+        prefill(out)
+    torch.cuda.synchronize()
+
+    for r in range(REPLAYS):
+        use_a = r % 2 == 0
+        inp["q"].copy_(q_a if use_a else q_b)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
+        assert int(ws.view(torch.int32)[0]) == 0, "the pair counter is left at zero"
+        eager = prefill(torch.empty_like(q_a))
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref_a if use_a else ref_b)
+    log(f"    {REPLAYS} replays bit-identical to the eager calls")
