@@ -156,6 +156,8 @@ def test_decode_unsupported(lib):
     expect(lib, call_decode(lib, good_decode(bs=8)), -5, "block_size")
     expect(lib, call_decode(lib, good_decode(H=64, Hkv=2)), -5, "group")
     expect(lib, call_decode(lib, good_decode(H=32, Hkv=2, kv=pa.PA_F32, q=pa.PA_F32)), -5, "group")
+    # one past the largest batch (65535 sequences)
+    expect(lib, call_decode(lib, good_decode(S=65536)), -5, "65535")
 
 
 def test_decode_argument_errors(lib):
@@ -323,6 +325,11 @@ def test_decode_layers_errors(lib):
     # the per-layer checks are pa_decode's: a workspace is required
     expect(lib, call(args()), -6)
     assert call(args(qshape=(0, S, H, D), kshape=(0, NB, bs, Hkv, D))) == 0  # no layers: nothing to do
+    # 2 layers x 40000 sequences: more (layer, sequence) pairs than one launch takes
+    big = 40000
+    a = [T([2, big, H, D], pa.PA_F16), T([2, big, H, D], pa.PA_F16), T([2, NB, bs, Hkv, D], pa.PA_F16),
+         T([2, NB, bs, Hkv, D], pa.PA_F16), T([big, W], pa.PA_I32), T([big], pa.PA_I32)]
+    expect(lib, call(a, with_workspace()), -5, "65535")
 
 
 def test_head_scale_errors(lib):
