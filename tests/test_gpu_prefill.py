@@ -100,6 +100,16 @@ CASES = {
                                    q_dtype="bf16", num_blocks=300, max_blocks_per_seq=64, ctx_kind="fixed",
                                    ctx_fixed=(5, 100, 600, 1000), partition_size=0),
                             (5, 64, 130, 200)),
+    # long batches: 3000 sequences verifying 4 draft tokens (key split, G = 8, one kv head) ...
+    "many_verify_gqa8_3000": P("many_verify_gqa8_3000",
+                               scaled(get_config("gqa70b"), num_seqs=3000, num_heads=8, num_kv_heads=1,
+                                      num_blocks=60000, max_blocks_per_seq=20, ctx_kind="uniform", ctx_lo=4,
+                                      ctx_hi=300), 4),
+    # ... and 1000 sequences of 24-token prompt chunks on 4 MHA heads
+    "many_chunks_mha_1000": P("many_chunks_mha_1000",
+                              scaled(get_config("llama7b"), num_seqs=1000, num_heads=4, num_kv_heads=4,
+                                     num_blocks=12000, max_blocks_per_seq=12, ctx_kind="uniform", ctx_lo=24,
+                                     ctx_hi=180), 24),
     # ... key split: 4 draft tokens, G = 8, block 32 ...
     "fp8_verify_gqa8": P("fp8_verify_gqa8",
                          scaled(get_config("gqa70b"), kv_dtype="fp8", num_seqs=12, num_blocks=2000,
