@@ -1,6 +1,6 @@
 """A serving step captured in a HIP graph (torch.cuda.graph) and replayed.
 
-The cache write followed by decode, or by prefill, goes through the C ABI into
+The cache write followed by decode (one layer or several), or by prefill, goes through the C ABI into
 caller-owned workspaces and outputs, so the graph holds kernel launches only:
 no allocation and no memset.  The kernels leave their merge and hand-out
 counters at zero, so the same workspace serves every replay.  Each replay,
@@ -118,6 +118,61 @@ def test_prefill_step_replays_in_a_graph(case):
         assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
         assert int(ws.view(torch.int32)[0]) == 0, "the pair counter is left at zero"
         eager = prefill(torch.empty_like(q_a))
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref_a if use_a else ref_b)
+    log(f"    {REPLAYS} replays bit-identical to the eager calls")
+
+
+@pytest.mark.parametrize("case", ["gqa8_bf16", "fp8_gqa4_d64"])
+def test_layers_step_replays_in_a_graph(case):
+    """pa_decode_layers after the cache write of every layer's new token,
+    captured once and replayed like the single-layer step."""
+    from pa_workloads import make_layout
+    from pa_workloads.layers import flat_slots, make_layer_inputs
+    from tests.test_gpu_layers import SMALL as LAYER_CASES
+
+    lcfg = LAYER_CASES[case]
+    cfg = lcfg.base
+    L, NB, bs = lcfg.num_layers, cfg.num_blocks, cfg.block_size
+    log(f"[graph layers {case}]")
+    inp = make_layer_inputs(lcfg, make_layout(cfg), "cuda")
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads)
+    kc = inp["k_cache"].view((L * NB,) + tuple(inp["k_cache"].shape[2:]))
+    vc = inp["v_cache"].view((L * NB,) + tuple(inp["v_cache"].shape[2:]))
+    kn = inp["k_new"].reshape((-1,) + tuple(inp["k_new"].shape[2:]))
+    vn = inp["v_new"].reshape((-1,) + tuple(inp["v_new"].shape[2:]))
+    slots = flat_slots(inp["slot_mapping"], L, NB * bs)
+    q_a = inp["q"].clone()
+    q_b = (-q_a.flip(1)).contiguous()
+
+    def step(out):
+        pa.cache_write(kn, vn, kc, vc, slots, k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+        pa.decode_layers(out, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                         bs, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                         workspace=ws)
+        return out
+
+    ref_a = step(torch.empty_like(q_a))
+    inp["q"].copy_(q_b)
+    ref_b = step(torch.empty_like(q_a))
+    torch.cuda.synchronize()
+    assert not torch.equal(ref_a, ref_b)
+
+    out = torch.empty_like(q_a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(out)
+    torch.cuda.synchronize()
+    n_counters = 4 * L * cfg.num_seqs * cfg.num_kv_heads
+    for r in range(REPLAYS):
+        use_a = r % 2 == 0
+        inp["q"].copy_(q_a if use_a else q_b)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
+        assert int(ws[:n_counters].view(torch.int32).abs().sum()) == 0
+        eager = step(torch.empty_like(q_a))
         torch.cuda.synchronize()
         assert torch.equal(eager, ref_a if use_a else ref_b)
     log(f"    {REPLAYS} replays bit-identical to the eager calls")
