@@ -100,6 +100,11 @@ CASES = {
                                    q_dtype="bf16", num_blocks=300, max_blocks_per_seq=64, ctx_kind="fixed",
                                    ctx_fixed=(5, 100, 600, 1000), partition_size=0),
                             (5, 64, 130, 200)),
+    # a whole 4096-token prompt (and a 1500-token one) in a single chunk
+    "long_prompt_4096": P("long_prompt_4096",
+                          scaled(get_config("llama7b"), num_seqs=2, num_heads=2, num_kv_heads=2, num_blocks=400,
+                                 max_blocks_per_seq=260, ctx_kind="fixed", ctx_fixed=(4096, 1500)),
+                          (4096, 1500)),
     # long batches: 3000 sequences verifying 4 draft tokens (key split, G = 8, one kv head) ...
     "many_verify_gqa8_3000": P("many_verify_gqa8_3000",
                                scaled(get_config("gqa70b"), num_seqs=3000, num_heads=8, num_kv_heads=1,
