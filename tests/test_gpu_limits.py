@@ -1,9 +1,10 @@
-"""Decode at the batch limits, against the fp64 oracle on every sequence:
+"""Decode at the limits, against the fp64 oracle on every sequence:
 65535 sequences (the most one launch takes) of 1-32 tokens on the
-matrix-core kernel, and 3000 sequences on the vector kernel.  Both are far
-past the 256 context lengths a worker reads in its first window, so the
-start-up walks many windows; the work splits cover few workers (long
-ranges), the default, and one unit per worker."""
+matrix-core kernel and 3000 sequences on the vector kernel, both far past
+the 256 context lengths a worker reads in its first window, so the start-up
+walks many windows; and 128k-token contexts on both kernels, cut across
+every worker.  The work splits cover few workers (long ranges), the default,
+and one unit per worker."""
 
 import numpy as np
 import pytest
@@ -24,6 +25,14 @@ LIMITS = {
     "many_seqs_3000_mha": scaled(get_config("llama7b"), num_seqs=3000, num_heads=4, num_kv_heads=4,
                                  num_blocks=12000, max_blocks_per_seq=8, ctx_kind="uniform", ctx_lo=1,
                                  ctx_hi=100),
+    # 128k-token contexts: cut across every worker, so one item's merge
+    # combines thousands of partials (vector kernel, fp16) ...
+    "ctx_128k_mha": scaled(get_config("llama7b"), num_seqs=3, num_heads=2, num_kv_heads=2, num_blocks=11000,
+                           max_blocks_per_seq=8192, ctx_kind="fixed", ctx_fixed=(131072, 5, 40000)),
+    # ... and matrix-core kernel, fp8 with one scale per kv head, G = 8
+    "ctx_128k_gqa8_fp8_heads": scaled(get_config("gqa70b_fp8"), num_seqs=2, num_heads=16, num_kv_heads=2,
+                                      num_blocks=4200, max_blocks_per_seq=4096, ctx_kind="fixed",
+                                      ctx_fixed=(131072, 777)),
 }
 SPLITS = [(0, 7), (0, 0), (0, 65536)]
 
