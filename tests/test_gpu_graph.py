@@ -176,3 +176,54 @@ def test_layers_step_replays_in_a_graph(case):
         torch.cuda.synchronize()
         assert torch.equal(eager, ref_a if use_a else ref_b)
     log(f"    {REPLAYS} replays bit-identical to the eager calls")
+
+
+def test_copy_on_write_then_decode_replays_in_a_graph():
+    """pa_copy_blocks (a private copy of sequence 0's last block, inside the
+    pool) then decode through a table that points at the copy, captured once.
+    Before every replay the copy's block is poisoned with NaN, so each replay
+    must redo the copy; its output must equal the eager decode of the
+    original table bit for bit."""
+    cfg = DECODE_CASES["gqa8_f16"]
+    log("[graph copy-on-write + decode gqa8_f16]")
+    _, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)
+    bt = inp["block_tables"]
+    ctx0 = int(inp["context_lens"][0])
+    j = (ctx0 - 1) // cfg.block_size
+    used = set(bt.flatten().tolist())
+    new = next(b for b in range(cfg.num_blocks - 1, -1, -1) if b not in used)
+    old = int(bt[0, j])
+    bt_copy = bt.clone()
+    bt_copy[0, j] = new
+    mapping = torch.tensor([[old, new]], dtype=torch.int64, device=bt.device)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads)
+    q_a = inp["q"].clone()
+    q_b = _other_q(q_a)
+
+    ref_a = gpu_decode(cfg, inp, workspace=ws).clone()
+    inp["q"].copy_(q_b)
+    ref_b = gpu_decode(cfg, inp, workspace=ws).clone()
+    torch.cuda.synchronize()
+
+    copied = dict(inp, block_tables=bt_copy)
+    out = torch.empty_like(ref_a)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.copy_blocks(inp["k_cache"], inp["v_cache"], inp["k_cache"], inp["v_cache"], mapping)
+        gpu_decode(cfg, copied, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        use_a = r % 2 == 0
+        inp["q"].copy_(q_a if use_a else q_b)
+        inp["k_cache"][new].fill_(float("nan"))
+        inp["v_cache"][new].fill_(float("nan"))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
+        # byte comparison: the pool's unwritten slots hold NaN on purpose
+        assert torch.equal(inp["k_cache"][new].view(torch.int16), inp["k_cache"][old].view(torch.int16))
+        assert torch.equal(inp["v_cache"][new].view(torch.int16), inp["v_cache"][old].view(torch.int16))
+        assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
+    log(f"    {REPLAYS} replays bit-identical to the eager calls")
