@@ -60,3 +60,30 @@ def test_batch_limits_match_oracle(case):
         log(f"    workers={workers}: err={err:.3e} err32={err32:.3e} max|ref|={np.abs(ref).max():.3f}")
         assert err <= TOL_OUT[cfg.kv_dtype]
         assert err32 <= TOL_F32[cfg.kv_dtype]
+
+
+def test_layers_at_the_pair_limit_match_oracle():
+    """pa_decode_layers over 8 layers x 8191 sequences: 65528 (layer,
+    sequence) pairs, just under the 65535 one launch takes, every output
+    against the multi-layer oracle."""
+    from pa_workloads import make_layout
+    from pa_workloads.layers import LayerConfig, make_layer_inputs
+    from tests.test_gpu_layers import gpu_layer_step, oracle_layer_step
+
+    lcfg = LayerConfig("max_pairs_8x8191",
+                       scaled(get_config("gqa70b"), num_seqs=8191, num_heads=4, num_kv_heads=1, head_dim=64,
+                              block_size=16, num_blocks=16500, max_blocks_per_seq=2, ctx_kind="uniform", ctx_lo=1,
+                              ctx_hi=32), 8)
+    cfg = lcfg.base
+    log(f"[{lcfg.name}] generating")
+    inp = make_layer_inputs(lcfg, make_layout(cfg), "cuda")
+    host = host_inputs(inp)
+    ws = pa.new_workspace(inp["q"], cfg.num_kv_heads)
+    out = gpu_layer_step(lcfg, inp, out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    assert_counters_zero(ws, lcfg.num_layers * cfg.num_seqs, cfg.num_kv_heads)
+    log(f"[{lcfg.name}] oracle")
+    ref, _, _ = oracle_layer_step(lcfg, host)
+    err32 = max_abs_err(out, ref)
+    log(f"    err32={err32:.3e} max|ref|={np.abs(ref).max():.3f}")
+    assert err32 <= TOL_F32[cfg.kv_dtype]
