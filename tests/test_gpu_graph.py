@@ -227,3 +227,35 @@ def test_copy_on_write_then_decode_replays_in_a_graph():
         assert torch.equal(inp["v_cache"][new].view(torch.int16), inp["v_cache"][old].view(torch.int16))
         assert_counters_zero(ws, cfg.num_seqs, cfg.num_kv_heads)
     log(f"    {REPLAYS} replays bit-identical to the eager calls")
+
+
+def test_swap_out_replays_in_a_graph():
+    """pa_copy_blocks from the device pool into pinned host pools, captured
+    once.  The host pools are cleared on the CPU before every replay; each
+    replay must write the mapped blocks back, byte for byte."""
+    cfg = DECODE_CASES["gqa8_f16"]
+    log("[graph swap-out gqa8_f16]")
+    _, inp = setup(cfg)
+    gpu_cache_write(cfg, inp)
+    torch.cuda.synchronize()
+    n_host = 40
+    src = torch.randperm(cfg.num_blocks, generator=torch.Generator().manual_seed(7))[:n_host]
+    mapping = torch.stack([src, torch.arange(n_host)], dim=1).to(torch.int64).cuda()
+    shape = (n_host,) + tuple(inp["k_cache"].shape[1:])
+    hk = torch.empty(shape, dtype=inp["k_cache"].dtype).pin_memory()
+    hv = torch.empty(shape, dtype=inp["v_cache"].dtype).pin_memory()
+    want_k = inp["k_cache"][src.cuda()].cpu().view(torch.int16)
+    want_v = inp["v_cache"][src.cuda()].cpu().view(torch.int16)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.copy_blocks(hk, hv, inp["k_cache"], inp["v_cache"], mapping)
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        hk.zero_()
+        hv.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hk.view(torch.int16), want_k), f"replay {r}: K blocks differ"
+        assert torch.equal(hv.view(torch.int16), want_v), f"replay {r}: V blocks differ"
+    log(f"    {REPLAYS} replays wrote the {n_host} blocks back")
