@@ -112,15 +112,18 @@ struct MfmaMath : MfmaCore<MT, D> {
 
   __device__ void write_partial(int64_t slot) const {
     if (c16 >= G) return;
-    float *pacc = slot_acc<G, D>(a, slot) + c16 * D;
+    const int64_t pacc = slot_acc<G, D>(slot) + c16 * D;
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
+    for (int n = 0; n < NT; ++n) {
+      float o[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_shared(pacc + 16 * n + 4 * j + i, acc[n][i]);
+      for (int i = 0; i < 4; ++i) o[i] = acc[n][i];
+      store_shared4(a, pacc + 16 * n + 4 * j, o);
+    }
     if (j == 0) {
-      float *pml = slot_ml<G>(a, slot);
-      store_shared(pml + 2 * c16, m);
-      store_shared(pml + 2 * c16 + 1, l);
+      const int64_t pml = slot_ml<G>(slot);
+      store_shared_ml(a, pml + 2 * c16, m);
+      store_shared_ml(a, pml + 2 * c16 + 1, l);
     }
   }
 };

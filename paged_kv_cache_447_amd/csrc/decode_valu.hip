@@ -362,18 +362,18 @@ struct ValuSeg {
 
   __device__ void write_partial(int64_t slot) const {
     if (tg == 0) {
-      float *pacc = slot_acc<G, D>(a, slot);
+      const int64_t pacc = slot_acc<G, D>(slot);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) store_shared(pacc + h * D + r * VEC + v, acc[h][v]);
+        for (int v = 0; v < VEC; v += 4) store_shared4(a, pacc + h * D + r * VEC + v, &acc[h][v]);
     }
     if (lane == 0) {
-      float *pml = slot_ml<G>(a, slot);
+      const int64_t pml = slot_ml<G>(slot);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        store_shared(pml + 2 * h, m[h]);
-        store_shared(pml + 2 * h + 1, l[h]);
+        store_shared_ml(a, pml + 2 * h, m[h]);
+        store_shared_ml(a, pml + 2 * h + 1, l[h]);
       }
     }
   }

@@ -260,6 +260,8 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
     return fail(PA_ERR_UNSUPPORTED, "too many work units");
   const int32_t nw = effective_workers(o.num_workers);
   const WsLayout ws = workspace_layout(layers * S, H, num_kv_heads, D, nw);
+  if (ws.total - ws.acc >= ((size_t)1 << 32))  // partial slots are addressed with 32-bit byte offsets
+    return fail(PA_ERR_UNSUPPORTED, "num_workers %d too large for this head shape", nw);
   if (!o.workspace || o.workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
                 o.workspace ? o.workspace_bytes : (size_t)0);
@@ -280,6 +282,8 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   a.counters = reinterpret_cast<int32_t *>(wsb + ws.counters);
   a.part_ml = reinterpret_cast<float *>(wsb + ws.ml);
   a.part_acc = reinterpret_cast<float *>(wsb + ws.acc);
+  a.ml_bytes = (uint32_t)(ws.acc - ws.ml);
+  a.acc_bytes = (uint32_t)(ws.total - ws.acc);
   a.q_ss = q.stride[0];
   a.q_sh = q.stride[1];
   a.o_ss = out.stride[0];

@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t *counters;   // [S * Hkv] finished-partial counters; zero between calls
   float *part_ml;      // [2 * num_workers, G, 2] partial (max in log2 units, sum)
   float *part_acc;     // [2 * num_workers, G, D] partial unnormalised outputs
+  uint32_t ml_bytes, acc_bytes;  // sizes of the two partial regions (< 2^32)
   int64_t q_ss, q_sh;           // q strides: sequence, head
   int64_t o_ss, o_sh;           // out strides
   int64_t k_sb, k_st, k_sh;     // k_cache strides: block, token, kv head

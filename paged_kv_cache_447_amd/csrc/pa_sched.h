@@ -140,24 +140,42 @@ __device__ __forceinline__ void load_windows(const DecodeArgs &a, int lane, Wind
   }
 }
 
-// Per-segment partial result layout in the workspace.
-template <int G, int D>
-__device__ __forceinline__ float *slot_acc(const DecodeArgs &a, int64_t slot) {
-  return a.part_acc + slot * (int64_t)(G * D);
+// Partials cross between wavefronts of different XCDs.  They are written and
+// read through buffer descriptors over the two workspace regions with the
+// device-coherent cache policy (sc1, the policy of device-scope atomic
+// stores and loads: writes go through to the coherent level past every XCD's
+// own L2, reads come from it), 16 bytes per access, so a wave's accesses
+// cover whole lines; an access outside a region is dropped by the
+// descriptor's bound.
+constexpr int kCoherent = 16;  // cache-policy operand: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(float *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
 }
-template <int G>
-__device__ __forceinline__ float *slot_ml(const DecodeArgs &a, int64_t slot) {
-  return a.part_ml + slot * (int64_t)(G * 2);
+__device__ __forceinline__ void store_shared4(const DecodeArgs &a, int64_t elem, const float *x) {
+  u32x4 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(uint32_t, x[i]);
+  __builtin_amdgcn_raw_buffer_store_b128(v, region(a.part_acc, a.acc_bytes), (uint32_t)(elem * 4), 0, kCoherent);
+}
+__device__ __forceinline__ u32x4 load_shared4(const DecodeArgs &a, int64_t elem) {
+  return __builtin_amdgcn_raw_buffer_load_b128(region(a.part_acc, a.acc_bytes), (uint32_t)(elem * 4), 0, kCoherent);
+}
+__device__ __forceinline__ void store_shared_ml(const DecodeArgs &a, int64_t elem, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), region(a.part_ml, a.ml_bytes),
+                                        (uint32_t)(elem * 4), 0, kCoherent);
+}
+__device__ __forceinline__ float load_shared_ml(const DecodeArgs &a, int64_t elem) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(region(a.part_ml, a.ml_bytes),
+                                                                        (uint32_t)(elem * 4), 0, kCoherent));
 }
 
-// Partials cross between wavefronts of different XCDs: device-scope atomic
-// stores and loads reach the coherent level past every XCD's own L2.
-__device__ __forceinline__ float load_shared(const float *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_shared(float *p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Where the partial of a slot lives: G * D unnormalised outputs (head-major)
+// and G (max, sum) pairs, in elements of the two regions.
+template <int G, int D>
+__device__ __forceinline__ int64_t slot_acc(int64_t slot) { return slot * (int64_t)(G * D); }
+template <int G>
+__device__ __forceinline__ int64_t slot_ml(int64_t slot) { return slot * (int64_t)(G * 2); }
 
 template <typename QT>
 __device__ __forceinline__ void store_elem(const DecodeArgs &a, int64_t idx, float x) {
@@ -171,61 +189,71 @@ __device__ __forceinline__ void store_elem(const DecodeArgs &a, int64_t idx, flo
 // caller is the last of its workers to finish.  The partials are read in
 // batches of up to PB, all loads of a batch in flight together, and folded
 // into a running (M, L, O) per output element, so a merge costs about one
-// memory round trip per batch.  Lane l owns elements l + 64 k of the [G][D]
-// block, whose head (64 k) / D is the same for the whole wave.
+// memory round trip per batch.  Lane l owns the 16-byte vectors l + 64 k of
+// the [G][D] block (4 outputs of one head each); the (max, sum) pairs of a
+// partial are read by lanes 0 .. 2G-1 and passed to the lanes that need them.
 template <typename QT, int G, int D>
 __device__ void merge_item(const DecodeArgs &a, int s, int kvh, int64_t a0, int64_t n, const Split &sp, int lane) {
-  constexpr int EPL = G * D / 64;
-  constexpr int PB0 = 64 / (EPL + 2);
-  constexpr int PB = PB0 < 1 ? 1 : (PB0 > 8 ? 8 : PB0);  // partials per batch: about 64 registers of loads
-  static_assert((G * D) % 64 == 0 && D % 64 == 0, "a wave covers whole heads");
+  constexpr int NV = G * D / 4;        // vectors of a partial's outputs
+  constexpr int VPL = (NV + 63) / 64;  // per lane
+  constexpr int PB0 = 96 / (4 * VPL + 1);
+  constexpr int PB = PB0 < 1 ? 1 : (PB0 > 8 ? 8 : PB0);  // partials per batch: up to ~96 registers of loads
+  static_assert(D % 4 == 0 && 2 * G <= 64, "a vector stays inside one head; a lane per (max, sum) value");
   const int64_t w0 = sp.owner(a0), w1 = sp.owner(a0 + n - 1);
   const bool first_is_last = sp.begin(w0) < a0;  // range w0 began in an earlier item
   const int cnt = (int)(w1 - w0 + 1);
-  float M[EPL], L[EPL], O[EPL];
+  float M[VPL], L[VPL], O[VPL][4];
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) {
+  for (int k = 0; k < VPL; ++k) {
     M[k] = -INFINITY;
     L[k] = 0.0f;
-    O[k] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) O[k][i] = 0.0f;
   }
   for (int i0 = 0; i0 < cnt; i0 += PB) {
-    float bm[PB], bl[PB], bacc[PB][EPL];
+    float bml[PB];
+    u32x4 bacc[PB][VPL];
 #pragma unroll
     for (int b = 0; b < PB; ++b) {
       if (i0 + b >= cnt) break;
       const int64_t wi = w0 + i0 + b;
       const int64_t slot = (i0 + b == 0 && first_is_last) ? 2 * wi + 1 : 2 * wi;
-      const float *ml = slot_ml<G>(a, slot);
-      const int g = lane < G ? lane : 0;
-      bm[b] = load_shared(ml + 2 * g);
-      bl[b] = load_shared(ml + 2 * g + 1);
-      const float *pacc = slot_acc<G, D>(a, slot);
+      bml[b] = lane < 2 * G ? load_shared_ml(a, slot_ml<G>(slot) + lane) : 0.0f;
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) bacc[b][k] = load_shared(pacc + lane + 64 * k);
+      for (int k = 0; k < VPL; ++k)
+        if (lane + 64 * k < NV) bacc[b][k] = load_shared4(a, slot_acc<G, D>(slot) + 4 * (lane + 64 * k));
     }
 #pragma unroll
     for (int b = 0; b < PB; ++b) {
       if (i0 + b >= cnt) break;
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) {
-        const int g = (64 * k) / D;
-        const float mi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bm[b]), g));
-        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bl[b]), g));
-        const float mn = fmaxf(M[k], mi);
-        const float f0 = fast_exp2(M[k] - mn), f1 = fast_exp2(mi - mn);
-        L[k] = L[k] * f0 + li * f1;
-        O[k] = O[k] * f0 + bacc[b][k] * f1;
-        M[k] = mn;
+      for (int k = 0; k < VPL; ++k) {
+        int g = (4 * (lane + 64 * k)) / D;
+        g = g < G ? g : G - 1;
+        const float mi = __shfl(bml[b], 2 * g), li = __shfl(bml[b], 2 * g + 1);
+        if (lane + 64 * k < NV) {
+          const float mn = fmaxf(M[k], mi);
+          const float f0 = fast_exp2(M[k] - mn), f1 = fast_exp2(mi - mn);
+          L[k] = L[k] * f0 + li * f1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t x = bacc[b][k][i];
+            O[k][i] = O[k][i] * f0 + __builtin_bit_cast(float, x) * f1;
+          }
+          M[k] = mn;
+        }
       }
     }
   }
   const float vsc = item_scale(a, s, kvh).v;
 #pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    const int e = lane + 64 * k;
+  for (int k = 0; k < VPL; ++k) {
+    if (lane + 64 * k >= NV) continue;
+    const int e = 4 * (lane + 64 * k);
     const int head = kvh * G + e / D;
-    store_elem<QT>(a, o_row(a, s) + (int64_t)head * a.o_sh + e % D, O[k] / L[k] * vsc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      store_elem<QT>(a, o_row(a, s) + (int64_t)head * a.o_sh + e % D + i, O[k][i] / L[k] * vsc);
   }
 }
 
