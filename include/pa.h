@@ -167,6 +167,30 @@ PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
                            const pa_opts *opts);
 
 /*
+ * pa_decode_static -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *   Arguments as pa_decode; opts->workspace must be NULL and
+ *   opts->workspace_bytes 0 (else PA_ERR_ARG).  The workspace is instead a
+ *   device array owned by the library, pa_decode_static_scratch_bytes()
+ *   (24 MiB) on each device it runs on, held until the process ends.  A
+ *   request whose pa_decode_workspace_size() exceeds it returns
+ *   PA_ERR_WORKSPACE before anything is enqueued (at the default worker count
+ *   that allows, for instance, 65535 sequences x 32 kv heads with 8 query
+ *   heads of 128 dims per kv head).
+ *   The first call on a device looks the array up and enqueues one kernel on
+ *   opts->stream that clears it; every decode leaves its counters at zero
+ *   again.  No call allocates or frees memory.  Every call on one device
+ *   shares that device's array: calls that overlap on one device (other
+ *   streams, other host threads) race and must be serialised by the caller.
+ *   The results are pa_decode's, bit for bit.
+ */
+PA_API size_t pa_decode_static_scratch_bytes(void);
+PA_API pa_status pa_decode_static(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
+                                  pa_tensor block_tables, pa_tensor context_lens, int32_t block_size, float scale,
+                                  int32_t num_kv_heads, const pa_opts *opts);
+
+/*
  * pa_decode_layers -- pa_decode for several layers of the same batch in one
  * launch (the translation of many lookups batched into one call, section 5.2
  * of page "vLLM框架中的KV cache优化与PagedAttention机制详解").

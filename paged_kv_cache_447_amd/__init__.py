@@ -17,6 +17,7 @@ __all__ = [
     "PaError",
     "load_library",
     "decode",
+    "decode_static",
     "decode_layers",
     "prefill",
     "cache_write",
@@ -100,6 +101,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_decode_static.restype = i32
+    lib.pa_decode_static.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_static_scratch_bytes.argtypes = []
     lib.pa_decode_layers.restype = i32
     lib.pa_decode_layers.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_prefill.restype = i32
@@ -240,6 +245,31 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
     if st != 0:
         _raise(lib, st)
     return out
+
+
+def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
+                  num_kv_heads: int, k_scale=1.0, v_scale=1.0, partition_size: int = 0, num_workers: int = 0,
+                  stream=None):
+    """pa_decode_static: pa_decode on the library's own per-device scratch (no
+    workspace argument, nothing allocated); returns ``out``.  Calls that
+    overlap on one device race."""
+    lib = load_library()
+    _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
+    o = PaOpts()
+    _set_scales(o, k_scale, v_scale, num_kv_heads)
+    o.partition_size = partition_size
+    o.num_workers = num_workers
+    o.stream = stream if stream is not None else _current_stream(q)
+    st = lib.pa_decode_static(describe(out), describe(q), describe(k_cache), describe(v_cache),
+                              describe(block_tables), describe(context_lens), block_size, scale, num_kv_heads,
+                              ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def static_scratch_bytes() -> int:
+    return int(load_library().pa_decode_static_scratch_bytes())
 
 
 def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_size: int, scale: float,

@@ -24,6 +24,14 @@ pa_status fail(pa_status s, const char *fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+namespace pa {
+pa_status fail_message(pa_status s, const char *msg) { return fail(s, "%s", msg); }
+}  // namespace pa
+
+namespace {
+
 int elem_bytes(int32_t dt) {
   switch (dt) {
     case PA_F32: return 4;
@@ -322,6 +330,28 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
+
+}  // namespace
+
+namespace pa {
+// pa_decode on a workspace the library provides (opts->workspace must be
+// NULL): the entry point for callers that cannot allocate.
+pa_status decode_with_workspace(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
+                                pa_tensor block_tables, pa_tensor context_lens, int32_t block_size, float scale,
+                                int32_t num_kv_heads, const pa_opts *opts, void *workspace, size_t workspace_bytes) {
+  pa_opts o;
+  std::memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  if (o.workspace || o.workspace_bytes)
+    return fail(PA_ERR_ARG, "opts->workspace must be NULL: this entry point uses the library's own scratch");
+  o.workspace = workspace;
+  o.workspace_bytes = workspace_bytes;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale, num_kv_heads, &o, 1, 0,
+                     0, 0, 0);
+}
+}  // namespace pa
+
+namespace {
 
 // The view of one layer of a [layers, ...] tensor: the leading dimension dropped.
 pa_tensor layer_view(const pa_tensor &t) {

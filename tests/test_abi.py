@@ -380,3 +380,20 @@ def test_prefill_workspace_errors(lib):
     p.workspace = FAKE + 16  # misaligned
     p.workspace_bytes = 1 << 20
     expect(lib, call_prefill(lib, good_prefill(), opts=p), -6, "aligned")
+
+
+def test_decode_static_host_checks(lib):
+    """pa_decode_static (no caller workspace): a caller workspace is refused, and
+    a request larger than the library's per-device scratch is refused on the
+    host, before any device is touched."""
+    assert lib.pa_decode_static_scratch_bytes() == 24 << 20
+    o = with_workspace()
+    expect(lib, lib.pa_decode_static(*[good_decode()[k] for k in ("out", "q", "k", "v", "bt", "cl")], 16, 0.088, 2,
+                                     ctypes.byref(o)), -7, "workspace")
+    big = good_decode(S=4, H=64, Hkv=4, D=128)  # 16 query heads per kv head, 8192 workers
+    need = lib.pa_decode_workspace_size(4, 64, 4, 128, 8192)
+    assert need > lib.pa_decode_static_scratch_bytes()
+    o = pa.PaOpts()
+    o.num_workers = 8192
+    expect(lib, lib.pa_decode_static(*[big[k] for k in ("out", "q", "k", "v", "bt", "cl")], 16, 0.088, 4,
+                                     ctypes.byref(o)), -6, "static scratch")
