@@ -167,6 +167,38 @@ PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
                            const pa_opts *opts);
 
 /*
+ * pa_decode_append -- one decode step in one launch: the cache write of every
+ * sequence's new token (pa_cache_write) followed by pa_decode, fused so that
+ * the step pays one launch (the batched translation of section 5.2 of page
+ * "vLLM框架中的KV cache优化与PagedAttention机制详解", which cuts kernel launches;
+ * the new token's slot from the allocator of section 2.2 of page
+ * "vLLM推理引擎架构：PagedAttention机制与高吞吐推理").
+ *   out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
+ *   num_kv_heads, opts   as pa_decode (one layer).
+ *   k_new, v_new   [num_seqs, num_kv_heads, head_dim], the caches' dtype
+ *                  (PA_F32, PA_F16 or PA_BF16; fp8 caches are refused with
+ *                  PA_ERR_UNSUPPORTED -- use pa_cache_write then pa_decode).
+ *   slot_mapping   [num_seqs] PA_I32 or PA_I64: the slot of sequence s's new
+ *                  token, which is the token at position context_lens[s] - 1,
+ *                  i.e. block_tables[s][(L-1) / block_size] * block_size +
+ *                  (L-1) % block_size for L = context_lens[s].
+ * Effect: rows k_new[s], v_new[s] are copied to their slot and out is
+ * pa_decode's result over the updated cache, bit for bit: the decode reads the
+ * new token's K/V from k_new/v_new directly instead of from the slot being
+ * written.  A slot < 0 or past the pool is skipped, as in pa_cache_write (for
+ * instance a last token that lies in a block already stored and shared with
+ * other sequences): nothing is written and the decode reads position L - 1
+ * from the cache as it stands.  If a slot is not the one of position L - 1, or
+ * two sequences share a slot, the result is unspecified.  A sequence with
+ * context length 0 has no new token: nothing is written for it and its output
+ * is zeros.
+ */
+PA_API pa_status pa_decode_append(pa_tensor out, pa_tensor q, pa_tensor k_new, pa_tensor v_new, pa_tensor k_cache,
+                                  pa_tensor v_cache, pa_tensor slot_mapping, pa_tensor block_tables,
+                                  pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
+                                  const pa_opts *opts);
+
+/*
  * pa_decode_static -- pa_decode for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.

@@ -18,6 +18,7 @@ __all__ = [
     "load_library",
     "decode",
     "decode_static",
+    "decode_append",
     "decode_layers",
     "prefill",
     "cache_write",
@@ -101,6 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_decode_workspace_size.argtypes = [i64, i64, i64, i64, i32]
     lib.pa_decode.restype = i32
     lib.pa_decode.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
+    lib.pa_decode_append.restype = i32
+    lib.pa_decode_append.argtypes = [PaTensor] * 9 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_decode_static.restype = i32
     lib.pa_decode_static.argtypes = [PaTensor] * 6 + [i32, ctypes.c_float, i32, ctypes.POINTER(PaOpts)]
     lib.pa_decode_static_scratch_bytes.restype = ctypes.c_size_t
@@ -242,6 +245,32 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
     o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                        describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return out
+
+
+def decode_append(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                  block_size: int, scale: float, num_kv_heads: int, partition_size: int = 0, num_workers: int = 0,
+                  workspace=None, stream=None):
+    """pa_decode_append: one decode step in one launch -- sequence s's new K/V
+    rows k_new[s], v_new[s] ([S, Hkv, D], the caches' dtype) go to their slot
+    slot_mapping[s] (the slot of position context_lens[s] - 1), and ``out``
+    gets the decode over the updated cache; returns ``out``.  16-bit and fp32
+    caches (fp8 caches: cache_write, then decode)."""
+    lib = load_library()
+    _check_device(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens)
+    if workspace is None:
+        workspace = new_workspace(q, num_kv_heads, num_workers)
+    o = PaOpts()
+    o.partition_size = partition_size
+    o.num_workers = num_workers
+    o.workspace = workspace.data_ptr()
+    o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.stream = stream if stream is not None else _current_stream(q)
+    st = lib.pa_decode_append(describe(out), describe(q), describe(k_new), describe(v_new), describe(k_cache),
+                              describe(v_cache), describe(slot_mapping), describe(block_tables),
+                              describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
     if st != 0:
         _raise(lib, st)
     return out

@@ -325,7 +325,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
 // Rows sit in a slot in the swizzled placement of RowSlot (mfma_core.h).  A
 // DMA instruction fills 1 KB of LDS in lane order, so each lane fetches the
 // global granule that belongs at its LDS position.
-template <typename MT, int D, int G, int BS>
+template <typename MT, int D, int G, int BS, bool APPEND = false>
 struct MfmaRingSeg : MfmaMath<MT, D, G> {
   using Math = MfmaMath<MT, D, G>;
   using Math::a;
@@ -352,6 +352,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
     const char *base;  // cache + kv head offset
     int blk0, blk1;    // block ids of the chunk's two 16-token tiles
     int cs, last;      // first token of the chunk, last token of its segment
+    int nrow;          // fused step, an item's last segment: (sequence * kv heads + kv head) of the new token's
+                       // row, read for token `last`; else -1
   };
 
   char *ring;  // this wavefront's LDS: K0 V0 K1 V1 (HB each), Q0 Q1 (QB each)
@@ -368,6 +370,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   int lcs, llast;  // next chunk of ls to load; last token of ls
   const_i32 *lbt;
   const char *lkb, *lvb;  // K / V rows of ls: its layer's cache at its kv head
+  int lnrow;  // fused step, ls the last segment of its item: (sequence * kv heads + kv head) of the new rows; else -1
   int nblk[2];  // block ids of chunk lcs
   int lord;     // non-empty segments whose query has been loaded
   Src vpend;    // the chunk whose V rows go out next
@@ -392,9 +395,19 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
     }
   }
 
-  // the 32 rows of one chunk's K or V into a ring slot
+  // the 32 rows of one chunk's K or V into a ring slot; in a fused step the
+  // chunk that holds an item's last token takes that row from the new rows
   template <bool ISV>
   __device__ __forceinline__ void dma(const Src &src, int64_t sb, int64_t st, char *slot) const {
+    // in a fused step the chunk that holds an item's new token takes that row's
+    // granules from the new rows: a per-lane address choice, no second loop
+    const bool redirect = APPEND && uniform(src.nrow >= 0 && src.cs + CT > src.last);
+    const char *nb = nullptr;
+    if (APPEND) {
+      const int s = src.nrow / a.num_kv_heads, kvh = src.nrow - (src.nrow / a.num_kv_heads) * a.num_kv_heads;
+      nb = reinterpret_cast<const char *>(ISV ? a.v_new : a.k_new) +
+           ((int64_t)s * (ISV ? a.vn_ss : a.kn_ss) + (int64_t)kvh * (ISV ? a.vn_sh : a.kn_sh)) * 2;
+    }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       int r, g;
@@ -403,6 +416,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       const int blk = (RPI * i) / 16 ? src.blk1 : src.blk0;
       const char *bb = src.base + (int64_t)blk * sb * 2;  // uniform block base
       const char *gp = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + 8 * g) * 2);
+      if (APPEND && redirect)  // a scalar branch around the choice only: the DMA instruction is the same
+        gp = reinterpret_cast<const char *>(t == src.last ? (uintptr_t)(nb + 16 * g) : (uintptr_t)gp);
       __builtin_amdgcn_global_load_lds(gp, lds_addr(slot + 1024 * i), 16, 0, kNontemporal);
     }
   }
@@ -428,6 +443,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
       lbt = as_const(a.block_tables) + (int64_t)seq_of(a, ls.s) * a.bt_ss;
       lkb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, ls.s) + (int64_t)ls.kvh * a.k_sh) * 2;
       lvb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, ls.s) + (int64_t)ls.kvh * a.v_sh) * 2;
+      lnrow = APPEND && ls.u_hi == ls.n && append_writes(a, ls.s) ? ls.s * a.num_kv_heads + ls.kvh : -1;
       lcs = ls.t_lo;
       llast = ls.t_hi - 1;
       fetch_blocks(lcs, llast, nblk);
@@ -443,8 +459,8 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
         dma_q(ls, ring + 4 * HB + (lord & 1) * QB);
         ++lord;
       }
-      const Src k{lkb, nblk[0], nblk[1], lcs, llast};
-      vpend = Src{lvb, nblk[0], nblk[1], lcs, llast};
+      const Src k{lkb, nblk[0], nblk[1], lcs, llast, lnrow};
+      vpend = Src{lvb, nblk[0], nblk[1], lcs, llast, lnrow};
       dma<false>(k, a.k_sb, a.k_st, slot);
       lcs += CT;
       if (lcs < ls.t_hi)
@@ -463,7 +479,7 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
   __device__ bool start(const Split &split, const Windows &first, int64_t b, int64_t e) {
     sp = split;
     ccnt = cord = lord = 0;
-    vpend = Src{reinterpret_cast<const char *>(a.v_cache), 0, 0, 0, 0};  // reloaded when there is nothing left
+    vpend = Src{reinterpret_cast<const char *>(a.v_cache), 0, 0, 0, 0, -1};  // reloaded when there is nothing left
     if (!cw.init(first, b, e, lane)) return false;
     lw = cw;
     next_load_seg();
@@ -532,8 +548,15 @@ struct MfmaRingSeg : MfmaMath<MT, D, G> {
 
 // One worker of the ring kernel: its range, segment by segment; the
 // segment owns both walks over it (loads ahead, arithmetic behind).
-template <typename MT, int G, int D, class Seg>
-__device__ void run_ring_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+template <typename MT, int G, int D, class Seg, bool APPEND = false>
+__device__ __forceinline__ void run_ring_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+  if constexpr (APPEND) {  // the fused step's copy of the new rows around the decode work
+    AppendCopy<D, 2> copy;
+    copy.begin(a, w, lane);
+    run_ring_worker<MT, G, D, Seg, false>(a, w, W, lane, seg);
+    copy.end(a, w, W, lane);
+    return;
+  }
   Windows first;
   const Split sp = make_split(count_units<MT>(a, w, W, lane, first), W);
   if (w >= sp.Ws) return;
@@ -551,24 +574,24 @@ __device__ void run_ring_worker(const DecodeArgs &a, int w, int W, int lane, Seg
   seg.end();
 }
 
-template <typename KVT, typename MT, int D, int G, int BS>
+template <typename KVT, typename MT, int D, int G, int BS, bool APPEND>
 struct SegFor {
   typedef MfmaRegSeg<KVT, MT, D, G, BS> type;
   __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
     run_worker<MT, G, D>(a, w, W, lane, seg);
   }
 };
-template <typename MT, int D, int G, int BS>
-struct SegFor<MT, MT, D, G, BS> {
-  typedef MfmaRingSeg<MT, D, G, BS> type;
+template <typename MT, int D, int G, int BS, bool APPEND>
+struct SegFor<MT, MT, D, G, BS, APPEND> {
+  typedef MfmaRingSeg<MT, D, G, BS, APPEND> type;
   __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
-    run_ring_worker<MT, G, D>(a, w, W, lane, seg);
+    run_ring_worker<MT, G, D, type, APPEND>(a, w, W, lane, seg);
   }
 };
 
-template <typename KVT, typename MT, int D, int G, int BS>
+template <typename KVT, typename MT, int D, int G, int BS, bool APPEND>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
-  typedef typename SegFor<KVT, MT, D, G, BS>::type Seg;
+  typedef typename SegFor<KVT, MT, D, G, BS, APPEND>::type Seg;
   __shared__ __attribute__((aligned(1024))) char lds[kWavesPerWG][Seg::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -577,16 +600,25 @@ __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
   Seg seg(a, lane, lds[wave]);
-  SegFor<KVT, MT, D, G, BS>::run(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
+  SegFor<KVT, MT, D, G, BS, APPEND>::run(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
 template <typename KVT, typename MT, int D, int G>
 hipError_t launch_g(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid(a.num_workers / kWavesPerWG), block(64 * kWavesPerWG);
+  if constexpr (__is_same(KVT, MT)) {  // the fused step: 16-bit caches (the ring kernel)
+    if (a.append) {
+      if (a.block_size == 16)
+        hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.block_size == 16)
-    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

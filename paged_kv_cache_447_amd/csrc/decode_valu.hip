@@ -154,7 +154,7 @@ __device__ __forceinline__ void store_vec(void *base, int64_t off, const float *
   }
 }
 
-template <typename KVT, typename QT, int D, int G, int BS, int NL>
+template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND = false>
 struct ValuSeg {
   static constexpr int VEC = Elem<KVT>::kPer16;  // KV elements per 16-byte load
   static constexpr int LPR = D / VEC;            // lanes per token row
@@ -188,14 +188,29 @@ struct ValuSeg {
   }
 
   // the block's base address is uniform (scalar registers); each lane adds a
-  // 32-bit offset inside the block
+  // 32-bit offset inside the block.  In a fused step (APPEND) the chunk that
+  // holds an item's last token -- the step's new token, nrow non-null, whose
+  // slot this launch is writing -- reads that token's row from the new rows:
+  // every lane whose (clamped) token is the last one gets the new row's
+  // address, in the same load instructions.
+  template <bool ISV = false>
   __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
-                                        u32x4 *dst) const {
+                                        u32x4 *dst, int nrow = -1) const {
+    const bool redirect = APPEND && uniform(nrow >= 0 && cs + CH > last);
+    const char *nb = nullptr;
+    if (APPEND) {  // the new row of (sequence, kv head) nrow
+      const int s = nrow / a.num_kv_heads, kvh = nrow - (nrow / a.num_kv_heads) * a.num_kv_heads;
+      nb = reinterpret_cast<const char *>(ISV ? a.v_new : a.k_new) +
+           ((int64_t)s * (ISV ? a.vn_ss : a.kn_ss) + (int64_t)kvh * (ISV ? a.vn_sh : a.kn_sh) + r * VEC) * EB;
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int t = min(cs + i * TPW + tg, last);
       const char *bb = base + (int64_t)blk[i] * sb * EB;
-      dst[i] = ld16_stream(bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + r * VEC) * EB));
+      const char *pl = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + r * VEC) * EB);
+      if (APPEND && redirect)  // a scalar branch around the choice only: the load instruction is the same
+        pl = reinterpret_cast<const char *>(t == last ? (uintptr_t)nb : (uintptr_t)pl);
+      dst[i] = ld16_stream(pl);
     }
   }
 
@@ -204,6 +219,7 @@ struct ValuSeg {
     const_i32 *bt;
     const char *kb, *vb;
     int last;
+    int nrow;  // fused step, the item's last segment: the (sequence * kv heads + kv head) of the new token's rows; else -1
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
@@ -211,6 +227,7 @@ struct ValuSeg {
     p.kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, g.s) + (int64_t)g.kvh * a.k_sh) * EB;  // uniform
     p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
+    p.nrow = APPEND && g.u_hi == g.n && append_writes(a, g.s) ? g.s * a.num_kv_heads + g.kvh : -1;
     return p;
   }
   __device__ __forceinline__ void load_q(const SegInfo &g, QSlice<KVT, QT> *dst) const {
@@ -237,9 +254,9 @@ struct ValuSeg {
     load_q(g, q);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
     __builtin_amdgcn_sched_barrier(0);
-    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
+    issue<false>(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr, p.nrow);
     __builtin_amdgcn_sched_barrier(0);
-    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
+    issue<true>(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr, p.nrow);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -273,6 +290,7 @@ struct ValuSeg {
       const char *kbn = lastc ? pn.kb : p.kb;
       const char *vbn = lastc ? pn.vb : p.vb;
       const int lastn = lastc ? pn.last : p.last;
+      const int nrn = lastc ? pn.nrow : p.nrow;
       int nblk[NL];
       fetch_blocks(btn, cn, lastn, nblk);
       // the scheduler would otherwise sink table reads and loads down to their
@@ -292,7 +310,7 @@ struct ValuSeg {
         for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * isc.qk : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
+      issue<false>(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr, nrn);
       __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -326,7 +344,7 @@ struct ValuSeg {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
+      issue<true>(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr, nrn);
       __builtin_amdgcn_sched_barrier(0);
       cs = cn;
 #pragma unroll
@@ -379,7 +397,7 @@ struct ValuSeg {
   }
 };
 
-template <typename KVT, typename QT, int D, int G, int BS, int NL>
+template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_valu(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -387,8 +405,9 @@ __global__ void __launch_bounds__(64 * kWavesPerWG) decode_valu(const DecodeArgs
   // XCD's workers hold one contiguous stretch of the work order
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  ValuSeg<KVT, QT, D, G, BS, NL> seg(a, lane);
-  run_worker<QT, G, D>(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
+  ValuSeg<KVT, QT, D, G, BS, NL, APPEND> seg(a, lane);
+  run_worker<QT, G, D, ValuSeg<KVT, QT, D, G, BS, NL, APPEND>, APPEND ? Elem<KVT>::kBytes : 0>(
+      a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
 // loads per chunk: fewer for larger groups, whose query, score and accumulator
@@ -399,10 +418,19 @@ template <typename KVT, typename QT, int D, int G>
 hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
   constexpr int NL = nl_for<G>();
   const dim3 grid(a.num_workers / kWavesPerWG), block(64 * kWavesPerWG);
+  if constexpr (!__is_same(KVT, fp8_t)) {  // the fused step copies rows of the cache's own dtype
+    if (a.append) {
+      if (a.block_size == 16)
+        hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if (a.block_size == 16)
-    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL, false>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

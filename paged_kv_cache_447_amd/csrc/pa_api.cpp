@@ -189,12 +189,19 @@ size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num
 
 namespace {
 
+// The new tokens of pa_decode_append.
+struct AppendIn {
+  pa_tensor k_new, v_new, slot_mapping;
+};
+
 // pa_decode over one layer (layers = 1, strides 0), or over several layers
 // whose per-layer views out/q/k_cache/v_cache are given with the layer
-// strides (elements) between consecutive layers.
+// strides (elements) between consecutive layers; with `ap`, the one-layer
+// step that also stores every sequence's new token (pa_decode_append).
 pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache, pa_tensor block_tables,
                       pa_tensor context_lens, int32_t block_size, float scale, int32_t num_kv_heads,
-                      const pa_opts *opts, int64_t layers, int64_t q_sl, int64_t o_sl, int64_t k_sl, int64_t v_sl) {
+                      const pa_opts *opts, int64_t layers, int64_t q_sl, int64_t o_sl, int64_t k_sl, int64_t v_sl,
+                      const AppendIn *ap = nullptr) {
   pa_opts o;
   std::memset(&o, 0, sizeof o);
   if (opts) o = *opts;
@@ -277,6 +284,22 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
 
   const float *khs = nullptr, *vhs = nullptr;
   if ((st = head_scales(o, kvk, &khs, &vhs))) return st;
+  if (ap) {
+    if ((st = check_tensor(ap->k_new, "k_new", 3, true))) return st;
+    if ((st = check_tensor(ap->v_new, "v_new", 3, true))) return st;
+    if ((st = check_tensor(ap->slot_mapping, "slot_mapping", 1, false))) return st;
+    if (kvk == pa::KV_FP8)
+      return fail(PA_ERR_UNSUPPORTED, "fp8 caches: write the new tokens with pa_cache_write, then pa_decode");
+    if (ap->k_new.dtype != k_cache.dtype || ap->v_new.dtype != k_cache.dtype)
+      return fail(PA_ERR_DTYPE, "k_new and v_new must have the caches' dtype");
+    if (ap->slot_mapping.dtype != PA_I64 && ap->slot_mapping.dtype != PA_I32)
+      return fail(PA_ERR_DTYPE, "slot_mapping: dtype must be I64 or I32");
+    for (const pa_tensor *t : {&ap->k_new, &ap->v_new})
+      if (t->shape[0] != S || t->shape[1] != num_kv_heads || t->shape[2] != D)
+        return fail(PA_ERR_SHAPE, "k_new and v_new must be [num_seqs, num_kv_heads, head_dim]");
+    if (ap->slot_mapping.shape[0] != S) return fail(PA_ERR_SHAPE, "slot_mapping must have one entry per sequence");
+    if (layers != 1) return fail(PA_ERR_UNSUPPORTED, "the fused step takes one layer");
+  }
 
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
@@ -325,6 +348,18 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   a.kv_kind = kvk;
   a.q_kind = kv_kind(q.dtype);
   a.out_f32 = out.dtype == PA_F32 && q.dtype != PA_F32;
+  if (ap) {
+    a.append = 1;
+    a.k_new = ap->k_new.data;
+    a.v_new = ap->v_new.data;
+    a.kn_ss = ap->k_new.stride[0];
+    a.kn_sh = ap->k_new.stride[1];
+    a.vn_ss = ap->v_new.stride[0];
+    a.vn_sh = ap->v_new.stride[1];
+    a.slot_mapping = ap->slot_mapping.data;
+    a.slot_i64 = ap->slot_mapping.dtype == PA_I64;
+    a.num_slots = NB * block_size;
+  }
 
   hipError_t e = pa::launch_decode(a, static_cast<hipStream_t>(o.stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "decode kernel launch: %s", hipGetErrorString(e));
@@ -376,6 +411,14 @@ pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_c
                     const pa_opts *opts) {
   return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale, num_kv_heads, opts, 1,
                      0, 0, 0, 0);
+}
+
+pa_status pa_decode_append(pa_tensor out, pa_tensor q, pa_tensor k_new, pa_tensor v_new, pa_tensor k_cache,
+                           pa_tensor v_cache, pa_tensor slot_mapping, pa_tensor block_tables, pa_tensor context_lens,
+                           int32_t block_size, float scale, int32_t num_kv_heads, const pa_opts *opts) {
+  const AppendIn ap{k_new, v_new, slot_mapping};
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale, num_kv_heads, opts, 1,
+                     0, 0, 0, 0, &ap);
 }
 
 pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches, pa_tensor v_caches,

@@ -53,6 +53,15 @@ struct DecodeArgs {
   // these strides (elements).  One layer: seqs_per_layer = num_seqs.
   int32_t seqs_per_layer;
   int64_t q_sl, o_sl, k_sl, v_sl;
+  // pa_decode_append: the step's new token of every sequence, stored at its
+  // slot by the launch itself and read in place of the cache row at position
+  // context_len - 1 (one layer; the new rows have the cache's dtype)
+  int32_t append;
+  const void *k_new, *v_new;       // [num_seqs, num_kv_heads, head_dim]
+  int64_t kn_ss, kn_sh, vn_ss, vn_sh;
+  const void *slot_mapping;        // [num_seqs] int32 or int64
+  int32_t slot_i64;
+  int64_t num_slots;               // num_blocks * block_size
 };
 
 // Everything a prefill launch needs, already validated; strides in elements.

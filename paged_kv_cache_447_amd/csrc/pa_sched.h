@@ -286,6 +286,67 @@ __device__ __forceinline__ void finish_partial(const DecodeArgs &a, int s, int k
   publish_partial<QT, G, D>(a, s, kvh, a0, n, sp, lane);
 }
 
+// The cache write of a fused step (pa_decode_append): every sequence's new
+// K and V rows, split into row pieces of one kv head (head_dim elements,
+// LPP lanes of 16 bytes each), piece p handled by lane group p % PPI of
+// worker (p / PPI) % W.  A worker loads its first pieces with the context
+// lengths it loads at its start (so they add no wait of their own) and
+// stores them when it has finished its decode work, so no store is pending
+// while its load pipeline runs; pieces past the first W * PPI (large batches)
+// are copied then too, one load and store each.  Slots < 0 or past the pool
+// are skipped, and so are sequences with an empty context.  No worker reads a
+// slot being written here: the decode takes the new token's rows from k_new /
+// v_new.
+template <int D, int EB>
+struct AppendRows {
+  static constexpr int LPP = D * EB / 16;  // lanes per piece
+  static constexpr int PPI = 64 / LPP;     // pieces per wave-wide instruction
+  static_assert(LPP >= 1 && LPP <= 64 && 64 % LPP == 0, "a piece is a whole number of lanes");
+  u32x4 v;
+  int64_t p, slot;
+  int ctx;
+
+  // Issue the loads of piece p (this lane's 16 bytes, the slot, the length);
+  // nothing here waits for them.
+  __device__ __forceinline__ void load(const DecodeArgs &a, int64_t piece, int lane) {
+    p = piece;
+    if (p >= 2 * (int64_t)a.num_seqs * a.num_kv_heads) return;
+    const int kvh = (int)(p % a.num_kv_heads);
+    const bool is_v = (p / a.num_kv_heads) & 1;
+    const int64_t n = p / (2 * (int64_t)a.num_kv_heads);
+    const int64_t c = (int64_t)(lane % LPP) * (16 / EB);  // this lane's element of the row
+    // both candidate addresses as values (a choice between fields of the
+    // kernel's argument block would place that block in private memory)
+    const uintptr_t src_k = (uintptr_t)a.k_new + (uintptr_t)((n * a.kn_ss + kvh * a.kn_sh + c) * EB);
+    const uintptr_t src_v = (uintptr_t)a.v_new + (uintptr_t)((n * a.vn_ss + kvh * a.vn_sh + c) * EB);
+    v = ld16(reinterpret_cast<const void *>(is_v ? src_v : src_k));
+    slot = a.slot_i64 ? reinterpret_cast<const int64_t *>(a.slot_mapping)[n]
+                      : (int64_t)reinterpret_cast<const int32_t *>(a.slot_mapping)[n];
+    ctx = a.context_lens[n];
+  }
+  // Store the piece to its slot (after the loads have arrived).
+  __device__ __forceinline__ void store(const DecodeArgs &a, int lane) const {
+    if (p >= 2 * (int64_t)a.num_seqs * a.num_kv_heads || slot < 0 || slot >= a.num_slots || ctx <= 0) return;
+    const int kvh = (int)(p % a.num_kv_heads);
+    const bool is_v = (p / a.num_kv_heads) & 1;
+    const int64_t c = (int64_t)(lane % LPP) * (16 / EB);
+    const int64_t blk = slot / a.block_size, off = slot % a.block_size;
+    const uintptr_t dst_k = (uintptr_t)a.k_cache + (uintptr_t)((blk * a.k_sb + off * a.k_st + kvh * a.k_sh + c) * EB);
+    const uintptr_t dst_v = (uintptr_t)a.v_cache + (uintptr_t)((blk * a.v_sb + off * a.v_st + kvh * a.v_sh + c) * EB);
+    st16(reinterpret_cast<void *>(is_v ? dst_v : dst_k), v);
+  }
+};
+
+// A fused step writes sequence s's new token only to a slot inside the pool;
+// only then does the decode take that token's rows from the new rows (a
+// skipped slot leaves the cache as it stands, and the decode reads it).
+__device__ __forceinline__ bool append_writes(const DecodeArgs &a, int s) {
+  typedef const __attribute__((address_space(4))) int64_t c64;
+  typedef const __attribute__((address_space(4))) int32_t c32;
+  const int64_t slot = a.slot_i64 ? ((c64 *)(uintptr_t)a.slot_mapping)[s] : (int64_t)((c32 *)(uintptr_t)a.slot_mapping)[s];
+  return slot >= 0 && slot < a.num_slots;
+}
+
 // Zero the output rows of sequences with an empty context (sequence s is
 // handled by worker s mod W).
 template <typename QT>
@@ -477,8 +538,35 @@ __device__ int64_t count_units(const DecodeArgs &a, int w, int W, int lane, Wind
   return T * a.num_kv_heads;
 }
 
-template <typename QT, int G, int D, class Seg>
-__device__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+// A fused step's copy of the new rows around a worker's decode work: its
+// first pieces loaded before the work starts, stored (and the rest copied)
+// after it ends.
+template <int D, int EB>
+struct AppendCopy {
+  typedef AppendRows<D, EB> Rows;
+  Rows rows;
+  __device__ __forceinline__ void begin(const DecodeArgs &a, int w, int lane) {
+    rows.load(a, (int64_t)w * Rows::PPI + lane / Rows::LPP, lane);
+  }
+  __device__ __forceinline__ void end(const DecodeArgs &a, int w, int W, int lane) {
+    rows.store(a, lane);
+    const int64_t pieces = 2 * (int64_t)a.num_seqs * a.num_kv_heads;
+    for (int64_t p0 = ((int64_t)W + w) * Rows::PPI; p0 < pieces; p0 += (int64_t)W * Rows::PPI) {
+      rows.load(a, p0 + lane / Rows::LPP, lane);
+      rows.store(a, lane);
+    }
+  }
+};
+
+template <typename QT, int G, int D, class Seg, int APPEND_EB = 0>
+__device__ __forceinline__ void run_worker(const DecodeArgs &a, int w, int W, int lane, Seg &seg) {
+  if constexpr (APPEND_EB > 0) {
+    AppendCopy<D, APPEND_EB> copy;
+    copy.begin(a, w, lane);
+    run_worker<QT, G, D, Seg, 0>(a, w, W, lane, seg);
+    copy.end(a, w, W, lane);
+    return;
+  }
   Windows first;
   const Split sp = make_split(count_units<QT>(a, w, W, lane, first), W);
   if (w >= sp.Ws) return;

@@ -397,3 +397,21 @@ def test_decode_static_host_checks(lib):
     o.num_workers = 8192
     expect(lib, lib.pa_decode_static(*[big[k] for k in ("out", "q", "k", "v", "bt", "cl")], 16, 0.088, 4,
                                      ctypes.byref(o)), -6, "static scratch")
+
+
+def test_decode_append_host_checks(lib):
+    """pa_decode_append: the new rows must have the caches' dtype and shape
+    [num_seqs, num_kv_heads, head_dim], one slot per sequence, no fp8 caches."""
+    def call(a, kn, vn, sm, opts=None):
+        return lib.pa_decode_append(a["out"], a["q"], kn, vn, a["k"], a["v"], sm, a["bt"], a["cl"], a["bs"],
+                                    a["scale"], a["hkv"], ctypes.byref(opts or with_workspace()))
+    a = good_decode()
+    kn, vn, sm = T([4, 2, 128], pa.PA_F16), T([4, 2, 128], pa.PA_F16), T([4], pa.PA_I64)
+    expect(lib, call(a, T([4, 2, 128], pa.PA_BF16), vn, sm), -2, "k_new")
+    expect(lib, call(a, kn, T([4, 3, 128], pa.PA_F16), sm), -3, "k_new")
+    expect(lib, call(a, kn, vn, T([5], pa.PA_I64)), -3, "slot_mapping")
+    expect(lib, call(a, kn, vn, T([4], pa.PA_F32)), -2, "slot_mapping")
+    expect(lib, call(a, T([4, 2, 128], pa.PA_F16, data=0), vn, sm), -1, "k_new")
+    f8 = good_decode(kv=pa.PA_FP8_E4M3)
+    expect(lib, call(f8, T([4, 2, 128], pa.PA_FP8_E4M3), T([4, 2, 128], pa.PA_FP8_E4M3), sm), -5, "fp8")
+    expect(lib, call(a, kn, vn, sm, pa.PaOpts()), -6, "workspace")  # the decode's own checks still apply

@@ -1,0 +1,117 @@
+"""The fused decode step (pa_decode_append: the cache write of every
+sequence's new token and the decode in one launch) against the two-launch
+step it stands for (pa_cache_write then pa_decode) and the oracle.
+
+The fused step reads the new token's rows from k_new / v_new instead of the
+slot it writes, so its output must equal the two-launch step's bit for bit,
+and the pools it leaves must be byte-equal to the oracle's cache write."""
+
+import pytest
+import torch
+
+import paged_kv_cache_447_amd as pa
+from pa_workloads import get_config, scaled
+from pa_workloads.configs import CONFIG_ORDER
+from tests.gpu_common import (TOL_F32, TOL_OUT, gpu_cache_write, gpu_decode, host_inputs, log, max_abs_err,
+                              oracle_step, setup)
+from tests.test_gpu_parity import SMALL, _bytes
+
+pytestmark = pytest.mark.gpu
+
+
+def fused(cfg, inp, out_dtype=None, partition_size=None, num_workers=0):
+    q = inp["q"]
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype or q.dtype, device=q.device)
+    part = cfg.partition_size if partition_size is None else partition_size
+    pa.decode_append(out, q, inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
+                     inp["block_tables"], inp["context_lens"], cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads,
+                     partition_size=part, num_workers=num_workers)
+    return out
+
+
+def check(cfg, partition_size=None, num_workers=0, name=""):
+    layout, inp = setup(cfg)
+    host = host_inputs(inp)
+    twin = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    # the two-launch step on one copy, the fused step on the other
+    gpu_cache_write(cfg, twin)
+    want32 = gpu_decode(cfg, twin, out_dtype=torch.float32, partition_size=partition_size, num_workers=num_workers)
+    want = gpu_decode(cfg, twin, partition_size=partition_size, num_workers=num_workers)
+    got32 = fused(cfg, inp, torch.float32, partition_size, num_workers)
+    got = fused(cfg, {**inp, "k_new": inp["k_new"], "v_new": inp["v_new"]}, None, partition_size, num_workers)
+    torch.cuda.synchronize()
+    ref, kc, vc = oracle_step(cfg, host)
+    assert torch.equal(_bytes(inp["k_cache"]), kc.view(torch.uint8)), "k_cache differs from the oracle's write"
+    assert torch.equal(_bytes(inp["v_cache"]), vc.view(torch.uint8)), "v_cache differs from the oracle's write"
+    assert torch.equal(got32.view(torch.int32), want32.view(torch.int32)), "fp32 output differs from the two-launch step"
+    assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), "output differs from the two-launch step"
+    err, err32 = max_abs_err(got, ref), max_abs_err(got32, ref)
+    log(f"[{name}] fused step = two-launch step bit for bit; err={err:.3e} err32={err32:.3e}")
+    assert err <= TOL_OUT[cfg.kv_dtype] and err32 <= TOL_F32[cfg.kv_dtype]
+
+
+@pytest.mark.parametrize("name", [n for n in CONFIG_ORDER if get_config(n).kv_dtype != "fp8"])
+def test_full_size_fused_step(name):
+    check(get_config(name), name=name)
+
+
+@pytest.mark.parametrize("case", sorted(k for k, c in SMALL.items() if c.kv_dtype != "fp8"))
+@pytest.mark.parametrize("split", [(0, 0), (64, 0), (0, 4), (16, 100)], ids=["p0w0", "p64w0", "p0w4", "p16w100"])
+def test_small_fused_steps(case, split):
+    cfg = SMALL[case]
+    part, workers = split
+    part = part if part % cfg.block_size == 0 else 0
+    check(cfg, partition_size=part, num_workers=workers, name=f"{case} p={part} w={workers}")
+
+
+def test_fused_step_refuses_fp8():
+    cfg = scaled(get_config("fp8_long"), num_seqs=2, num_blocks=600, max_blocks_per_seq=256, ctx_lo=100, ctx_hi=400)
+    layout, inp = setup(cfg)
+    with pytest.raises(pa.PaError) as e:
+        fused(cfg, inp)
+    assert e.value.status == -5
+
+
+def test_fused_step_replays_in_a_graph():
+    """The fused step captured in a HIP graph (torch.cuda.graph) and replayed:
+    every replay equals the eager call bit for bit, with eager calls and a
+    changed query between replays."""
+    cfg = SMALL["gqa8_f16"]
+    for c in (cfg, SMALL["mha_f16_edges"]):
+        layout, inp = setup(c)
+        ws = pa.new_workspace(inp["q"], c.num_kv_heads)
+        out = torch.empty_like(inp["q"])
+        q_a = inp["q"].clone()
+        q_b = torch.randn_like(q_a)
+
+        def step(o):
+            pa.decode_append(o, inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"],
+                             inp["slot_mapping"], inp["block_tables"], inp["context_lens"], c.block_size,
+                             c.softmax_scale, c.num_kv_heads, workspace=ws)
+            return o
+
+        refs = {}
+        for name, qv in (("a", q_a), ("b", q_b)):
+            inp["q"].copy_(qv)
+            refs[name] = step(torch.empty_like(out)).clone()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(out)  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(out)
+        for r in range(4):
+            name = "a" if r % 2 == 0 else "b"
+            inp["q"].copy_(q_a if name == "a" else q_b)
+            out.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, refs[name]), f"replay {r} differs from the eager call"
+            eager = step(torch.empty_like(out))
+            torch.cuda.synchronize()
+            assert torch.equal(eager, refs[name])
+        log(f"[graph fused step G={c.num_heads // c.num_kv_heads}] 4 replays bit-identical to the eager call")
