@@ -88,9 +88,10 @@ def test_small_layer_steps_match_oracle(case, split):
 
 
 @pytest.mark.parametrize("name", sorted(LAYER_CONFIGS))
-def test_full_size_layer_step_sampled_sequences(name):
-    """The benchmark's multi-layer workloads at full size: all outputs finite,
-    and 6 sequences of every layer against the oracle."""
+def test_full_size_layer_step_every_sequence(name):
+    """The benchmark's multi-layer workloads at full size: every sequence of
+    every layer against the multi-layer oracle, in the query's dtype and in
+    fp32, and the pools byte-equal to the oracle's cache write."""
     lcfg = LAYER_CONFIGS[name]
     cfg = lcfg.base
     log(f"[{name}] generating")
@@ -98,15 +99,19 @@ def test_full_size_layer_step_sampled_sequences(name):
     inp = make_layer_inputs(lcfg, layout, "cuda")
     host = host_inputs(inp)
     out = gpu_layer_step(lcfg, inp)
+    out32 = torch.empty(inp["q"].shape, dtype=torch.float32, device="cuda")
+    pa.decode_layers(out32, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"],
+                     cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
+                     v_scale=inp["v_scale"])
     torch.cuda.synchronize()
-    assert torch.isfinite(out).all()
-    seqs = torch.tensor(sorted({0, 1, cfg.num_seqs // 2, cfg.num_seqs - 2, cfg.num_seqs - 1,
-                                int(layout.context_lens.argmax())}))
-    log(f"[{name}] oracle on sequences {seqs.tolist()}")
-    ref, _, _ = oracle_layer_step(lcfg, host, seqs)
-    err = max_abs_err(out[:, seqs.cuda()], ref)
-    log(f"    err={err:.3e}")
+    log(f"[{name}] oracle on all {lcfg.num_layers} x {cfg.num_seqs} (layer, sequence) pairs")
+    ref, kc, vc = oracle_layer_step(lcfg, host)
+    assert torch.equal(inp["k_cache"].cpu().view(torch.uint8), kc.view(torch.uint8))
+    assert torch.equal(inp["v_cache"].cpu().view(torch.uint8), vc.view(torch.uint8))
+    err, err32 = max_abs_err(out, ref), max_abs_err(out32, ref)
+    log(f"    err={err:.3e} err32={err32:.3e}")
     assert err <= TOL_OUT[cfg.kv_dtype]
+    assert err32 <= TOL_F32[cfg.kv_dtype]
 
 
 def test_each_layer_equals_a_single_layer_decode():
