@@ -49,6 +49,19 @@
  *     [0, num_blocks) or a context length above max_blocks_per_seq *
  *     block_size does not fault -- the kernel clamps it -- but the result for
  *     that sequence is then unspecified.
+ *   - Debugging: with PA_FLAG_VALIDATE in opts->flags a call first copies the
+ *     index and scale arrays it reads (block tables, context lengths, slot
+ *     mappings, query_start_loc, block pairs, per-head scales) to the host,
+ *     after the stream's earlier work, and checks every entry the contract
+ *     above leaves unspecified; the first bad one is returned as
+ *     PA_ERR_BAD_INDEX, with its position in pa_last_error(), and nothing is
+ *     enqueued.  Such a call waits for the stream (the one exception to "no
+ *     call synchronises"), and is refused with PA_ERR_ARG on a stream that is
+ *     being captured.  The pages treat these entries as faults reported to the
+ *     owner of the mapping: an unmapped page-table entry faults (page
+ *     "Paged KVCache：大模型推理显存管理优化方案", section 2.3), and a request
+ *     the block pool cannot serve raises an error (page
+ *     "vLLM推理引擎架构：PagedAttention机制与高吞吐推理", section 2.2).
  */
 #ifndef PA_H_
 #define PA_H_
@@ -89,7 +102,11 @@ typedef enum pa_status {
   PA_ERR_WORKSPACE = -6,   /* workspace missing, misaligned or smaller than pa_decode_workspace_size() */
   PA_ERR_ARG = -7,         /* a scalar argument out of range (scale, partition size, ...) */
   PA_ERR_HIP = -8,         /* the HIP runtime reported an error while enqueuing */
+  PA_ERR_BAD_INDEX = -9,   /* PA_FLAG_VALIDATE: an index or scale array entry the results would not survive */
 } pa_status;
+
+/* opts->flags bits */
+#define PA_FLAG_VALIDATE 1u /* check the index and scale arrays on the host first (see the conventions above) */
 
 /* Options common to both operations.  A NULL opts means all defaults. */
 typedef struct pa_opts {
@@ -99,7 +116,7 @@ typedef struct pa_opts {
                              0 = library choice (a few dozen tokens) */
   int32_t num_workers;    /* decode: wavefronts that share the work (rounded up to a multiple of 4);
                              0 = library choice for the current device */
-  uint32_t flags;         /* reserved, must be 0 */
+  uint32_t flags;         /* 0 or PA_FLAG_VALIDATE; other bits are reserved and must be 0 */
   uint32_t reserved;      /* must be 0 */
   void *workspace;        /* decode: device scratch of >= pa_decode_workspace_size() bytes */
   size_t workspace_bytes;
@@ -122,14 +139,22 @@ typedef struct pa_opts {
  * choice for the current device).  Always a positive multiple of 4. */
 PA_API int32_t pa_decode_num_workers(int32_t requested);
 
-/* Bytes of workspace pa_decode needs: one int32 counter per (sequence, kv
- * head), then two partial-result slots per worker, each holding for every
- * query head of a group a running max, a running sum and an unnormalised
- * head_dim-long output (fp32).  num_workers as in pa_opts (0 = default).
+/* Bytes of workspace pa_decode needs: two partial-result slots per worker,
+ * each holding for every query head of a group a running max, a running sum
+ * and an unnormalised head_dim-long output (fp32), from the workspace's
+ * start; one int32 merge counter per (sequence, kv head) at its end (in the
+ * last bytes of workspace_bytes rounded down to 256).  num_workers as in
+ * pa_opts (0 = default).
  * The workspace belongs to the caller: it must be zero-filled once before its
- * first use; every pa_decode call leaves the counters at zero again.  One
- * workspace serves one pa_decode at a time (calls that overlap on different
- * streams need separate workspaces). */
+ * first use.  Every pa_decode call leaves its counters at zero again and
+ * garbage only in its slots, whose extent depends on the group size
+ * (num_heads / num_kv_heads), head_dim and num_workers alone; so calls that
+ * agree on those three may share one workspace whatever their number of
+ * sequences (or layers), each sized for its own request.  A call with another
+ * group size, head_dim or worker count may lay its counters over earlier
+ * slots: zero-fill the workspace again before it.  One workspace serves one
+ * pa_decode at a time (calls that overlap on different streams need separate
+ * workspaces). */
 PA_API size_t pa_decode_workspace_size(int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
                                        int64_t head_dim, int32_t num_workers);
 
@@ -212,7 +237,11 @@ PA_API pa_status pa_decode_append(pa_tensor out, pa_tensor q, pa_tensor k_new, p
  *   heads of 128 dims per kv head).
  *   The first call on a device looks the array up and enqueues one kernel on
  *   opts->stream that clears it; every decode leaves its counters at zero
- *   again.  No call allocates or frees memory.  Every call on one device
+ *   again, so calls of any batch size follow without a clear.  A call whose
+ *   counters would overlap partial-result slots used since the last clear
+ *   (another group size, head_dim or worker count; see
+ *   pa_decode_workspace_size) enqueues the clear again first.  No call
+ *   allocates or frees memory.  Every call on one device
  *   shares that device's array: calls that overlap on one device (other
  *   streams, other host threads) race and must be serialised by the caller.
  *   The results are pa_decode's, bit for bit.
@@ -275,7 +304,7 @@ PA_API pa_status pa_decode_layers(pa_tensor out, pa_tensor q, pa_tensor k_caches
  *   block_tables    [num_seqs, max_blocks_per_seq] PA_I32, as in pa_decode.
  *   block_size      16 or 32; num_kv_heads divides num_heads; head_dim 64 or 128.
  *   opts            stream, fp8 scales, optional workspace (partition_size and
- *                   num_workers are ignored; flags must be 0).
+ *                   num_workers are ignored; flags as in pa_opts).
  *   opts->workspace NULL, or device memory of pa_prefill_workspace_size()
  *                   bytes, 256-byte aligned, zero-filled before its first use
  *                   and left at zero by every call.  With it, steps of few
@@ -342,7 +371,7 @@ PA_API pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_
  *                             skipped.  Destinations must be distinct and, within
  *                             one pool, no destination may also be a source;
  *                             otherwise the result is unspecified (never a fault).
- *   opts                      stream only (flags must be 0).
+ *   opts                      stream and flags only.
  * Errors: PA_ERR_ARG if a pointer is neither device memory nor pinned host
  * memory (pageable host memory is refused before anything is enqueued).
  * Work: one launch, a workgroup per (pair, K or V, 16 KB of the block).

@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 __all__ = [
     "LIB_PATH",
@@ -33,6 +34,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
 
 PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_I32, PA_I64 = range(6)
 
+PA_FLAG_VALIDATE = 1  # opts->flags: check index and scale arrays on the host first (debugging)
+
 STATUS_NAMES = {
     0: "PA_OK",
     -1: "PA_ERR_NULL",
@@ -43,6 +46,7 @@ STATUS_NAMES = {
     -6: "PA_ERR_WORKSPACE",
     -7: "PA_ERR_ARG",
     -8: "PA_ERR_HIP",
+    -9: "PA_ERR_BAD_INDEX",
 }
 
 
@@ -207,42 +211,89 @@ def workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: i
     return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, num_workers))
 
 
-def new_workspace(q, num_kv_heads: int, num_workers: int = 0):
-    """A zero-filled, caller-owned decode workspace for queries shaped like ``q``.
-
-    pa_decode leaves its counters at zero, so one workspace can serve any
-    number of calls of this shape, one at a time."""
-    import torch
-
+def _decode_ws_bytes(q, num_kv_heads: int, num_workers: int) -> int:
     *lead, H, D = q.shape  # [S, H, D], or [layers, S, H, D] for decode_layers
     S = 1
     for x in lead:
         S *= x
-    n = workspace_size(max(S, 1), H, num_kv_heads, D, num_workers)
-    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+    return workspace_size(max(S, 1), H, num_kv_heads, D, num_workers)
+
+
+def _decode_kind(q, num_kv_heads: int, num_workers: int):
+    return ("decode", q.shape[-2] // num_kv_heads, q.shape[-1], num_workers)
+
+
+def new_workspace(q, num_kv_heads: int, num_workers: int = 0):
+    """A zero-filled, caller-owned decode workspace for queries shaped like ``q``.
+
+    pa_decode leaves its counters at zero, so one workspace can serve any
+    number of calls, one at a time, with the same group size, head_dim and
+    worker count and at most as many (layer, sequence) pairs as ``q``."""
+    import torch
+
+    return torch.zeros(_decode_ws_bytes(q, num_kv_heads, num_workers), dtype=torch.uint8, device=q.device)
+
+
+_WS_LOCK = threading.Lock()
+_WS = {}  # (kind, device index, stream handle) -> zero-filled uint8 device tensor
+_WS_RETIRED = []  # outgrown workspaces, kept alive: launches already enqueued may still use them
+
+
+def _cached_workspace(kind, device, stream: int, nbytes: int):
+    """The binding's own workspace for calls that pass none: one zero-filled
+    buffer per (kind, device, stream), allocated by the first call that needs
+    it (again, larger, when a call needs more) and reused by every later call
+    on that stream.  Calls on one stream run in order and every call leaves
+    the workspace's counters at zero, so they can share it; calls on other
+    streams get their own.  A decode ``kind`` carries the group size, head_dim
+    and worker count: calls that differ in them lay out their partial slots
+    differently and must not share a workspace."""
+    import torch
+
+    key = (kind, device.index, int(stream or 0))
+    with _WS_LOCK:
+        ws = _WS.get(key)
+        if ws is not None and ws.numel() >= nbytes:
+            return ws
+        cur = torch.cuda.current_stream(device)
+        fresh = torch.zeros(max(nbytes, 2 * ws.numel() if ws is not None else 0), dtype=torch.uint8, device=device)
+        if int(stream or 0) != cur.cuda_stream:
+            cur.synchronize()  # the zero-fill ran on torch's current stream, not the call's
+        if ws is not None:
+            _WS_RETIRED.append(ws)
+        _WS[key] = fresh
+        return fresh
+
+
+def _flags(validate: bool) -> int:
+    return PA_FLAG_VALIDATE if validate else 0
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float, num_kv_heads: int,
            k_scale=1.0, v_scale=1.0, partition_size: int = 0, num_workers: int = 0, workspace=None,
-           stream=None):
+           stream=None, validate: bool = False):
     """pa_decode: fill ``out`` [S, H, D] with paged attention over the cache; returns ``out``.
 
-    ``workspace`` is a zero-filled device tensor from new_workspace() (made
-    here, once per call, if not given; pass one to avoid that allocation).
-    ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale per tensor, or
-    float32 tensors [num_kv_heads], one scale per kv head.
+    ``workspace``: a zero-filled device tensor from new_workspace(); if None,
+    the binding's own workspace for this device and stream (allocated once,
+    then reused).  ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale
+    per tensor, or float32 tensors [num_kv_heads], one scale per kv head.
+    ``validate``: PA_FLAG_VALIDATE (tables, lengths and scales checked on the
+    host first; waits for the stream; PaError PA_ERR_BAD_INDEX on a bad entry).
     """
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
-    if workspace is None:
-        workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
     _set_scales(o, k_scale, v_scale, num_kv_heads)
     o.partition_size = partition_size
     o.num_workers = num_workers
+    o.flags = _flags(validate)
+    o.stream = stream if stream is not None else _current_stream(q)
+    if workspace is None:
+        workspace = _cached_workspace(_decode_kind(q, num_kv_heads, num_workers), q.device, o.stream,
+                                      _decode_ws_bytes(q, num_kv_heads, num_workers))
     o.workspace = workspace.data_ptr()
     o.workspace_bytes = workspace.numel() * workspace.element_size()
-    o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                        describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
     if st != 0:
@@ -252,22 +303,25 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
 
 def decode_append(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens,
                   block_size: int, scale: float, num_kv_heads: int, partition_size: int = 0, num_workers: int = 0,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, validate: bool = False):
     """pa_decode_append: one decode step in one launch -- sequence s's new K/V
     rows k_new[s], v_new[s] ([S, Hkv, D], the caches' dtype) go to their slot
     slot_mapping[s] (the slot of position context_lens[s] - 1), and ``out``
     gets the decode over the updated cache; returns ``out``.  16-bit and fp32
-    caches (fp8 caches: cache_write, then decode)."""
+    caches (fp8 caches: cache_write, then decode).  ``workspace`` and
+    ``validate`` as in decode()."""
     lib = load_library()
     _check_device(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_tables, context_lens)
-    if workspace is None:
-        workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
     o.partition_size = partition_size
     o.num_workers = num_workers
+    o.flags = _flags(validate)
+    o.stream = stream if stream is not None else _current_stream(q)
+    if workspace is None:
+        workspace = _cached_workspace(_decode_kind(q, num_kv_heads, num_workers), q.device, o.stream,
+                                      _decode_ws_bytes(q, num_kv_heads, num_workers))
     o.workspace = workspace.data_ptr()
     o.workspace_bytes = workspace.numel() * workspace.element_size()
-    o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode_append(describe(out), describe(q), describe(k_new), describe(v_new), describe(k_cache),
                               describe(v_cache), describe(slot_mapping), describe(block_tables),
                               describe(context_lens), block_size, scale, num_kv_heads, ctypes.byref(o))
@@ -278,7 +332,7 @@ def decode_append(out, q, k_new, v_new, k_cache, v_cache, slot_mapping, block_ta
 
 def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int, scale: float,
                   num_kv_heads: int, k_scale=1.0, v_scale=1.0, partition_size: int = 0, num_workers: int = 0,
-                  stream=None):
+                  stream=None, validate: bool = False):
     """pa_decode_static: pa_decode on the library's own per-device scratch (no
     workspace argument, nothing allocated); returns ``out``.  Calls that
     overlap on one device race."""
@@ -288,6 +342,7 @@ def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, block_si
     _set_scales(o, k_scale, v_scale, num_kv_heads)
     o.partition_size = partition_size
     o.num_workers = num_workers
+    o.flags = _flags(validate)
     o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode_static(describe(out), describe(q), describe(k_cache), describe(v_cache),
                               describe(block_tables), describe(context_lens), block_size, scale, num_kv_heads,
@@ -303,21 +358,24 @@ def static_scratch_bytes() -> int:
 
 def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_size: int, scale: float,
                   num_kv_heads: int, k_scale=1.0, v_scale=1.0, partition_size: int = 0,
-                  num_workers: int = 0, workspace=None, stream=None):
+                  num_workers: int = 0, workspace=None, stream=None, validate: bool = False):
     """pa_decode_layers: ``out`` [L, S, H, D] = pa_decode of every layer l on q[l],
     k_caches[l], v_caches[l] ([L, NB, bs, Hkv, D]), with the block tables and
-    context lengths shared by all layers; returns ``out``."""
+    context lengths shared by all layers; returns ``out``.  ``workspace`` and
+    ``validate`` as in decode()."""
     lib = load_library()
     _check_device(out, q, k_caches, v_caches, block_tables, context_lens)
-    if workspace is None:
-        workspace = new_workspace(q, num_kv_heads, num_workers)
     o = PaOpts()
     _set_scales(o, k_scale, v_scale, q.shape[0] * num_kv_heads)
     o.partition_size = partition_size
     o.num_workers = num_workers
+    o.flags = _flags(validate)
+    o.stream = stream if stream is not None else _current_stream(q)
+    if workspace is None:
+        workspace = _cached_workspace(_decode_kind(q, num_kv_heads, num_workers), q.device, o.stream,
+                                      _decode_ws_bytes(q, num_kv_heads, num_workers))
     o.workspace = workspace.data_ptr()
     o.workspace_bytes = workspace.numel() * workspace.element_size()
-    o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_decode_layers(describe(out), describe(q), describe(k_caches), describe(v_caches),
                               describe(block_tables), describe(context_lens), block_size, scale, num_kv_heads,
                               ctypes.byref(o))
@@ -338,25 +396,27 @@ def new_prefill_workspace(device):
 
 
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, block_size: int, scale: float,
-            num_kv_heads: int, k_scale=1.0, v_scale=1.0, workspace=None, stream=None):
+            num_kv_heads: int, k_scale=1.0, v_scale=1.0, workspace=None, stream=None, validate: bool = False):
     """pa_prefill: fill ``out`` [N, H, D] with causal paged attention of the
     query rows of every sequence (rows query_start_loc[s] .. [s+1]-1 are the
     newest tokens of sequence s); returns ``out``.
 
     ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale per tensor, or
     float32 tensors [num_kv_heads], one scale per kv head.
-    ``workspace``: a tensor from new_prefill_workspace() (made here, once per
-    call, if None), or False for none (pairs dealt round-robin)."""
+    ``workspace``: a tensor from new_prefill_workspace(); if None, the
+    binding's own for this device and stream (allocated once, then reused);
+    False for none (pairs dealt round-robin).  ``validate`` as in decode()."""
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
-    if workspace is None:
-        workspace = new_prefill_workspace(q.device)
     o = PaOpts()
     _set_scales(o, k_scale, v_scale, num_kv_heads)
+    o.flags = _flags(validate)
+    o.stream = stream if stream is not None else _current_stream(q)
+    if workspace is None:
+        workspace = _cached_workspace("prefill", q.device, o.stream, prefill_workspace_size())
     if workspace is not False:
         o.workspace = workspace.data_ptr()
         o.workspace_bytes = workspace.numel() * workspace.element_size()
-    o.stream = stream if stream is not None else _current_stream(q)
     st = lib.pa_prefill(describe(out), describe(q), describe(k_cache), describe(v_cache), describe(block_tables),
                         describe(context_lens), describe(query_start_loc), block_size, scale, num_kv_heads,
                         ctypes.byref(o))
@@ -365,12 +425,14 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     return out
 
 
-def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None):
+def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, stream=None,
+                validate: bool = False):
     """pa_cache_write: scatter rows of k, v [N, Hkv, D] into the caches at slot_mapping [N]."""
     lib = load_library()
     _check_device(k, v, k_cache, v_cache, slot_mapping)
     o = PaOpts()
     _set_scales(o, k_scale, v_scale, k.shape[1])
+    o.flags = _flags(validate)
     o.stream = stream if stream is not None else _current_stream(k)
     st = lib.pa_cache_write(describe(k), describe(v), describe(k_cache), describe(v_cache), describe(slot_mapping),
                             ctypes.byref(o))
@@ -379,7 +441,8 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, 
     return k_cache, v_cache
 
 
-def copy_blocks(dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mapping, stream=None):
+def copy_blocks(dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mapping, stream=None,
+                validate: bool = False):
     """pa_copy_blocks: for each pair (s, d) of block_mapping [M, 2], K and V block d
     of the destination pools become copies of block s of the source pools.  Pools
     and the mapping may be GPU tensors or pinned CPU tensors (swap out / in)."""
@@ -388,6 +451,7 @@ def copy_blocks(dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mappin
         if not (t.is_cuda or t.is_pinned()):
             raise ValueError("pools and mapping must be GPU tensors or pinned CPU tensors")
     o = PaOpts()
+    o.flags = _flags(validate)
     dev = next((t for t in (dst_k_cache, src_k_cache, block_mapping) if t.is_cuda), None)
     if stream is not None:
         o.stream = stream

@@ -7,9 +7,13 @@
 // address on each device is looked up once, with that device current, by
 // hipGetSymbolAddress, and only that address reaches the kernels.  At that
 // first use on a device the array is cleared by a fill kernel on the
-// caller's stream; every decode leaves its counters at zero again, so later
-// calls find them cleared.  Every call on one device shares that device's
-// array: calls that overlap on one device race.
+// caller's stream; every decode leaves its counters (at the array's end) at
+// zero again and garbage only in its partial-result slots (from the array's
+// start, an extent fixed by the head shape and worker count), so later calls
+// of any batch size find their counters cleared.  A call whose counters would
+// reach into slots an earlier call used (another head shape or worker count)
+// clears the array again first.  Every call on one device shares that
+// device's array: calls that overlap on one device race.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -19,6 +23,7 @@
 #include "pa_internal.h"
 
 namespace pa {
+size_t decode_partials_bytes(int64_t num_heads, int64_t num_kv_heads, int64_t head_dim, int32_t num_workers);
 pa_status decode_with_workspace(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
                                 pa_tensor block_tables, pa_tensor context_lens, int32_t block_size, float scale,
                                 int32_t num_kv_heads, const pa_opts *opts, void *workspace, size_t workspace_bytes);
@@ -38,12 +43,27 @@ __global__ void clear_scratch(uint4 *p, size_t n) {
 }
 
 std::mutex g_mu;
-void *g_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up and cleared
+void *g_ptr[kMaxDevices];     // device address of `scratch` on each device, once looked up
+size_t g_dirty[kMaxDevices];  // bytes from the array's start that calls since its last clear may have left non-zero
 
-// The scratch of the current device: its address (looked up and cleared on
-// the device's first call, the clear enqueued on `stream`), or null with the
-// error message set.
-void *device_scratch(hipStream_t stream, pa_status *st) {
+pa_status enqueue_clear(void *ptr, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_scratch, dim3(256), dim3(256), 0, stream, static_cast<uint4 *>(ptr),
+                     kScratchBytes / sizeof(uint4));
+  const hipError_t le = hipGetLastError();
+  if (le != hipSuccess) {
+    char msg[160];
+    snprintf(msg, sizeof msg, "clearing the static scratch: %s", hipGetErrorString(le));
+    return pa::fail_message(PA_ERR_HIP, msg);
+  }
+  return PA_OK;
+}
+
+// The scratch of the current device for a call whose counters start
+// `counters_from` bytes into it and whose slots end `parts` bytes into it:
+// its address (looked up and cleared on the device's first call; cleared
+// again if the counters would overlap slots earlier calls used; clears
+// enqueued on `stream`), or null with the error message set.
+void *device_scratch(hipStream_t stream, size_t counters_from, size_t parts, pa_status *st) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -51,7 +71,14 @@ void *device_scratch(hipStream_t stream, pa_status *st) {
     return nullptr;
   }
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_ptr[dev]) return g_ptr[dev];
+  if (g_ptr[dev]) {
+    if (counters_from < g_dirty[dev]) {
+      if ((*st = enqueue_clear(g_ptr[dev], stream)) != PA_OK) return nullptr;
+      g_dirty[dev] = 0;
+    }
+    if (parts > g_dirty[dev]) g_dirty[dev] = parts;
+    return g_ptr[dev];
+  }
   void *ptr = nullptr;
   const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
   if (e != hipSuccess || !ptr) {
@@ -61,16 +88,9 @@ void *device_scratch(hipStream_t stream, pa_status *st) {
     *st = pa::fail_message(PA_ERR_HIP, msg);
     return nullptr;
   }
-  hipLaunchKernelGGL(clear_scratch, dim3(256), dim3(256), 0, stream, static_cast<uint4 *>(ptr),
-                     kScratchBytes / sizeof(uint4));
-  const hipError_t le = hipGetLastError();
-  if (le != hipSuccess) {
-    char msg[160];
-    snprintf(msg, sizeof msg, "clearing the static scratch: %s", hipGetErrorString(le));
-    *st = pa::fail_message(PA_ERR_HIP, msg);
-    return nullptr;
-  }
+  if ((*st = enqueue_clear(ptr, stream)) != PA_OK) return nullptr;
   g_ptr[dev] = ptr;
+  g_dirty[dev] = parts;
   return ptr;
 }
 
@@ -87,8 +107,11 @@ pa_status pa_decode_static(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
     return pa::fail_message(PA_ERR_ARG, "opts->workspace must be NULL: this entry point uses the library's own scratch");
   // refuse requests past the scratch before anything touches a device
   const int64_t S = q.ndim == 3 ? q.shape[0] : 0, H = q.ndim == 3 ? q.shape[1] : 0, D = q.ndim == 3 ? q.shape[2] : 0;
+  const int32_t workers = opts ? opts->num_workers : 0;
+  size_t need = 0, parts = 0;
   if (S > 0 && H > 0 && num_kv_heads > 0 && H % num_kv_heads == 0) {
-    const size_t need = pa_decode_workspace_size(S, H, num_kv_heads, D, opts ? opts->num_workers : 0);
+    need = pa_decode_workspace_size(S, H, num_kv_heads, D, workers);
+    parts = pa::decode_partials_bytes(H, num_kv_heads, D, workers);
     if (need > kScratchBytes) {
       char msg[200];
       snprintf(msg, sizeof msg, "this decode needs %zu bytes of workspace; the static scratch holds %zu", need,
@@ -97,7 +120,9 @@ pa_status pa_decode_static(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
     }
   }
   pa_status st = PA_OK;
-  void *ws = device_scratch(static_cast<hipStream_t>(opts ? opts->stream : nullptr), &st);
+  // the counters take the array's last (need - parts) bytes
+  void *ws = device_scratch(static_cast<hipStream_t>(opts ? opts->stream : nullptr), kScratchBytes - (need - parts),
+                            parts, &st);
   if (!ws) return st;
   return pa::decode_with_workspace(out, q, k_cache, v_cache, block_tables, context_lens, block_size, scale,
                                    num_kv_heads, opts, ws, kScratchBytes);

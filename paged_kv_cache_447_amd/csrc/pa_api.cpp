@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "pa_internal.h"
+#include "pa_validate.h"
 
 namespace {
 
@@ -54,9 +55,9 @@ int kv_kind(int32_t dt) {
   return -1;
 }
 
-// rank, non-null data, contiguous last dimension, 16-byte alignment of the base
-// and of every outer stride (vector loads/stores address whole rows)
-// (an empty tensor may have a NULL data pointer)
+// rank, non-null data, non-negative strides, contiguous last dimension,
+// 16-byte alignment of the base and of every outer stride (vector loads/stores
+// address whole rows) (an empty tensor may have a NULL data pointer)
 pa_status check_tensor(const pa_tensor &t, const char *name, int ndim, bool need_rows_aligned) {
   if (t.ndim != ndim) return fail(PA_ERR_SHAPE, "%s: rank %d, expected %d", name, t.ndim, ndim);
   const int eb = elem_bytes(t.dtype);
@@ -68,6 +69,8 @@ pa_status check_tensor(const pa_tensor &t, const char *name, int ndim, bool need
   }
   if (empty) return PA_OK;
   if (!t.data) return fail(PA_ERR_NULL, "%s: data pointer is NULL", name);
+  for (int i = 0; i < ndim; ++i)
+    if (t.stride[i] < 0 && t.shape[i] > 1) return fail(PA_ERR_LAYOUT, "%s: negative stride in dim %d", name, i);
   if (t.stride[ndim - 1] != 1 && t.shape[ndim - 1] > 1)
     return fail(PA_ERR_LAYOUT, "%s: last dimension must be contiguous", name);
   if (need_rows_aligned) {
@@ -77,6 +80,24 @@ pa_status check_tensor(const pa_tensor &t, const char *name, int ndim, bool need
       if ((t.stride[i] * eb) % 16 && t.shape[i] > 1)
         return fail(PA_ERR_LAYOUT, "%s: stride of dim %d is not a multiple of 16 bytes", name, i);
   }
+  return PA_OK;
+}
+
+// The attention kernels address a row inside a block by a 32-bit byte offset
+// from the block's start: (block_size - 1) token strides plus one row must stay
+// below 4 GiB (a token-major view of a very large pool can exceed that).
+pa_status check_block_extent(const pa_tensor &c, const char *name) {
+  const int64_t eb = elem_bytes(c.dtype), st = c.stride[1];
+  if (c.shape[0] == 0 || c.shape[1] == 0) return PA_OK;
+  if (st >= ((int64_t)1 << 32) || ((c.shape[1] - 1) * st + c.shape[3]) * eb >= ((int64_t)1 << 32))
+    return fail(PA_ERR_LAYOUT, "%s: a block spans 4 GiB or more (token stride %lld elements)", name, (long long)st);
+  return PA_OK;
+}
+
+// opts->flags: PA_FLAG_VALIDATE or nothing
+pa_status check_flags(const pa_opts &o) {
+  if ((o.flags & ~PA_FLAG_VALIDATE) != 0 || o.reserved != 0)
+    return fail(PA_ERR_ARG, "flags: only PA_FLAG_VALIDATE is defined; reserved must be 0");
   return PA_OK;
 }
 
@@ -105,18 +126,30 @@ int32_t effective_workers(int32_t requested) {
   return (int32_t)(w > kMaxWorkers ? kMaxWorkers : w);
 }
 
+// The decode workspace: the partial-result slots from its start (the (max,
+// sum) pairs, then the outputs), the merge counters at its end.  A call
+// leaves its counters at zero and garbage in its slots; the slots' extent
+// depends only on the group size, head_dim and worker count, and the counters
+// sit past it whatever the batch, so calls with those three in common may
+// share a workspace whatever their number of sequences or layers: each
+// call's counters lie where earlier calls left zeros.
 struct WsLayout {
-  size_t counters, ml, acc, total;  // byte offsets and total size
+  size_t ml, acc, parts;  // byte offsets of the two slot regions, and where the slots end
+  size_t counters_bytes;  // the counters' region (at the end of the workspace)
+  size_t total;           // bytes needed
+  // the counters' offset in a workspace of `bytes` (>= total) bytes
+  size_t counters(size_t bytes) const { return bytes / 256 * 256 - counters_bytes; }
 };
 
 WsLayout workspace_layout(int64_t S, int64_t H, int64_t Hkv, int64_t D, int64_t W) {
   WsLayout l;
   const int64_t G = H / Hkv;
   const int64_t slots = 2 * W;
-  l.counters = 0;
-  l.ml = (size_t)round_up(S * Hkv * 4, 256);
-  l.acc = l.ml + (size_t)round_up(slots * G * 2 * 4, 256);
-  l.total = l.acc + (size_t)round_up(slots * G * D * 4, 256);
+  l.ml = 0;
+  l.acc = (size_t)round_up(slots * G * 2 * 4, 256);
+  l.parts = l.acc + (size_t)round_up(slots * G * D * 4, 256);
+  l.counters_bytes = (size_t)round_up(S * Hkv * 4, 256);
+  l.total = l.parts + l.counters_bytes;
   return l;
 }
 
@@ -251,8 +284,10 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   if (kvk != pa::KV_FP8) ks = vs = 1.0f;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
-  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((st = check_flags(o))) return st;
   if ((st = check_head_scale_args(o, kvk))) return st;
+  if ((st = check_block_extent(k_cache, "k_cache"))) return st;
+  if ((st = check_block_extent(v_cache, "v_cache"))) return st;
   const int64_t W = block_tables.shape[1];
   if (S > 65535 || num_kv_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "more than 65535 sequences or kv heads");
   if (W * block_size > (int64_t)1 << 30) return fail(PA_ERR_UNSUPPORTED, "table width too large");
@@ -275,7 +310,7 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
     return fail(PA_ERR_UNSUPPORTED, "too many work units");
   const int32_t nw = effective_workers(o.num_workers);
   const WsLayout ws = workspace_layout(layers * S, H, num_kv_heads, D, nw);
-  if (ws.total - ws.acc >= ((size_t)1 << 32))  // partial slots are addressed with 32-bit byte offsets
+  if (ws.parts - ws.acc >= ((size_t)1 << 32))  // partial slots are addressed with 32-bit byte offsets
     return fail(PA_ERR_UNSUPPORTED, "num_workers %d too large for this head shape", nw);
   if (!o.workspace || o.workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws.total,
@@ -300,6 +335,19 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
     if (ap->slot_mapping.shape[0] != S) return fail(PA_ERR_SHAPE, "slot_mapping must have one entry per sequence");
     if (layers != 1) return fail(PA_ERR_UNSUPPORTED, "the fused step takes one layer");
   }
+  if (o.flags & PA_FLAG_VALIDATE) {
+    const hipStream_t stream = static_cast<hipStream_t>(o.stream);
+    pa::HostInts bt, lens, slots;
+    if ((st = pa::validation_allowed(stream))) return st;
+    if ((st = bt.fetch(block_tables, "block_tables", stream))) return st;
+    if ((st = lens.fetch(context_lens, "context_lens", stream))) return st;
+    if ((st = pa::check_tables(bt, lens, block_size, NB))) return st;
+    if (ap) {
+      if ((st = slots.fetch(ap->slot_mapping, "slot_mapping", stream))) return st;
+      if ((st = pa::check_new_token_slots(slots, bt, lens, block_size, NB * block_size))) return st;
+    }
+    if ((st = pa::check_head_scales(khs, vhs, layers * num_kv_heads, stream))) return st;
+  }
 
   pa::DecodeArgs a;
   std::memset(&a, 0, sizeof a);
@@ -310,11 +358,11 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   a.block_tables = static_cast<const int32_t *>(block_tables.data);
   a.context_lens = static_cast<const int32_t *>(context_lens.data);
   char *wsb = static_cast<char *>(o.workspace);
-  a.counters = reinterpret_cast<int32_t *>(wsb + ws.counters);
+  a.counters = reinterpret_cast<int32_t *>(wsb + ws.counters(o.workspace_bytes));
   a.part_ml = reinterpret_cast<float *>(wsb + ws.ml);
   a.part_acc = reinterpret_cast<float *>(wsb + ws.acc);
   a.ml_bytes = (uint32_t)(ws.acc - ws.ml);
-  a.acc_bytes = (uint32_t)(ws.total - ws.acc);
+  a.acc_bytes = (uint32_t)(ws.parts - ws.acc);
   a.q_ss = q.stride[0];
   a.q_sh = q.stride[1];
   a.o_ss = out.stride[0];
@@ -369,6 +417,13 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
 }  // namespace
 
 namespace pa {
+// Bytes at the start of a decode workspace that a call with this head shape
+// and worker request may leave non-zero (its partial-result slots).
+size_t decode_partials_bytes(int64_t num_heads, int64_t num_kv_heads, int64_t head_dim, int32_t num_workers) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_heads % num_kv_heads) return 0;
+  return workspace_layout(1, num_heads, num_kv_heads, head_dim, effective_workers(num_workers)).parts;
+}
+
 // pa_decode on a workspace the library provides (opts->workspace must be
 // NULL): the entry point for callers that cannot allocate.
 pa_status decode_with_workspace(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_cache,
@@ -489,8 +544,10 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   if (!pa::prefill_supported(kv_kind(k_cache.dtype), (int)D))
     return fail(PA_ERR_UNSUPPORTED, "no prefill kernel for head_dim %lld (built: 64, 128)", (long long)D);
   if (!(scale > 0.0f) || !std::isfinite(scale)) return fail(PA_ERR_ARG, "scale must be finite and > 0");
-  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((st = check_flags(o))) return st;
   if ((st = check_head_scale_args(o, kv_kind(k_cache.dtype)))) return st;
+  if ((st = check_block_extent(k_cache, "k_cache"))) return st;
+  if ((st = check_block_extent(v_cache, "v_cache"))) return st;
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (k_cache.dtype != PA_FP8_E4M3) ks = vs = 1.0f;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
@@ -549,6 +606,17 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
     a.pair_counter = static_cast<int32_t *>(o.workspace);
   }
+  if (o.flags & PA_FLAG_VALIDATE) {
+    const hipStream_t stream = static_cast<hipStream_t>(o.stream);
+    pa::HostInts bt, lens, qsl;
+    if ((st = pa::validation_allowed(stream))) return st;
+    if ((st = bt.fetch(block_tables, "block_tables", stream))) return st;
+    if ((st = lens.fetch(context_lens, "context_lens", stream))) return st;
+    if ((st = qsl.fetch(query_start_loc, "query_start_loc", stream))) return st;
+    if ((st = pa::check_tables(bt, lens, block_size, NB))) return st;
+    if ((st = pa::check_query_starts(qsl, lens, N))) return st;
+    if ((st = pa::check_head_scales(a.k_head_scale, a.v_head_scale, num_kv_heads, stream))) return st;
+  }
   a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)ks);
   a.v_scale = vs;
   a.kv_kind = kv_kind(k_cache.dtype);
@@ -594,11 +662,19 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   float ks = o.k_scale == 0.0f ? 1.0f : o.k_scale, vs = o.v_scale == 0.0f ? 1.0f : o.v_scale;
   if (!(ks > 0.0f) || !std::isfinite(ks) || !(vs > 0.0f) || !std::isfinite(vs))
     return fail(PA_ERR_ARG, "k_scale / v_scale must be finite and > 0");
-  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((st = check_flags(o))) return st;
   if ((st = check_head_scale_args(o, ck))) return st;
   if (N == 0 || Hkv == 0 || D == 0) return PA_OK;
   const float *khs = nullptr, *vhs = nullptr;
   if ((st = head_scales(o, ck, &khs, &vhs))) return st;
+  if (o.flags & PA_FLAG_VALIDATE) {
+    const hipStream_t stream = static_cast<hipStream_t>(o.stream);
+    pa::HostInts slots;
+    if ((st = pa::validation_allowed(stream))) return st;
+    if ((st = slots.fetch(slot_mapping, "slot_mapping", stream))) return st;
+    if ((st = pa::check_distinct_slots(slots, k_cache.shape[0] * k_cache.shape[1]))) return st;
+    if (ik != pa::KV_FP8 && (st = pa::check_head_scales(khs, vhs, Hkv, stream))) return st;
+  }
 
   pa::CacheWriteArgs a;
   std::memset(&a, 0, sizeof a);
@@ -663,7 +739,7 @@ pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor
     return fail(PA_ERR_SHAPE, "K and V pools of one side must have the same number of blocks");
   if (dst_k_cache.stride[0] != dst_v_cache.stride[0] || src_k_cache.stride[0] != src_v_cache.stride[0])
     return fail(PA_ERR_LAYOUT, "K and V pools of one side must have the same block stride");
-  if (o.flags != 0 || o.reserved != 0) return fail(PA_ERR_ARG, "flags must be 0");
+  if ((st = check_flags(o))) return st;
   const int64_t M = block_mapping.shape[0];
   const int64_t block_bytes = src_k_cache.shape[1] * src_k_cache.shape[2] * src_k_cache.shape[3] * eb;
   if (M == 0 || block_bytes == 0 || src_k_cache.shape[0] == 0 || dst_k_cache.shape[0] == 0) return PA_OK;
@@ -680,6 +756,14 @@ pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor
   const char *pnames[5] = {"dst_k_cache", "dst_v_cache", "src_k_cache", "src_v_cache", "block_mapping"};
   for (int i = 0; i < 5; ++i)
     if ((st = device_address(ptrs[i], pnames[i], &dev[i]))) return st;
+  if (o.flags & PA_FLAG_VALIDATE) {
+    const hipStream_t stream = static_cast<hipStream_t>(o.stream);
+    pa::HostInts pairs;
+    if ((st = pa::validation_allowed(stream))) return st;
+    if ((st = pairs.fetch(block_mapping, "block_mapping", stream))) return st;
+    const bool same_pool = dst_k_cache.data == src_k_cache.data || dst_v_cache.data == src_v_cache.data;
+    if ((st = pa::check_block_pairs(pairs, src_k_cache.shape[0], dst_k_cache.shape[0], same_pool))) return st;
+  }
   a.dst_k = static_cast<char *>(dev[0]);
   a.dst_v = static_cast<char *>(dev[1]);
   a.src_k = static_cast<const char *>(dev[2]);
@@ -710,6 +794,7 @@ const char *pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_ARG: return "argument out of range";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_BAD_INDEX: return "index or scale entry out of range";
   }
   return "unknown status";
 }

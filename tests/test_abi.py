@@ -168,7 +168,7 @@ def test_decode_argument_errors(lib):
     o.partition_size = 24  # not a multiple of 16
     expect(lib, call_decode(lib, good_decode(), o), -7, "partition")
     o = with_workspace()
-    o.flags = 1
+    o.flags = 2  # bit 0 is PA_FLAG_VALIDATE; the others are reserved
     expect(lib, call_decode(lib, good_decode(), o), -7, "flags")
     o = with_workspace()
     o.num_workers = -4
@@ -180,7 +180,7 @@ def test_decode_workspace_errors(lib):
     expect(lib, call_decode(lib, good_decode(), o), -6, "workspace")
     o.num_workers = 64
     need = lib.pa_decode_workspace_size(4, 8, 2, 128, 64)
-    # counters (4 seqs x 2 kv heads), then 2 slots per worker of G=4 heads x (2 + 128) floats,
+    # 2 slots per worker of G=4 heads x (2 + 128) floats, then the counters (4 seqs x 2 kv heads),
     # each region rounded up to 256 bytes
     assert need == 256 + 2 * 64 * 4 * 2 * 4 + 2 * 64 * 4 * 128 * 4
     o.workspace = FAKE
@@ -260,7 +260,7 @@ def test_prefill_errors(lib):
     expect(lib, call_prefill(lib, good_prefill(), scale=0.0), -7, "scale")
     expect(lib, call_prefill(lib, good_prefill(), scale=float("nan")), -7, "scale")
     o = pa.PaOpts()
-    o.flags = 1
+    o.flags = 2
     expect(lib, call_prefill(lib, good_prefill(), opts=o), -7, "flags")
     a = good_prefill()
     a[1] = T([40, 8, 128], pa.PA_F16, data=0)
@@ -415,3 +415,74 @@ def test_decode_append_host_checks(lib):
     f8 = good_decode(kv=pa.PA_FP8_E4M3)
     expect(lib, call(f8, T([4, 2, 128], pa.PA_FP8_E4M3), T([4, 2, 128], pa.PA_FP8_E4M3), sm), -5, "fp8")
     expect(lib, call(a, kn, vn, sm, pa.PaOpts()), -6, "workspace")  # the decode's own checks still apply
+
+
+def test_negative_strides_refused(lib):
+    """A negative stride (of a dimension longer than 1) is refused on every tensor."""
+    a = good_decode()
+    a["k"] = T([64, 16, 2, 128], pa.PA_F16, strides=[16 * 2 * 128, -2 * 128, 128, 1])
+    expect(lib, call_decode(lib, a), -4, "negative stride")
+    a = good_decode()
+    a["q"] = T([4, 8, 128], pa.PA_F16, strides=[-8 * 128, 128, 1])
+    expect(lib, call_decode(lib, a), -4, "negative stride")
+    a = good_prefill()
+    a[3] = T([64, 16, 2, 128], pa.PA_F16, strides=[-16 * 2 * 128, 2 * 128, 128, 1])
+    expect(lib, call_prefill(lib, a), -4, "negative stride")
+    a = good_write()
+    a[0] = T([4, 2, 128], pa.PA_F16, strides=[2 * 128, -128, 1])
+    expect(lib, call_write(lib, a), -4, "negative stride")
+    # a size-1 dimension's stride is never used: any value passes
+    a = good_decode(S=1)
+    a["q"] = T([1, 8, 128], pa.PA_F16, strides=[-5, 128, 1])
+    a["out"] = T([1, 8, 128], pa.PA_F16, strides=[-5, 128, 1])
+    assert call_decode(lib, a) != -4
+
+
+def test_block_extent_limit(lib):
+    """Rows inside a block are addressed by a 32-bit byte offset: a token
+    stride that makes (block_size - 1) strides plus one row reach 4 GiB is
+    refused for decode and prefill, K and V (a token-major view of a pool of
+    more than ~140k blocks at 2 kv heads x 128 dims, f16, block 16)."""
+    bs, D, eb = 16, 128, 2
+    over = 143165576  # elements, a multiple of 8 (16 bytes): (15 * over + 128) * 2 >= 2^32
+    under = over - 16  # (15 * under + 128) * 2 < 2^32
+    assert ((bs - 1) * over + D) * eb >= 1 << 32 > ((bs - 1) * under + D) * eb
+
+    def cache(st):
+        return T([64, bs, 2, D], pa.PA_F16, strides=[bs * st, st, D, 1])
+
+    for key in ("k", "v"):
+        a = good_decode()
+        a[key] = cache(over)
+        if key == "k":
+            a["v"] = cache(over)  # shapes agree; only k is checked first
+        expect(lib, call_decode(lib, a), -4, "4 GiB")
+        a = good_decode()
+        a[key] = cache(under)
+        assert call_decode(lib, a) != -4, lib.pa_last_error()
+    a = good_prefill()
+    a[2] = cache(over)
+    expect(lib, call_prefill(lib, a), -4, "4 GiB")
+    a = good_prefill()
+    a[3] = cache(over)
+    expect(lib, call_prefill(lib, a), -4, "4 GiB")
+
+
+def test_validate_flag_reaches_the_copy(lib):
+    """PA_FLAG_VALIDATE is accepted by every operation: the call passes its
+    argument checks and stops only where it first needs the device (no
+    device here), never with PA_ERR_ARG; unknown flag bits are refused."""
+    o = with_workspace()
+    o.flags = pa.PA_FLAG_VALIDATE
+    expect(lib, call_decode(lib, good_decode(), o), -8, "PA_FLAG_VALIDATE")
+    p = pa.PaOpts()
+    p.flags = pa.PA_FLAG_VALIDATE
+    expect(lib, call_prefill(lib, good_prefill(), opts=p), -8, "PA_FLAG_VALIDATE")
+    w = pa.PaOpts()
+    w.flags = pa.PA_FLAG_VALIDATE
+    expect(lib, call_write(lib, good_write(), w), -8, "PA_FLAG_VALIDATE")
+    for bad in (2, 4, 1 << 31, pa.PA_FLAG_VALIDATE | 8):
+        w = pa.PaOpts()
+        w.flags = bad
+        expect(lib, call_write(lib, good_write(), w), -7, "flags")
+    assert lib.pa_status_string(-9) == b"index or scale entry out of range"

@@ -163,7 +163,6 @@ def test_layers_step_replays_in_a_graph(case):
     with torch.cuda.graph(g):
         step(out)
     torch.cuda.synchronize()
-    n_counters = 4 * L * cfg.num_seqs * cfg.num_kv_heads
     for r in range(REPLAYS):
         use_a = r % 2 == 0
         inp["q"].copy_(q_a if use_a else q_b)
@@ -171,7 +170,7 @@ def test_layers_step_replays_in_a_graph(case):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref_a if use_a else ref_b), f"replay {r} differs from the eager call"
-        assert int(ws[:n_counters].view(torch.int32).abs().sum()) == 0
+        assert_counters_zero(ws, L * cfg.num_seqs, cfg.num_kv_heads)
         eager = step(torch.empty_like(q_a))
         torch.cuda.synchronize()
         assert torch.equal(eager, ref_a if use_a else ref_b)

@@ -11,6 +11,7 @@ import paged_kv_cache_447_amd as pa
 from pa_workloads import get_config, make_layout, scaled
 from pa_workloads.layers import LAYER_CONFIGS, LayerConfig, flat_slots, make_layer_inputs
 from tests.gpu_common import NTHREADS, TOL_F32, TOL_OUT, host_inputs, log, max_abs_err
+from tests.test_gpu_parity import assert_counters_zero
 
 pytestmark = pytest.mark.gpu
 
@@ -84,7 +85,7 @@ def test_small_layer_steps_match_oracle(case, split):
     log(f"    err={err:.3e} err32={err32:.3e}")
     assert err <= TOL_OUT[cfg.kv_dtype]
     assert err32 <= TOL_F32[cfg.kv_dtype]
-    assert int(ws[: 4 * lcfg.num_layers * cfg.num_seqs * cfg.num_kv_heads].view(torch.int32).abs().sum()) == 0
+    assert_counters_zero(ws, lcfg.num_layers * cfg.num_seqs, cfg.num_kv_heads)
 
 
 @pytest.mark.parametrize("name", sorted(LAYER_CONFIGS))

@@ -1,9 +1,11 @@
 """pa_decode_static, the decode entry point for callers that cannot allocate
 (its workspace is a per-device array inside the library), against pa_decode on
 a caller workspace: the same kernels on the same split, so the outputs must be
-identical bit for bit.  Two calls in a row, the second on a smaller batch of
-another shape, check that what the first call leaves in the shared array does
-not reach the second; each is also held to the oracle's tolerance."""
+identical bit for bit.  Calls in a row on the shared array -- a smaller batch
+of another head shape after a larger one, then a larger batch of the same
+shape (its merge counters reach further into the array), then the first head
+shape again on the largest batch -- check that what one call leaves in the
+array never reaches the next; each is also held to the oracle's tolerance."""
 
 import pytest
 import torch
@@ -25,10 +27,14 @@ def _static(cfg, inp, out_dtype):
     return out
 
 
-def test_static_scratch_matches_caller_workspace_on_two_calls():
-    first = scaled(get_config("gqa70b"), num_seqs=40)          # grouped heads, matrix-core kernel
-    second = scaled(get_config("llama7b"), num_seqs=6, num_blocks=800)  # fewer items, vector kernel
-    for name, cfg in (("first (gqa70b x40)", first), ("second (llama7b x6)", second)):
+def test_static_scratch_matches_caller_workspace_on_calls_in_a_row():
+    calls = (
+        ("first (gqa70b x40)", scaled(get_config("gqa70b"), num_seqs=40)),  # grouped heads, matrix-core kernel
+        ("second (llama7b x6)", scaled(get_config("llama7b"), num_seqs=6, num_blocks=800)),  # fewer items, vector kernel
+        ("third (llama7b x32)", get_config("llama7b")),  # same head shape, more counters than the second
+        ("fourth (gqa70b x128)", get_config("gqa70b")),  # back to grouped heads, the largest batch
+    )
+    for name, cfg in calls:
         log(f"[no-alloc {name}]")
         layout, inp = setup(cfg)
         host = host_inputs(inp)
