@@ -60,13 +60,13 @@ def _load():
             i64, i32, vp, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_double
             lib.oracle_paged_decode.restype = i32
             lib.oracle_paged_decode.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp] + [i64] * 7 + [dbl] * 3 + \
-                [vp, vp, i32]
+                [vp, vp, vp, vp, i32]
             lib.oracle_paged_prefill.restype = i32
             lib.oracle_paged_prefill.argtypes = [vp, vp, i32, vp, vp, i32, vp, vp, vp] + [i64] * 7 + [dbl] * 3 + \
-                [vp, vp, i32]
+                [vp, vp, vp, vp, i32]
             lib.oracle_cache_write.restype = i32
             lib.oracle_cache_write.argtypes = [vp, vp, i32, vp, vp, i32, vp] + [i64] * 5 + [ctypes.c_float] * 2 + \
-                [vp, vp]
+                [vp, vp, vp, vp]
             lib.oracle_f16_to_double.restype = dbl
             lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
             lib.oracle_bf16_to_double.restype = dbl
@@ -101,17 +101,27 @@ def _host(t, dtype=None):
     return t.contiguous()
 
 
-def _scales(k_scale, v_scale, count: int, dtype):
-    """(per-tensor k, per-tensor v, per-head k array or None, per-head v array
-    or None): scalars are per-tensor fp8 scales, sequences of ``count`` values
-    one scale per kv head."""
+def _scales(k_scale, v_scale, count: int, dtype, num_blocks: int = 0):
+    """(per-tensor k, per-tensor v, per-head k, per-head v, per-block k,
+    per-block v): scalars are per-tensor fp8 scales, sequences of ``count``
+    values one scale per kv head, [num_blocks, count] arrays one scale per
+    (physical block, kv head); the arrays not given are None."""
     if np.ndim(k_scale) == 0 and np.ndim(v_scale) == 0:
-        return float(k_scale), float(v_scale), None, None
-    ka = np.ascontiguousarray(np.asarray(_host_array(k_scale), dtype=dtype).reshape(-1))
-    va = np.ascontiguousarray(np.asarray(_host_array(v_scale), dtype=dtype).reshape(-1))
+        return float(k_scale), float(v_scale), None, None, None, None
+    ka = np.ascontiguousarray(np.asarray(_host_array(k_scale), dtype=dtype))
+    va = np.ascontiguousarray(np.asarray(_host_array(v_scale), dtype=dtype))
+    if ka.ndim == 2 or va.ndim == 2:
+        if ka.shape != (num_blocks, count) or va.shape != (num_blocks, count):
+            raise ValueError(f"per-block scales need [{num_blocks}, {count}] values each")
+        return 1.0, 1.0, None, None, ka, va
+    ka, va = ka.reshape(-1), va.reshape(-1)
     if ka.shape[0] != count or va.shape[0] != count:
         raise ValueError(f"per-head scales need {count} values each")
-    return 1.0, 1.0, ka, va
+    return 1.0, 1.0, ka, va, None, None
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
 
 
 def _host_array(x):
@@ -124,8 +134,9 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
                  k_scale=1.0, v_scale=1.0, nthreads: int = 1) -> np.ndarray:
     """Reference decode; returns float64 [num_seqs, num_heads, head_dim].
 
-    ``k_scale`` / ``v_scale`` (fp8 caches): one scale per tensor, or a
-    sequence of num_kv_heads scales, one per kv head."""
+    ``k_scale`` / ``v_scale`` (fp8 caches): one scale per tensor, a sequence
+    of num_kv_heads scales (one per kv head), or a [num_blocks, num_kv_heads]
+    array (one per physical block and kv head)."""
     import torch
 
     lib = _load()
@@ -139,12 +150,11 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, 
     if k_cache.dtype != v_cache.dtype:
         raise ValueError("k_cache and v_cache dtypes differ")
     W = bt.shape[1] if bt.dim() == 2 else 0
-    ks, vs, kh, vh = _scales(k_scale, v_scale, Hkv, np.float64)
+    ks, vs, kh, vh, kb, vb = _scales(k_scale, v_scale, Hkv, np.float64, NB)
     out = np.empty((S, H, D), dtype=np.float64)
     rc = lib.oracle_paged_decode(out.ctypes.data, q.data_ptr(), _code(q), k_cache.data_ptr(), v_cache.data_ptr(),
                                  _code(k_cache), bt.data_ptr(), cl.data_ptr(), S, H, Hkv, D, NB, bs, W,
-                                 float(scale), ks, vs, None if kh is None else kh.ctypes.data,
-                                 None if vh is None else vh.ctypes.data, int(nthreads))
+                                 float(scale), ks, vs, _ptr(kh), _ptr(vh), _ptr(kb), _ptr(vb), int(nthreads))
     if rc != 0:
         raise OracleError(f"oracle_paged_decode: {STATUS.get(rc, rc)}")
     return out
@@ -164,9 +174,11 @@ def paged_decode_layers(q, k_caches, v_caches, block_tables, context_lens, scale
     if k_caches.shape[0] != L or v_caches.shape[0] != L:
         raise ValueError("q, k_caches and v_caches must have the same number of layers")
     per_head = np.ndim(k_scale) > 0
-    if per_head:  # [L, num_kv_heads]: layer l's row
-        k_scale = np.asarray(_host_array(k_scale), dtype=np.float64).reshape(L, num_kv_heads)
-        v_scale = np.asarray(_host_array(v_scale), dtype=np.float64).reshape(L, num_kv_heads)
+    if per_head:  # [L, num_kv_heads] or [L, num_blocks, num_kv_heads]: layer l's part
+        k_scale = np.asarray(_host_array(k_scale), dtype=np.float64)
+        v_scale = np.asarray(_host_array(v_scale), dtype=np.float64)
+        if k_scale.ndim != 3:
+            k_scale, v_scale = k_scale.reshape(L, num_kv_heads), v_scale.reshape(L, num_kv_heads)
     return np.stack([paged_decode(q[l], k_caches[l], v_caches[l], block_tables, context_lens, scale, num_kv_heads,
                                   k_scale[l] if per_head else k_scale, v_scale[l] if per_head else v_scale,
                                   nthreads) for l in range(L)]) if L else \
@@ -195,12 +207,12 @@ def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start_l
     if qsl.shape[0] != S + 1 or int(qsl[-1]) != N:
         raise ValueError("query_start_loc must have num_seqs + 1 entries ending at the query row count")
     W = bt.shape[1] if bt.dim() == 2 else 0
-    ks, vs, kh, vh = _scales(k_scale, v_scale, Hkv, np.float64)
+    ks, vs, kh, vh, kb, vb = _scales(k_scale, v_scale, Hkv, np.float64, NB)
     out = np.empty((N, H, D), dtype=np.float64)
     rc = lib.oracle_paged_prefill(out.ctypes.data, q.data_ptr(), _code(q), k_cache.data_ptr(), v_cache.data_ptr(),
                                   _code(k_cache), bt.data_ptr(), cl.data_ptr(), qsl.data_ptr(), S, H, Hkv, D, NB,
-                                  bs, W, float(scale), ks, vs, None if kh is None else kh.ctypes.data,
-                                  None if vh is None else vh.ctypes.data, int(nthreads))
+                                  bs, W, float(scale), ks, vs, _ptr(kh), _ptr(vh), _ptr(kb), _ptr(vb),
+                                  int(nthreads))
     if rc != 0:
         raise OracleError(f"oracle_paged_prefill: {STATUS.get(rc, rc)}")
     return out
@@ -225,10 +237,9 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0,
     sm = _host(slot_mapping, torch.int64)
     N, Hkv, D = k.shape
     NB, bs = kc.shape[0], kc.shape[1]
-    ks, vs, kh, vh = _scales(k_scale, v_scale, Hkv, np.float32)
+    ks, vs, kh, vh, kb, vb = _scales(k_scale, v_scale, Hkv, np.float32, NB)
     rc = lib.oracle_cache_write(k.data_ptr(), v.data_ptr(), _code(k), kc.data_ptr(), vc.data_ptr(), _code(kc),
-                                sm.data_ptr(), N, Hkv, D, NB, bs, ks, vs, None if kh is None else kh.ctypes.data,
-                                None if vh is None else vh.ctypes.data)
+                                sm.data_ptr(), N, Hkv, D, NB, bs, ks, vs, _ptr(kh), _ptr(vh), _ptr(kb), _ptr(vb))
     if rc != 0:
         raise OracleError(f"oracle_cache_write: {STATUS.get(rc, rc)}")
     return kc, vc

@@ -26,7 +26,10 @@
  *     one fp32 scale per tensor (page "大模型推理KV Cache内存管理与PagedAttention分页
  *     显存实战", closing paragraph on FP8 KV caches), or one per kv head: the
  *     scale of the head the element belongs to (precision set per attention
- *     head, page "vLLM框架中的KV cache优化与PagedAttention机制详解", section 8.2).
+ *     head, page "vLLM框架中的KV cache优化与PagedAttention机制详解", section 8.2), or
+ *     one per (physical block, kv head): the scale of the block that holds the
+ *     token, for that head (the finer grain of the same section's per-head
+ *     precision: a block's tokens share one scale, like a page's contents).
  *   - The cache write puts the K/V row of new token n at slot_mapping[n], slot
  *     = block * block_size + offset, and skips negative slots.
  *   - Prefill (several query tokens per sequence): the query rows of sequence
@@ -168,6 +171,7 @@ typedef struct {
   int64_t num_seqs, num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks;
   double scale, k_scale, v_scale;
   const double *k_heads, *v_heads; /* fp8: one scale per kv head instead of k_scale / v_scale, or NULL */
+  const double *k_blocks, *v_blocks; /* fp8: one scale per (block, kv head) [num_blocks][num_kv_heads], or NULL */
   /* work distribution */
   int64_t next_item;
   pthread_mutex_t lock;
@@ -198,9 +202,11 @@ static int decode_item(decode_job *J, int64_t seq, int64_t kvh, double *Kc, doub
     int64_t off = t % bs;
     if (blk < 0 || blk >= J->num_blocks) return ORC_BAD_BLOCK;
     int64_t row = ((blk * bs + off) * Hkv + kvh) * D;
+    const double kst = J->k_blocks ? J->k_blocks[blk * Hkv + kvh] : ks;
+    const double vst = J->v_blocks ? J->v_blocks[blk * Hkv + kvh] : vs;
     for (int64_t d = 0; d < D; ++d) {
-      Kc[t * D + d] = load_elem(J->k_cache, J->kv_dtype, row + d) * ks;
-      Vc[t * D + d] = load_elem(J->v_cache, J->kv_dtype, row + d) * vs;
+      Kc[t * D + d] = load_elem(J->k_cache, J->kv_dtype, row + d) * kst;
+      Vc[t * D + d] = load_elem(J->v_cache, J->kv_dtype, row + d) * vst;
     }
   }
 
@@ -265,7 +271,7 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
                         int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads, int64_t head_dim,
                         int64_t num_blocks, int64_t block_size, int64_t max_blocks_per_seq, double scale,
                         double k_scale, double v_scale, const double *k_head_scale, const double *v_head_scale,
-                        int nthreads) {
+                        const double *k_block_scale, const double *v_block_scale, int nthreads) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return ORC_BAD_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0)
@@ -292,8 +298,11 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
   J.k_scale = k_scale;
   J.v_scale = v_scale;
   if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
+  if ((k_block_scale == NULL) != (v_block_scale == NULL) || (k_head_scale && k_block_scale)) return ORC_BAD_ARG;
   J.k_heads = k_head_scale;
   J.v_heads = v_head_scale;
+  J.k_blocks = k_block_scale;
+  J.v_blocks = v_block_scale;
   J.status = ORC_OK;
   pthread_mutex_init(&J.lock, NULL);
   if (nthreads < 1) nthreads = 1;
@@ -326,6 +335,7 @@ typedef struct {
   int64_t num_seqs, num_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks;
   double scale, k_scale, v_scale;
   const double *k_heads, *v_heads; /* fp8: one scale per kv head instead of k_scale / v_scale, or NULL */
+  const double *k_blocks, *v_blocks; /* fp8: one scale per (block, kv head) [num_blocks][num_kv_heads], or NULL */
   int64_t next_item;
   pthread_mutex_t lock;
   int status;
@@ -352,9 +362,11 @@ static int prefill_item(prefill_job *J, int64_t seq, int64_t kvh, double *Kc, do
     const int64_t blk = J->block_tables[seq * J->max_blocks + t / bs];
     if (blk < 0 || blk >= J->num_blocks) return ORC_BAD_BLOCK;
     const int64_t src = ((blk * bs + t % bs) * Hkv + kvh) * D;
+    const double kst = J->k_blocks ? J->k_blocks[blk * Hkv + kvh] : ks;
+    const double vst = J->v_blocks ? J->v_blocks[blk * Hkv + kvh] : vs;
     for (int64_t d = 0; d < D; ++d) {
-      Kc[t * D + d] = load_elem(J->k_cache, J->kv_dtype, src + d) * ks;
-      Vc[t * D + d] = load_elem(J->v_cache, J->kv_dtype, src + d) * vs;
+      Kc[t * D + d] = load_elem(J->k_cache, J->kv_dtype, src + d) * kst;
+      Vc[t * D + d] = load_elem(J->v_cache, J->kv_dtype, src + d) * vst;
     }
   }
   for (int64_t j = 0; j < nq; ++j) {
@@ -419,7 +431,8 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
                          const int32_t *query_start_loc, int64_t num_seqs, int64_t num_heads,
                          int64_t num_kv_heads, int64_t head_dim, int64_t num_blocks, int64_t block_size,
                          int64_t max_blocks_per_seq, double scale, double k_scale, double v_scale,
-                         const double *k_head_scale, const double *v_head_scale, int nthreads) {
+                         const double *k_head_scale, const double *v_head_scale, const double *k_block_scale,
+                         const double *v_block_scale, int nthreads) {
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc) return ORC_BAD_ARG;
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
       num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0)
@@ -450,8 +463,11 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
   J.k_scale = k_scale;
   J.v_scale = v_scale;
   if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
+  if ((k_block_scale == NULL) != (v_block_scale == NULL) || (k_head_scale && k_block_scale)) return ORC_BAD_ARG;
   J.k_heads = k_head_scale;
   J.v_heads = v_head_scale;
+  J.k_blocks = k_block_scale;
+  J.v_blocks = v_block_scale;
   J.status = ORC_OK;
   pthread_mutex_init(&J.lock, NULL);
   if (nthreads < 1) nthreads = 1;
@@ -478,13 +494,16 @@ int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_
  * cache_dtype.  Same dtype: the bytes are copied.  fp8 cache: each element is
  * converted to fp32, divided in fp32 by its scale -- the tensor's fp32 scale,
  * or its kv head's when k_head_scale / v_head_scale ([num_kv_heads]) are
- * given -- and encoded with oracle_float_to_fp8.  Validates every slot before
- * writing anything. */
+ * given, or its (destination block, kv head)'s when k_block_scale /
+ * v_block_scale ([num_blocks][num_kv_heads]) are -- and encoded with
+ * oracle_float_to_fp8.  Validates every slot before writing anything. */
 int oracle_cache_write(const void *k, const void *v, int in_dtype, void *k_cache, void *v_cache, int cache_dtype,
                        const int64_t *slot_mapping, int64_t num_tokens, int64_t num_kv_heads, int64_t head_dim,
                        int64_t num_blocks, int64_t block_size, float k_scale, float v_scale,
-                       const float *k_head_scale, const float *v_head_scale) {
+                       const float *k_head_scale, const float *v_head_scale, const float *k_block_scale,
+                       const float *v_block_scale) {
   if ((k_head_scale == NULL) != (v_head_scale == NULL)) return ORC_BAD_ARG;
+  if ((k_block_scale == NULL) != (v_block_scale == NULL) || (k_head_scale && k_block_scale)) return ORC_BAD_ARG;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return ORC_BAD_ARG;
   if (!elem_size(in_dtype) || !elem_size(cache_dtype)) return ORC_BAD_ARG;
   if (in_dtype != cache_dtype && !(cache_dtype == ORC_FP8 && in_dtype != ORC_FP8)) return ORC_BAD_ARG;
@@ -506,11 +525,13 @@ int oracle_cache_write(const void *k, const void *v, int in_dtype, void *k_cache
       const void *src = which ? v : k;
       char *cache = (char *)(which ? v_cache : k_cache);
       const float *heads = which ? v_head_scale : k_head_scale;
+      const float *blocks = which ? v_block_scale : k_block_scale; /* the scales of block blk's heads */
       if (in_dtype == cache_dtype) {
         memcpy(cache + dst * es_c, (const char *)src + n * row * es_in, (size_t)(row * es_c));
       } else {
         for (int64_t i = 0; i < row; ++i) {
-          const float sc = heads ? heads[i / head_dim] : (which ? v_scale : k_scale);
+          const float sc = blocks ? blocks[blk * num_kv_heads + i / head_dim]
+                                  : (heads ? heads[i / head_dim] : (which ? v_scale : k_scale));
           float x = (float)load_elem(src, in_dtype, n * row + i);
           ((uint8_t *)cache)[dst + i] = oracle_float_to_fp8(x / sc);
         }

@@ -21,17 +21,20 @@ int oracle_paged_decode(double *out, const void *q, int q_dtype, const void *k_c
                         int kv_dtype, const int32_t *block_tables, const int32_t *context_lens, int64_t num_seqs,
                         int64_t num_heads, int64_t num_kv_heads, int64_t head_dim, int64_t num_blocks,
                         int64_t block_size, int64_t max_blocks_per_seq, double scale, double k_scale, double v_scale,
-                        const double *k_head_scale, const double *v_head_scale, int nthreads);
+                        const double *k_head_scale, const double *v_head_scale, const double *k_block_scale,
+                        const double *v_block_scale, int nthreads);
 int oracle_paged_prefill(double *out, const void *q, int q_dtype, const void *k_cache, const void *v_cache,
                          int kv_dtype, const int32_t *block_tables, const int32_t *context_lens,
                          const int32_t *query_start_loc, int64_t num_seqs, int64_t num_heads, int64_t num_kv_heads,
                          int64_t head_dim, int64_t num_blocks, int64_t block_size, int64_t max_blocks_per_seq,
                          double scale, double k_scale, double v_scale, const double *k_head_scale,
-                         const double *v_head_scale, int nthreads);
+                         const double *v_head_scale, const double *k_block_scale, const double *v_block_scale,
+                         int nthreads);
 int oracle_cache_write(const void *k, const void *v, int in_dtype, void *k_cache, void *v_cache, int cache_dtype,
                        const int64_t *slot_mapping, int64_t num_tokens, int64_t num_kv_heads, int64_t head_dim,
                        int64_t num_blocks, int64_t block_size, float k_scale, float v_scale,
-                       const float *k_head_scale, const float *v_head_scale);
+                       const float *k_head_scale, const float *v_head_scale, const float *k_block_scale,
+                       const float *v_block_scale);
 
 static int fails = 0;
 #define EXPECT(c)                                                          \
@@ -120,11 +123,29 @@ static void attention(int kv_dt, int q_dt, int heads_per_kv) {
   double ks[2] = {0.5, 0.25}, vs[2] = {0.125, 2.0};
   const double *khs = kv_dt == FP8 ? ks : NULL, *vhs = kv_dt == FP8 ? vs : NULL;
   EXPECT(oracle_paged_decode(o1, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
-                             1.0, 1.0, khs, vhs, 1) == 0);
+                             1.0, 1.0, khs, vhs, NULL, NULL, 1) == 0);
   EXPECT(oracle_paged_decode(o3, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
-                             1.0, 1.0, khs, vhs, 3) == 0);
+                             1.0, 1.0, khs, vhs, NULL, NULL, 3) == 0);
   EXPECT(memcmp(o1, o3, sizeof(double) * (size_t)(L.S * L.H * L.D)) == 0);
   for (int64_t i = 0; i < L.S * L.H * L.D; ++i) EXPECT(isfinite(o1[i]));
+  if (kv_dt == FP8) { /* one scale per (block, kv head); not together with per-head scales */
+    double *kb = (double *)malloc(sizeof(double) * (size_t)(L.NB * L.Hkv));
+    double *vb = (double *)malloc(sizeof(double) * (size_t)(L.NB * L.Hkv));
+    for (int64_t i = 0; i < L.NB * L.Hkv; ++i) {
+      kb[i] = 0.25 + 0.125 * (double)(i % 5);
+      vb[i] = 2.0 - 0.25 * (double)(i % 7);
+    }
+    EXPECT(oracle_paged_decode(o3, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
+                               1.0, 1.0, NULL, NULL, kb, vb, 3) == 0);
+    for (int64_t i = 0; i < L.S * L.H * L.D; ++i) EXPECT(isfinite(o3[i]));
+    EXPECT(oracle_paged_decode(o3, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
+                               1.0, 1.0, khs, vhs, kb, vb, 3) != 0);
+    int32_t qs1[6] = {0, 0, 1, 2, 3, 4};
+    double *o4 = (double *)malloc(sizeof(double) * (size_t)(4 * L.H * L.D));
+    EXPECT(oracle_paged_prefill(o4, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, qs1, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W,
+                                0.25, 1.0, 1.0, NULL, NULL, kb, vb, 2) == 0);
+    free(kb), free(vb), free(o4);
+  }
   /* prefill: the last min(3, L) tokens of each sequence as queries */
   int32_t qsl[6] = {0};
   for (int64_t s = 0; s < L.S; ++s) qsl[s + 1] = qsl[s] + (L.ctx[s] < 3 ? L.ctx[s] : 3);
@@ -133,18 +154,18 @@ static void attention(int kv_dt, int q_dt, int heads_per_kv) {
   for (int64_t i = 0; i < rows * L.H * L.D; ++i) put(qp, q_dt, i, urand());
   double *op = (double *)malloc(sizeof(double) * (size_t)(rows * L.H * L.D));
   EXPECT(oracle_paged_prefill(op, qp, q_dt, kc, vc, kv_dt, L.bt, L.ctx, qsl, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W,
-                              0.25, 1.0, 1.0, khs, vhs, 2) == 0);
+                              0.25, 1.0, 1.0, khs, vhs, NULL, NULL, 2) == 0);
   for (int64_t i = 0; i < rows * L.H * L.D; ++i) EXPECT(isfinite(op[i]));
   /* a table entry outside the pool and a context longer than its table are refused */
   L.bt[1 * L.W] = (int32_t)L.NB;
   EXPECT(oracle_paged_decode(o1, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
-                             1.0, 1.0, khs, vhs, 2) != 0);
+                             1.0, 1.0, khs, vhs, NULL, NULL, 2) != 0);
   L.bt[1 * L.W] = 0;
   L.ctx[2] = (int32_t)(L.W * L.bs + 1);
   EXPECT(oracle_paged_decode(o1, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
-                             1.0, 1.0, khs, vhs, 2) != 0);
+                             1.0, 1.0, khs, vhs, NULL, NULL, 2) != 0);
   EXPECT(oracle_paged_decode(NULL, q, q_dt, kc, vc, kv_dt, L.bt, L.ctx, L.S, L.H, L.Hkv, L.D, L.NB, L.bs, L.W, 0.25,
-                             1.0, 1.0, khs, vhs, 1) != 0);
+                             1.0, 1.0, khs, vhs, NULL, NULL, 1) != 0);
   free(kc), free(vc), free(q), free(o1), free(o3), free(qp), free(op), free(L.bt), free(L.ctx);
 }
 
@@ -160,14 +181,22 @@ static void cache_write(int in_dt, int cache_dt) {
   int64_t slots[6] = {3, -1, 31, 0, 17, -5};
   const float hs[2] = {0.5f, 0.25f};
   const float *khs = cache_dt == FP8 ? hs : NULL;
-  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs) == 0);
+  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs, NULL, NULL) == 0);
+  if (cache_dt == FP8) { /* one scale per (destination block, kv head) */
+    float kb[8], vb[8];
+    for (int i = 0; i < 8; ++i) kb[i] = 0.5f + 0.25f * (float)i, vb[i] = 4.0f / (float)(i + 1);
+    EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, NULL, NULL, kb,
+                              vb) == 0);
+    EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, NULL, NULL, kb,
+                              NULL) != 0);
+  }
   if (in_dt == cache_dt) /* same dtype: the bytes of token 2 land at slot 31 */
     EXPECT(memcmp((char *)kc + 31 * Hkv * D * kElem[cache_dt], (char *)k + 2 * Hkv * D * kElem[in_dt],
                   (size_t)(Hkv * D * kElem[in_dt])) == 0);
   slots[1] = NB * bs; /* past the pool */
-  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs) != 0);
+  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs, NULL, NULL) != 0);
   slots[1] = 3; /* a duplicate */
-  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs) != 0);
+  EXPECT(oracle_cache_write(k, v, in_dt, kc, vc, cache_dt, slots, N, Hkv, D, NB, bs, 1.0f, 1.0f, khs, khs, NULL, NULL) != 0);
   free(kc), free(vc), free(k), free(v);
 }
 
