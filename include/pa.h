@@ -133,6 +133,20 @@ typedef struct pa_opts {
    * trusted like the block tables: finite and > 0, else results are unspecified. */
   const float *k_head_scales;
   const float *v_head_scales;
+  /* fp8 caches, one scale per (physical block, kv head): NULL, or fp32 arrays
+   * [num_blocks, num_kv_heads] (pa_decode_layers: [layers, num_blocks,
+   * num_kv_heads]) in device memory or pinned host memory.  The stored value
+   * of kv head h in block b is then code * k_block_scales[b * num_kv_heads + h]
+   * (v_block_scales for the value cache): a block's tokens share a scale, so
+   * it can follow the magnitude of the tokens a block holds (the per-head
+   * precision of section 8.2 of page "vLLM框架中的KV cache优化与PagedAttention机制详解",
+   * at the grain of the pool's blocks).  pa_decode, pa_decode_layers and
+   * pa_cache_write take them (the cache write quantises each new row with its
+   * destination block's scales); pa_prefill refuses them (PA_ERR_UNSUPPORTED).
+   * Both or neither, and not with per-head scales; with them k_scale and
+   * v_scale must be 0.  Trusted like the per-head scales. */
+  const float *k_block_scales;
+  const float *v_block_scales;
 } pa_opts;
 
 /* Number of workers pa_decode launches for this request (0 = the library's

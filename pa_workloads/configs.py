@@ -46,7 +46,8 @@ class DecodeConfig:
     churn_band: Tuple[float, float] = (0.70, 0.90)
     partition_size: int = 0  # tokens per split-context partition, 0 = library choice
     scale: Optional[float] = None  # softmax scale, default 1/sqrt(head_dim)
-    # fp8 caches: "tensor" = one scale per K / V tensor, "head" = one per kv head
+    # fp8 caches: "tensor" = one scale per K / V tensor, "head" = one per kv head,
+    # "block" = one per (physical block, kv head)
     fp8_scales: str = "tensor"
     # standard deviation of kv head h's K and V values, geometric from the first
     # to the second number over the heads (heads of different magnitude)
@@ -115,6 +116,14 @@ CONFIGS = {
         block_size=32, num_blocks=40000, max_blocks_per_seq=256, kv_dtype="fp8", q_dtype="f16",
         ctx_kind="lognormal", ctx_median=1024.0, ctx_sigma=1.0, ctx_lo=1, ctx_hi=8192,
         allocator="churn", fp8_scales="head", head_std=(0.25, 4.0),
+    ),
+    # The same with one fp8 scale per (physical block, kv head): the grain of
+    # the pool's own blocks, each scale fitted to what its block holds.
+    "gqa70b_fp8_blocks": DecodeConfig(
+        name="gqa70b_fp8_blocks", seed=6, num_seqs=128, num_heads=64, num_kv_heads=8, head_dim=128,
+        block_size=32, num_blocks=40000, max_blocks_per_seq=256, kv_dtype="fp8", q_dtype="f16",
+        ctx_kind="lognormal", ctx_median=1024.0, ctx_sigma=1.0, ctx_lo=1, ctx_hi=8192,
+        allocator="churn", fp8_scales="block", head_std=(0.25, 4.0),
     ),
 }
 

@@ -267,6 +267,22 @@ def _pool_masked_amax(shape, gen_seed, mask_t, device, chunk_blocks, std_t):
     return amax
 
 
+def _pool_masked_block_amax(shape, gen_seed, mask_t, device, chunk_blocks, std_t):
+    """float32 [num_blocks, num_kv_heads]: the largest stored magnitude of each
+    (block, kv head) -- the same draws as _fill_pool."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(gen_seed)
+    amax = torch.zeros((shape[0], shape[2]), dtype=torch.float32, device=device)
+    for b0 in range(0, shape[0], chunk_blocks):
+        b1 = min(shape[0], b0 + chunk_blocks)
+        x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32) * std_t
+        m = mask_t[b0:b1, :, None, None]
+        amax[b0:b1] = torch.where(m, x.abs(), torch.zeros_like(x)).amax(dim=(1, 3))
+    return amax
+
+
 def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, std_t, quant_scale=None):
     import torch
 
@@ -278,7 +294,10 @@ def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, std_t,
         x = torch.randn((b1 - b0,) + tuple(shape[1:]), generator=g, device=device, dtype=torch.float32) * std_t
         m = mask_t[b0:b1, :, None, None].expand_as(x)
         if dtype_name == "fp8":
-            codes = (x / quant_scale).to(torch.float8_e4m3fn).view(torch.uint8)
+            qs = quant_scale
+            if torch.is_tensor(qs) and qs.dim() == 4 and qs.shape[0] == shape[0]:  # per block: this chunk's
+                qs = qs[b0:b1]
+            codes = (x / qs).to(torch.float8_e4m3fn).view(torch.uint8)
             codes = torch.where(m, codes, torch.full_like(codes, FP8_NAN_CODE))
             out[b0:b1] = codes.view(torch.float8_e4m3fn)
         else:
@@ -294,10 +313,12 @@ def make_inputs(cfg: DecodeConfig, layout: Layout, device="cpu", seed_offset: in
     [num_blocks, block_size, Hkv, D]; k_new/v_new [S, Hkv, D]; int32
     context_lens and block_tables; int64 slot_mapping; plus k_scale/v_scale:
     per-tensor fp8 scales (floats; 1.0 for other dtypes), or for workloads with
-    per-head fp8 scales float32 tensors [Hkv] on ``device``.  fp8 scales are
-    chosen so the largest stored magnitude of the tensor (or of the kv head),
-    new tokens included, maps just under 448.  Kv head h's values are N(0, 1)
-    times head_stds(cfg)[h].
+    per-head fp8 scales float32 tensors [Hkv] on ``device`` (per-block:
+    [num_blocks, Hkv]).  fp8 scales are chosen so the largest stored magnitude
+    of the tensor (or of the kv head, or of the block's kv head), new tokens
+    included, maps just under 448; a block with nothing stored gets the scale
+    of a thousandth of its head's std.  Kv head h's values are N(0, 1) times
+    head_stds(cfg)[h].
     """
     import torch
 
@@ -334,6 +355,19 @@ def make_inputs(cfg: DecodeConfig, layout: Layout, device="cpu", seed_offset: in
             k_scale = torch.from_numpy(kh).to(device)
             v_scale = torch.from_numpy(vh).to(device)
             k_q, v_q = k_scale.reshape(1, 1, Hkv, 1), v_scale.reshape(1, 1, Hkv, 1)
+        elif cfg.fp8_scales == "block":
+            blocks = []
+            for seed, new in ((base + 2, k_new), (base + 3, v_new)):
+                am = _pool_masked_block_amax(shape, seed, mask_t, device, chunk_blocks, std_t)
+                slot = torch.from_numpy(layout.slot_mapping.copy()).to(device)
+                live = slot >= 0
+                if bool(live.any()):  # the new rows land in their slot's block
+                    dst = (slot[live] // cfg.block_size).long()
+                    am.scatter_reduce_(0, dst[:, None].expand(-1, Hkv), new.float().abs().amax(dim=2)[live], "amax")
+                am = torch.maximum(am, 1e-3 * std_t.reshape(1, Hkv))
+                blocks.append((am.double() / FP8_MAX * (1.0 + 2.0**-16)).to(torch.float32))
+            k_scale, v_scale = blocks
+            k_q, v_q = k_scale.reshape(cfg.num_blocks, 1, Hkv, 1), v_scale.reshape(cfg.num_blocks, 1, Hkv, 1)
         elif cfg.fp8_scales == "tensor":
             k_scale = float(np.float32(ka.max() / FP8_MAX * (1.0 + 2.0**-16)))
             v_scale = float(np.float32(va.max() / FP8_MAX * (1.0 + 2.0**-16)))
@@ -373,5 +407,7 @@ def algorithmic_bytes(cfg: DecodeConfig, context_lens: np.ndarray, out_dtype: st
     S, H, D = cfg.num_seqs, cfg.num_heads, cfg.head_dim
     table = 4 * int((-(-ctx // cfg.block_size)).sum())
     head_scales = 2 * 4 * cfg.num_kv_heads if (cfg.kv_dtype == "fp8" and cfg.fp8_scales == "head") else 0
+    # per-block scales: a key and a value scale per table entry read and kv head
+    block_scales = 2 * cfg.num_kv_heads * table if (cfg.kv_dtype == "fp8" and cfg.fp8_scales == "block") else 0
     return (kv_bytes(cfg, ctx) + S * H * D * (ELEM_BYTES[cfg.q_dtype] + ELEM_BYTES[out_dtype])
-            + table + 4 * S + head_scales)
+            + table + 4 * S + head_scales + block_scales)

@@ -73,6 +73,8 @@ class PaOpts(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("k_head_scales", ctypes.c_void_p),
         ("v_head_scales", ctypes.c_void_p),
+        ("k_block_scales", ctypes.c_void_p),
+        ("v_block_scales", ctypes.c_void_p),
     ]
 
 
@@ -180,23 +182,34 @@ def _raise(lib, status: int):
     raise PaError(status, lib.pa_last_error().decode(errors="replace"))
 
 
-def _set_scales(o: PaOpts, k_scale, v_scale, count: int) -> None:
+def _set_scales(o: PaOpts, k_scale, v_scale, count: int, block_shape=None) -> None:
     """fp8 scales into the options: floats are per-tensor scales; fp32 tensors
     of ``count`` elements (one scale per kv head, [num_kv_heads] or [layers,
     num_kv_heads], on the device or in pinned host memory) are per-head
-    scales."""
+    scales; fp32 tensors of shape ``block_shape`` ([num_blocks, num_kv_heads],
+    or [layers, num_blocks, num_kv_heads]) are per-block scales."""
     import torch
 
     if torch.is_tensor(k_scale) or torch.is_tensor(v_scale):
         if not (torch.is_tensor(k_scale) and torch.is_tensor(v_scale)):
-            raise ValueError("k_scale and v_scale: both per-head tensors or both floats")
+            raise ValueError("k_scale and v_scale: both tensors or both floats")
+        per_block = block_shape is not None and tuple(k_scale.shape) == tuple(block_shape)
         for t in (k_scale, v_scale):
-            if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != count:
-                raise ValueError(f"per-head scales must be contiguous float32 tensors of {count} elements")
+            if t.dtype != torch.float32 or not t.is_contiguous():
+                raise ValueError("fp8 scale tensors must be contiguous float32")
+            if per_block and tuple(t.shape) != tuple(block_shape):
+                raise ValueError(f"per-block scales must both be {tuple(block_shape)}")
+            if not per_block and t.numel() != count:
+                raise ValueError(f"per-head scales must have {count} elements"
+                                 + (f"; per-block scales the shape {tuple(block_shape)}" if block_shape else ""))
         o.k_scale = 0.0
         o.v_scale = 0.0
-        o.k_head_scales = k_scale.data_ptr()
-        o.v_head_scales = v_scale.data_ptr()
+        if per_block:
+            o.k_block_scales = k_scale.data_ptr()
+            o.v_block_scales = v_scale.data_ptr()
+        else:
+            o.k_head_scales = k_scale.data_ptr()
+            o.v_head_scales = v_scale.data_ptr()
     else:
         o.k_scale = float(k_scale)
         o.v_scale = float(v_scale)
@@ -277,14 +290,15 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size: int
     ``workspace``: a zero-filled device tensor from new_workspace(); if None,
     the binding's own workspace for this device and stream (allocated once,
     then reused).  ``k_scale`` / ``v_scale`` (fp8 caches): floats, one scale
-    per tensor, or float32 tensors [num_kv_heads], one scale per kv head.
+    per tensor; float32 tensors [num_kv_heads], one scale per kv head; or
+    float32 tensors [num_blocks, num_kv_heads], one scale per block and kv head.
     ``validate``: PA_FLAG_VALIDATE (tables, lengths and scales checked on the
     host first; waits for the stream; PaError PA_ERR_BAD_INDEX on a bad entry).
     """
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
     o = PaOpts()
-    _set_scales(o, k_scale, v_scale, num_kv_heads)
+    _set_scales(o, k_scale, v_scale, num_kv_heads, (k_cache.shape[0], num_kv_heads))
     o.partition_size = partition_size
     o.num_workers = num_workers
     o.flags = _flags(validate)
@@ -339,7 +353,7 @@ def decode_static(out, q, k_cache, v_cache, block_tables, context_lens, block_si
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens)
     o = PaOpts()
-    _set_scales(o, k_scale, v_scale, num_kv_heads)
+    _set_scales(o, k_scale, v_scale, num_kv_heads, (k_cache.shape[0], num_kv_heads))
     o.partition_size = partition_size
     o.num_workers = num_workers
     o.flags = _flags(validate)
@@ -366,7 +380,8 @@ def decode_layers(out, q, k_caches, v_caches, block_tables, context_lens, block_
     lib = load_library()
     _check_device(out, q, k_caches, v_caches, block_tables, context_lens)
     o = PaOpts()
-    _set_scales(o, k_scale, v_scale, q.shape[0] * num_kv_heads)
+    _set_scales(o, k_scale, v_scale, q.shape[0] * num_kv_heads,
+                (q.shape[0], k_caches.shape[1], num_kv_heads))
     o.partition_size = partition_size
     o.num_workers = num_workers
     o.flags = _flags(validate)
@@ -409,7 +424,7 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     lib = load_library()
     _check_device(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc)
     o = PaOpts()
-    _set_scales(o, k_scale, v_scale, num_kv_heads)
+    _set_scales(o, k_scale, v_scale, num_kv_heads, (k_cache.shape[0], num_kv_heads))
     o.flags = _flags(validate)
     o.stream = stream if stream is not None else _current_stream(q)
     if workspace is None:
@@ -431,7 +446,7 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, k_scale=1.0, v_scale=1.0, 
     lib = load_library()
     _check_device(k, v, k_cache, v_cache, slot_mapping)
     o = PaOpts()
-    _set_scales(o, k_scale, v_scale, k.shape[1])
+    _set_scales(o, k_scale, v_scale, k.shape[1], (k_cache.shape[0], k.shape[1]))
     o.flags = _flags(validate)
     o.stream = stream if stream is not None else _current_stream(k)
     st = lib.pa_cache_write(describe(k), describe(v), describe(k_cache), describe(v_cache), describe(slot_mapping),

@@ -89,12 +89,15 @@ __global__ void __launch_bounds__(kThreads) cache_quant_kernel(const CacheWriteA
   const int64_t s_n = is_v ? a.v_sn : a.k_sn, s_h = is_v ? a.v_sh : a.k_sh;
   const int64_t c_b = is_v ? a.vc_sb : a.kc_sb, c_t = is_v ? a.vc_st : a.kc_st, c_h = is_v ? a.vc_sh : a.kc_sh;
   const float *head_scale = is_v ? a.v_head_scale : a.k_head_scale;  // null: one scale for the tensor
+  // per (block, kv head): the scales of this token's destination block, else null
+  const float *block_scale = is_v ? a.v_block_scale : a.k_block_scale;
+  if (block_scale) block_scale += blk * a.num_kv_heads;
   const float tensor_scale = is_v ? a.v_scale : a.k_scale;
   const int per_head = a.head_dim / 16;
   const int total = a.num_kv_heads * per_head;
   for (int i = threadIdx.x; i < total; i += kThreads) {
     const int h = i / per_head, c = (i % per_head) * 16;
-    const float scale = head_scale ? head_scale[h] : tensor_scale;
+    const float scale = block_scale ? block_scale[h] : (head_scale ? head_scale[h] : tensor_scale);
     const int64_t sb = (int64_t)n * s_n + (int64_t)h * s_h + c;
     constexpr int IVEC = Elem<InT>::kPer16;
     float x[16];

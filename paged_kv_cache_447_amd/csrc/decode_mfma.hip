@@ -93,6 +93,11 @@ struct MfmaMath : MfmaCore<MT, D> {
   __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, u32x4 &phi, u32x4 &plo) {
     Core::weights(sc, cs, last, isc.qk, phi, plo);
   }
+  // the same with a key and a value factor per 16-token tile
+  __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, const float *kf, const float *vf,
+                                          u32x4 &phi, u32x4 &plo) {
+    Core::template weights<false, true>(sc, cs, last, isc.qk, phi, plo, kf, vf);
+  }
 
   __device__ void write_out(int s, int kvh) const {
     if (c16 >= G) return;
@@ -217,6 +222,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
     const_i32 *bt;
     const char *kb, *vb;
     int last;
+    const float *ksb, *vsb;  // per-block scales: this layer's and kv head's (stride num_kv_heads per block), or null
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
@@ -224,7 +230,27 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
     p.kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, g.s) + (int64_t)g.kvh * a.k_sh) * EB;
     p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
+    p.ksb = p.vsb = nullptr;
+    if (a.k_block_scale != nullptr) {
+      const int64_t o = (int64_t)layer_of(a, g.s) * a.num_blocks * a.num_kv_heads + g.kvh;
+      p.ksb = a.k_block_scale + o;
+      p.vsb = a.v_block_scale + o;
+    }
     return p;
+  }
+  // per-block scales: the key and value scales of the chunk's two tiles'
+  // blocks (scalar loads, a chunk ahead of their use); 1 without them
+  __device__ __forceinline__ void fetch_scales(const float *ksb, const float *vsb, const int *blk, float *kf,
+                                               float *vf) const {
+    typedef const __attribute__((address_space(4))) float cf;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      kf[tt] = vf[tt] = 1.0f;
+      if (ksb != nullptr) {
+        kf[tt] = ((cf *)(uintptr_t)ksb)[(int64_t)blk[tt] * a.num_kv_heads];
+        vf[tt] = ((cf *)(uintptr_t)vsb)[(int64_t)blk[tt] * a.num_kv_heads];
+      }
+    }
   }
   // q^T operand: lane (h, j) holds q[h][32 kb + 8 j ..], zeros for padding heads
   __device__ __forceinline__ void load_q(const SegInfo &g, u32x4 *dst) const {
@@ -240,6 +266,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
   // pipeline state carried from one segment into the next
   u32x4 qop[KS];
   int blk[2];
+  float kf[2], vf[2];  // the current chunk's tiles' key and value block scales (1 without per-block scales)
   u32x4 kr[NLD], vr[NLD];
 
   __device__ void begin(const SegInfo &g, const Walker &) { begin(g); }
@@ -252,6 +279,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
     const Ptrs p = ptrs(g);
     load_q(g, qop);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
+    fetch_scales(p.ksb, p.vsb, blk, kf, vf);
     __builtin_amdgcn_sched_barrier(0);
     issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
     __builtin_amdgcn_sched_barrier(0);
@@ -284,6 +312,8 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
       const int lastn = lastc ? pn.last : p.last;
       int nblk[2];
       fetch_blocks(btn, cn, lastn, nblk);
+      float nkf[2], nvf[2];
+      fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkf, nvf);
       __builtin_amdgcn_sched_barrier(0);
 
       // this chunk's K and V rows to LDS, then the next chunk's loads into the
@@ -299,11 +329,18 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
       f32x4 sc[2];
       Math::scores(qop, [&](int tt, int kb) { return k_operand(tt, kb); }, sc);
       u32x4 phi, plo;
-      Math::weights(sc, cs, p.last, phi, plo);
+      if (p.ksb != nullptr)
+        Math::weights(sc, cs, p.last, kf, vf, phi, plo);
+      else
+        Math::weights(sc, cs, p.last, phi, plo);
       Math::accumulate(phi, plo, [&](int n) { return vt_operand(n); });
       cs = cn;
-      blk[0] = nblk[0];
-      blk[1] = nblk[1];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        blk[tt] = nblk[tt];
+        kf[tt] = nkf[tt];
+        vf[tt] = nvf[tt];
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) qop[kb] = qn[kb];

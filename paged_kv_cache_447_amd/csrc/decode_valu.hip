@@ -220,6 +220,7 @@ struct ValuSeg {
     const char *kb, *vb;
     int last;
     int nrow;  // fused step, the item's last segment: the (sequence * kv heads + kv head) of the new token's rows; else -1
+    const float *ksb, *vsb;  // fp8 per-block scales: this layer's and kv head's (stride num_kv_heads per block), or null
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
     Ptrs p;
@@ -228,7 +229,37 @@ struct ValuSeg {
     p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
     p.nrow = APPEND && g.u_hi == g.n && append_writes(a, g.s) ? g.s * a.num_kv_heads + g.kvh : -1;
+    p.ksb = p.vsb = nullptr;
+    if (IS_FP8 && a.k_block_scale != nullptr) {
+      const int64_t o = (int64_t)layer_of(a, g.s) * a.num_blocks * a.num_kv_heads + g.kvh;
+      p.ksb = a.k_block_scale + o;
+      p.vsb = a.v_block_scale + o;
+    }
     return p;
+  }
+
+  // fp8 caches with per-block scales: the key and value scales of the
+  // blocks that load i of a chunk reads (scalar loads, a chunk ahead of their
+  // use); 1 without them
+  static constexpr bool IS_FP8 = __is_same(KVT, fp8_t);
+  __device__ __forceinline__ void fetch_scales(const float *ksb, const float *vsb, const int *blk, float *ks,
+                                               float *vs) const {
+    typedef const __attribute__((address_space(4))) float cf;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) ks[i] = vs[i] = 1.0f;
+    if (!IS_FP8 || ksb == nullptr) return;
+#pragma unroll
+    for (int j = 0; j < NBC; ++j) {
+      const int i0 = NBC == 1 ? 0 : (j * BS) / TPW;  // the first load in block j of the chunk
+      const int64_t off = (int64_t)blk[i0] * a.num_kv_heads;
+      const float kx = ((cf *)(uintptr_t)ksb)[off], vx = ((cf *)(uintptr_t)vsb)[off];
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if ((NBC == 1 ? 0 : (i * TPW) / BS) == j) {
+          ks[i] = kx;
+          vs[i] = vx;
+        }
+    }
   }
   __device__ __forceinline__ void load_q(const SegInfo &g, QSlice<KVT, QT> *dst) const {
     const int64_t qr = q_row(a, g.s);
@@ -239,6 +270,7 @@ struct ValuSeg {
   // pipeline state carried from one segment into the next
   QSlice<KVT, QT> q[G];
   int blk[NL];
+  float kbs[NL], vbs[NL];  // the current chunk's per-load block scales (fp8 with per-block scales; else 1)
   u32x4 kr[NL], vr[NL];
 
   // q, block ids and the K / V loads of g's first chunk; K before V, so that
@@ -253,6 +285,7 @@ struct ValuSeg {
     const Ptrs p = ptrs(g);
     load_q(g, q);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
+    if constexpr (IS_FP8) fetch_scales(p.ksb, p.vsb, blk, kbs, vbs);
     __builtin_amdgcn_sched_barrier(0);
     issue<false>(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr, p.nrow);
     __builtin_amdgcn_sched_barrier(0);
@@ -293,6 +326,8 @@ struct ValuSeg {
       const int nrn = lastc ? pn.nrow : p.nrow;
       int nblk[NL];
       fetch_blocks(btn, cn, lastn, nblk);
+      float nkbs[NL], nvbs[NL];
+      if constexpr (IS_FP8) fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkbs, nvbs);
       // the scheduler would otherwise sink table reads and loads down to their
       // uses and drain the pipeline: keep the program order at these points
       __builtin_amdgcn_sched_barrier(0);
@@ -307,7 +342,7 @@ struct ValuSeg {
       for (int i = 0; i < NL; ++i) {
         const bool valid = cs + i * TPW + tg <= p.last;
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * isc.qk : -INFINITY;
+        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * (IS_FP8 ? isc.qk * kbs[i] : isc.qk) : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
       issue<false>(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr, nrn);
@@ -339,8 +374,9 @@ struct ValuSeg {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           l[h] += sc[h][i];
+          const float w = IS_FP8 ? sc[h][i] * vbs[i] : sc[h][i];  // the weight times its block's value scale
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) acc[h][v] = __builtin_fmaf(sc[h][i], vf[v], acc[h][v]);
+          for (int v = 0; v < VEC; ++v) acc[h][v] = __builtin_fmaf(w, vf[v], acc[h][v]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -349,6 +385,13 @@ struct ValuSeg {
       cs = cn;
 #pragma unroll
       for (int i = 0; i < NL; ++i) blk[i] = nblk[i];
+      if constexpr (IS_FP8) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          kbs[i] = nkbs[i];
+          vbs[i] = nvbs[i];
+        }
+      }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) q[h] = qn[h];

@@ -172,15 +172,17 @@ struct MfmaCore {
   // split as P = hi + lo in the operand type.  EMPTY_OK: the column may have
   // seen no position yet and see none in this chunk either (its running max
   // still -inf); its weights are then zeros instead of exp2(-inf - -inf).
-  template <bool EMPTY_OK = false>
+  // TILE_SCALES: each 16-token tile tt has its own key factor kf[tt] (on its
+  // scores) and value factor vf[tt] (on its weights in P, not in the sum l).
+  template <bool EMPTY_OK = false, bool TILE_SCALES = false>
   __device__ __forceinline__ void weights(const f32x4 *sc, int cs, int last, float qk_scale_log2, u32x4 &phi,
-                                          u32x4 &plo) {
+                                          u32x4 &plo, const float *kf = nullptr, const float *vf = nullptr) {
     float p8[8];
     float cm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int tok = (i < 4 ? 4 * j + i : 16 + 4 * j + i - 4);
-      const float x = sc[i >> 2][i & 3] * qk_scale_log2;
+      const float x = sc[i >> 2][i & 3] * (TILE_SCALES ? qk_scale_log2 * kf[i >> 2] : qk_scale_log2);
       p8[i] = cs + tok <= last ? x : -INFINITY;
       cm = fmaxf(cm, p8[i]);
     }
@@ -200,8 +202,12 @@ struct MfmaCore {
     const float mn = EMPTY_OK && m == -INFINITY ? 0.0f : m;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
+      float e0 = fast_exp2(p8[i] - mn), e1 = fast_exp2(p8[i + 1] - mn);
       l += e0 + e1;
+      if (TILE_SCALES) {  // tokens i and i + 1 share a tile
+        e0 *= vf[i >> 2];
+        e1 *= vf[i >> 2];
+      }
       const uint32_t h0 = Op<MT>::bits(e0), h1 = Op<MT>::bits(e1);
       phi[i >> 1] = h0 | (h1 << 16);
       plo[i >> 1] = Op<MT>::bits(e0 - Op<MT>::value(h0)) | (Op<MT>::bits(e1 - Op<MT>::value(h1)) << 16);

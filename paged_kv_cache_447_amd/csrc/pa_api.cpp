@@ -204,6 +204,27 @@ pa_status head_scales(const pa_opts &o, int cache_kind, const float **ks, const 
   return PA_OK;
 }
 
+// Per-(block, kv head) fp8 scales of opts: both or neither, fp8 caches only,
+// not with per-head or per-tensor scales; device addresses, or null when not given.
+pa_status block_scales(const pa_opts &o, int cache_kind, const float **kb, const float **vb) {
+  *kb = *vb = nullptr;
+  if (!o.k_block_scales && !o.v_block_scales) return PA_OK;
+  if (!o.k_block_scales || !o.v_block_scales) return fail(PA_ERR_NULL, "k_block_scales and v_block_scales go together");
+  if (cache_kind != pa::KV_FP8) return fail(PA_ERR_ARG, "per-block scales apply to FP8_E4M3 caches only");
+  if (o.k_head_scales || o.v_head_scales) return fail(PA_ERR_ARG, "per-block and per-head scales exclude each other");
+  if (o.k_scale != 0.0f || o.v_scale != 0.0f)
+    return fail(PA_ERR_ARG, "per-tensor and per-block scales exclude each other: leave k_scale and v_scale at 0");
+  if (reinterpret_cast<uintptr_t>(o.k_block_scales) % 4 || reinterpret_cast<uintptr_t>(o.v_block_scales) % 4)
+    return fail(PA_ERR_LAYOUT, "per-block scales must be 4-byte aligned");
+  void *dk = nullptr, *dv = nullptr;
+  pa_status st;
+  if ((st = device_address(o.k_block_scales, "k_block_scales", &dk))) return st;
+  if ((st = device_address(o.v_block_scales, "v_block_scales", &dv))) return st;
+  *kb = static_cast<const float *>(dk);
+  *vb = static_cast<const float *>(dv);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -317,8 +338,9 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
                 o.workspace ? o.workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(o.workspace) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
 
-  const float *khs = nullptr, *vhs = nullptr;
+  const float *khs = nullptr, *vhs = nullptr, *kbs = nullptr, *vbs = nullptr;
   if ((st = head_scales(o, kvk, &khs, &vhs))) return st;
+  if ((st = block_scales(o, kvk, &kbs, &vbs))) return st;
   if (ap) {
     if ((st = check_tensor(ap->k_new, "k_new", 3, true))) return st;
     if ((st = check_tensor(ap->v_new, "v_new", 3, true))) return st;
@@ -347,6 +369,8 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
       if ((st = pa::check_new_token_slots(slots, bt, lens, block_size, NB * block_size))) return st;
     }
     if ((st = pa::check_head_scales(khs, vhs, layers * num_kv_heads, stream))) return st;
+    if ((st = pa::check_head_scales(kbs, vbs, layers * NB * num_kv_heads, stream, "k_block_scales", "v_block_scales")))
+      return st;
   }
 
   pa::DecodeArgs a;
@@ -393,6 +417,8 @@ pa_status decode_impl(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v
   a.v_scale = vs;
   a.k_head_scale = khs;
   a.v_head_scale = vhs;
+  a.k_block_scale = kbs;
+  a.v_block_scale = vbs;
   a.kv_kind = kvk;
   a.q_kind = kv_kind(q.dtype);
   a.out_f32 = out.dtype == PA_F32 && q.dtype != PA_F32;
@@ -599,6 +625,8 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");
   a.tile_slots = (int32_t)slots;
   if ((st = head_scales(o, kv_kind(k_cache.dtype), &a.k_head_scale, &a.v_head_scale))) return st;
+  if (o.k_block_scales || o.v_block_scales)
+    return fail(PA_ERR_UNSUPPORTED, "per-block scales: pa_decode, pa_decode_layers and pa_cache_write only");
   if (o.workspace) {  // the key split's pair counter
     if (o.workspace_bytes < pa_prefill_workspace_size())
       return fail(PA_ERR_WORKSPACE, "prefill workspace of %zu bytes needed, %zu given", pa_prefill_workspace_size(),
@@ -665,8 +693,9 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   if ((st = check_flags(o))) return st;
   if ((st = check_head_scale_args(o, ck))) return st;
   if (N == 0 || Hkv == 0 || D == 0) return PA_OK;
-  const float *khs = nullptr, *vhs = nullptr;
+  const float *khs = nullptr, *vhs = nullptr, *kbs = nullptr, *vbs = nullptr;
   if ((st = head_scales(o, ck, &khs, &vhs))) return st;
+  if ((st = block_scales(o, ck, &kbs, &vbs))) return st;
   if (o.flags & PA_FLAG_VALIDATE) {
     const hipStream_t stream = static_cast<hipStream_t>(o.stream);
     pa::HostInts slots;
@@ -674,6 +703,8 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
     if ((st = slots.fetch(slot_mapping, "slot_mapping", stream))) return st;
     if ((st = pa::check_distinct_slots(slots, k_cache.shape[0] * k_cache.shape[1]))) return st;
     if (ik != pa::KV_FP8 && (st = pa::check_head_scales(khs, vhs, Hkv, stream))) return st;
+    if ((st = pa::check_head_scales(kbs, vbs, k_cache.shape[0] * Hkv, stream, "k_block_scales", "v_block_scales")))
+      return st;
   }
 
   pa::CacheWriteArgs a;
@@ -705,6 +736,8 @@ pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_tensor 
   a.v_scale = vs;
   a.k_head_scale = khs;
   a.v_head_scale = vhs;
+  a.k_block_scale = kbs;
+  a.v_block_scale = vbs;
   if (a.block_size <= 0) return fail(PA_ERR_SHAPE, "block_size must be positive");
   hipError_t e = pa::launch_cache_write(a, static_cast<hipStream_t>(o.stream));
   if (e != hipSuccess) return fail(PA_ERR_HIP, "cache-write kernel launch: %s", hipGetErrorString(e));

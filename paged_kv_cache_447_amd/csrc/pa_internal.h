@@ -44,6 +44,10 @@ struct DecodeArgs {
   // fp8 caches with one scale per (layer, kv head): [layers * num_kv_heads]
   // each, multiplied into the two above (then scale * log2(e) and 1); or null
   const float *k_head_scale, *v_head_scale;
+  // fp8 caches with one scale per (layer, block, kv head): [layers *
+  // num_blocks * num_kv_heads] each, the scale of a token's block applied to
+  // its score (key) and its weight (value); or null
+  const float *k_block_scale, *v_block_scale;
   int32_t kv_kind;              // KvKind
   int32_t q_kind;               // KV_F32 / KV_F16 / KV_BF16
   int32_t out_f32;              // 1: out is fp32, 0: out has q's dtype
@@ -134,6 +138,7 @@ struct CacheWriteArgs {
   int32_t in_kind, cache_kind;     // KvKind of the inputs and of the cache
   float k_scale, v_scale;          // fp8 caches only
   const float *k_head_scale, *v_head_scale;  // fp8 caches: [num_kv_heads] each, or null (per-tensor scales)
+  const float *k_block_scale, *v_block_scale;  // fp8 caches: [num_blocks * num_kv_heads] each, or null
 };
 
 // Tokens per chunk (the unit of one pipelined load batch) of the decode kernel

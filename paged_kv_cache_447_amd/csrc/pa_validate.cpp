@@ -177,11 +177,12 @@ pa_status check_block_pairs(const HostInts &map, int64_t src_blocks, int64_t dst
   return PA_OK;
 }
 
-pa_status check_head_scales(const float *k_head_scales, const float *v_head_scales, int64_t n, hipStream_t stream) {
+pa_status check_head_scales(const float *k_head_scales, const float *v_head_scales, int64_t n, hipStream_t stream,
+                            const char *k_name, const char *v_name) {
   if (!k_head_scales || n <= 0) return PA_OK;
   std::vector<float> h((size_t)n);
   const float *src[2] = {k_head_scales, v_head_scales};
-  const char *names[2] = {"k_head_scales", "v_head_scales"};
+  const char *names[2] = {k_name, v_name};
   for (int i = 0; i < 2; ++i) {
     pa_status st = copy_to_host(h.data(), src[i], (size_t)n * sizeof(float), stream, names[i]);
     if (st) return st;

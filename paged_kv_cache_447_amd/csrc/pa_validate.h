@@ -38,7 +38,9 @@ pa_status check_distinct_slots(const HostInts &slots, int64_t num_slots);
 pa_status check_query_starts(const HostInts &query_start_loc, const HostInts &context_lens, int64_t num_rows);
 // Block pairs: distinct destinations; in one pool no destination is a source.
 pa_status check_block_pairs(const HostInts &mapping, int64_t src_blocks, int64_t dst_blocks, bool same_pool);
-// Per-kv-head scales (n of each, device or pinned host memory): finite and > 0.
-pa_status check_head_scales(const float *k_head_scales, const float *v_head_scales, int64_t n, hipStream_t stream);
+// Per-kv-head (or per-block) scales (n of each, device or pinned host
+// memory): finite and > 0.  The names are those the message gives.
+pa_status check_head_scales(const float *k_head_scales, const float *v_head_scales, int64_t n, hipStream_t stream,
+                            const char *k_name = "k_head_scales", const char *v_name = "v_head_scales");
 
 }  // namespace pa
