@@ -140,9 +140,9 @@ typedef struct pa_opts {
    * (v_block_scales for the value cache): a block's tokens share a scale, so
    * it can follow the magnitude of the tokens a block holds (the per-head
    * precision of section 8.2 of page "vLLM框架中的KV cache优化与PagedAttention机制详解",
-   * at the grain of the pool's blocks).  pa_decode, pa_decode_layers and
-   * pa_cache_write take them (the cache write quantises each new row with its
-   * destination block's scales); pa_prefill refuses them (PA_ERR_UNSUPPORTED).
+   * at the grain of the pool's blocks).  pa_decode, pa_decode_layers,
+   * pa_prefill and pa_cache_write take them (the cache write quantises each
+   * new row with its destination block's scales).
    * Both or neither, and not with per-head scales; with them k_scale and
    * v_scale must be 0.  Trusted like the per-head scales. */
   const float *k_block_scales;

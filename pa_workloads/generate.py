@@ -283,6 +283,29 @@ def _pool_masked_block_amax(shape, gen_seed, mask_t, device, chunk_blocks, std_t
     return amax
 
 
+def block_scales(cfg, base, k_new, v_new, slot_mapping, mask_t, device, std_t):
+    """float32 [num_blocks, num_kv_heads] key and value scales, one per (block,
+    kv head): the largest magnitude the block holds for that head -- its
+    stored values and the new rows whose slots lie in it -- maps just under
+    448; a block with nothing stored gets a thousandth of its head's std."""
+    import torch
+
+    Hkv = cfg.num_kv_heads
+    shape = (cfg.num_blocks, cfg.block_size, Hkv, cfg.head_dim)
+    chunk_blocks = max(1, (1 << 24) // (cfg.block_size * Hkv * cfg.head_dim))
+    out = []
+    for seed, new in ((base + 2, k_new), (base + 3, v_new)):
+        am = _pool_masked_block_amax(shape, seed, mask_t, device, chunk_blocks, std_t)
+        slot = torch.from_numpy(np.asarray(slot_mapping).copy()).to(device)
+        live = slot >= 0
+        if bool(live.any()):  # the new rows land in their slot's block
+            dst = (slot[live] // cfg.block_size).long()
+            am.scatter_reduce_(0, dst[:, None].expand(-1, Hkv), new.float().abs().amax(dim=2)[live], "amax")
+        am = torch.maximum(am, 1e-3 * std_t.reshape(1, Hkv))
+        out.append((am.double() / FP8_MAX * (1.0 + 2.0**-16)).to(torch.float32))
+    return out[0], out[1]
+
+
 def _fill_pool(shape, dtype_name, gen_seed, mask_t, device, chunk_blocks, std_t, quant_scale=None):
     import torch
 
@@ -356,17 +379,7 @@ def make_inputs(cfg: DecodeConfig, layout: Layout, device="cpu", seed_offset: in
             v_scale = torch.from_numpy(vh).to(device)
             k_q, v_q = k_scale.reshape(1, 1, Hkv, 1), v_scale.reshape(1, 1, Hkv, 1)
         elif cfg.fp8_scales == "block":
-            blocks = []
-            for seed, new in ((base + 2, k_new), (base + 3, v_new)):
-                am = _pool_masked_block_amax(shape, seed, mask_t, device, chunk_blocks, std_t)
-                slot = torch.from_numpy(layout.slot_mapping.copy()).to(device)
-                live = slot >= 0
-                if bool(live.any()):  # the new rows land in their slot's block
-                    dst = (slot[live] // cfg.block_size).long()
-                    am.scatter_reduce_(0, dst[:, None].expand(-1, Hkv), new.float().abs().amax(dim=2)[live], "amax")
-                am = torch.maximum(am, 1e-3 * std_t.reshape(1, Hkv))
-                blocks.append((am.double() / FP8_MAX * (1.0 + 2.0**-16)).to(torch.float32))
-            k_scale, v_scale = blocks
+            k_scale, v_scale = block_scales(cfg, base, k_new, v_new, layout.slot_mapping, mask_t, device, std_t)
             k_q, v_q = k_scale.reshape(cfg.num_blocks, 1, Hkv, 1), v_scale.reshape(cfg.num_blocks, 1, Hkv, 1)
         elif cfg.fp8_scales == "tensor":
             k_scale = float(np.float32(ka.max() / FP8_MAX * (1.0 + 2.0**-16)))

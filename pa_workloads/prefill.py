@@ -15,7 +15,8 @@ from typing import Dict, Tuple, Union
 import numpy as np
 
 from .configs import DecodeConfig
-from .generate import ELEM_BYTES, FP8_MAX, Layout, _fill_pool, _pool_masked_amax, head_stds, make_layout, torch_dtype
+from .generate import (ELEM_BYTES, FP8_MAX, Layout, _fill_pool, _pool_masked_amax, block_scales, head_stds, make_layout,
+                       torch_dtype)
 
 
 @dataclass(frozen=True)
@@ -134,8 +135,9 @@ def make_prefill_inputs(pcfg: PrefillConfig, pl: PrefillLayout, device="cpu", se
     """q [N, H, D]; k_cache/v_cache with every position before the new tokens
     stored (the rest NaN, code 0x7F for fp8); k_new/v_new [N, Hkv, D]; int32
     context_lens, block_tables, query_start_loc; int64 slot_mapping [N];
-    k_scale/v_scale: fp8 scales per tensor (floats; 1.0 for other dtypes) or
-    per kv head (float32 tensors [Hkv]), as make_inputs draws them."""
+    k_scale/v_scale: fp8 scales per tensor (floats; 1.0 for other dtypes), per
+    kv head (float32 tensors [Hkv]) or per block (float32 tensors [num_blocks,
+    Hkv]), as make_inputs draws them."""
     import torch
 
     cfg = pcfg.base
@@ -163,7 +165,11 @@ def make_prefill_inputs(pcfg: PrefillConfig, pl: PrefillLayout, device="cpu", se
                            k_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
         va = torch.maximum(_pool_masked_amax(shape, base + 3, mask_t, device, chunk_blocks, std_t),
                            v_new.float().abs().amax(dim=(0, 2))).cpu().numpy().astype(np.float64)
-        if cfg.fp8_scales == "head":  # one scale per kv head, float32 tensors [Hkv]
+        if cfg.fp8_scales == "block":  # one scale per (block, kv head), float32 tensors [num_blocks, Hkv]
+            k_scale, v_scale = block_scales(cfg, base, k_new, v_new, pl.slot_mapping, mask_t, device, std_t)
+            k_q = k_scale.reshape(cfg.num_blocks, 1, Hkv, 1)
+            v_q = v_scale.reshape(cfg.num_blocks, 1, Hkv, 1)
+        elif cfg.fp8_scales == "head":  # one scale per kv head, float32 tensors [Hkv]
             k_scale = torch.from_numpy((ka / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)).to(device)
             v_scale = torch.from_numpy((va / FP8_MAX * (1.0 + 2.0**-16)).astype(np.float32)).to(device)
             k_q, v_q = k_scale.reshape(1, 1, Hkv, 1), v_scale.reshape(1, 1, Hkv, 1)

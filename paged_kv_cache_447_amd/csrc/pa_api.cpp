@@ -625,8 +625,7 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
   if (slots * num_kv_heads > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "too many tiles");
   a.tile_slots = (int32_t)slots;
   if ((st = head_scales(o, kv_kind(k_cache.dtype), &a.k_head_scale, &a.v_head_scale))) return st;
-  if (o.k_block_scales || o.v_block_scales)
-    return fail(PA_ERR_UNSUPPORTED, "per-block scales: pa_decode, pa_decode_layers and pa_cache_write only");
+  if ((st = block_scales(o, kv_kind(k_cache.dtype), &a.k_block_scale, &a.v_block_scale))) return st;
   if (o.workspace) {  // the key split's pair counter
     if (o.workspace_bytes < pa_prefill_workspace_size())
       return fail(PA_ERR_WORKSPACE, "prefill workspace of %zu bytes needed, %zu given", pa_prefill_workspace_size(),
@@ -644,6 +643,9 @@ pa_status pa_prefill(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_tensor v_
     if ((st = pa::check_tables(bt, lens, block_size, NB))) return st;
     if ((st = pa::check_query_starts(qsl, lens, N))) return st;
     if ((st = pa::check_head_scales(a.k_head_scale, a.v_head_scale, num_kv_heads, stream))) return st;
+    if ((st = pa::check_head_scales(a.k_block_scale, a.v_block_scale, NB * num_kv_heads, stream, "k_block_scales",
+                                    "v_block_scales")))
+      return st;
   }
   a.qk_scale_log2 = (float)((double)scale * 1.4426950408889634 * (double)ks);
   a.v_scale = vs;

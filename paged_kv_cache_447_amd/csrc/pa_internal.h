@@ -100,6 +100,7 @@ struct PrefillArgs {
   // fp8 caches with one scale per kv head: [num_kv_heads] each, multiplied
   // into the two above (then scale * log2(e) and 1); or null
   const float *k_head_scale, *v_head_scale;
+  const float *k_block_scale, *v_block_scale;  // fp8 caches: [num_blocks * num_kv_heads] each, or null
   int32_t kv_kind;                 // KvKind of the caches: q's, or KV_FP8
   int32_t q_kind;                  // KvKind of q (and of the matrix-core operands)
   int32_t out_f32;                 // 1: out is fp32, 0: out has q's dtype

@@ -185,6 +185,7 @@ struct PrefillTile {
   // the workgroup's tile
   int s, kvh, q0, pos0, c_hi, last_max;
   float qk_sc, v_sc;  // its score scale (log2 units) and output scale: the launch's, or its fp8 kv head's
+  const float *ksb, *vsb;  // fp8 per-block scales of its kv head (stride num_kv_heads per block), or null
   const_i32 *bt;
   const char *kbase, *vbase;
   // this wavefront's columns
@@ -211,10 +212,15 @@ struct PrefillTile {
     kvh = kh;
     qk_sc = a.qk_scale_log2;
     v_sc = a.v_scale;
+    ksb = vsb = nullptr;
     if constexpr (kFp8) {
       if (a.k_head_scale != nullptr) {
         qk_sc *= a.k_head_scale[kvh];
         v_sc *= a.v_head_scale[kvh];
+      }
+      if (a.k_block_scale != nullptr) {
+        ksb = a.k_block_scale + kvh;
+        vsb = a.v_block_scale + kvh;
       }
     }
     int q1;
@@ -285,8 +291,25 @@ struct PrefillTile {
     }
   }
 
-  // scores and softmax weights of chunk c from the K rows at ks
-  __device__ __forceinline__ void qk(int c, const char *ks, u32x4 *phi, u32x4 *plo) {
+  // fp8 per-block scales: the key and value scales of chunk c's two tiles'
+  // blocks (scalar loads; taken a chunk ahead of their use); 1 without them
+  __device__ __forceinline__ void chunk_scales(int c, float *kf, float *vf) const {
+    typedef const __attribute__((address_space(4))) float cf;
+    kf[0] = kf[1] = vf[0] = vf[1] = 1.0f;
+    if (ksb == nullptr) return;
+    int b[2];
+    blocks_of(c, b[0], b[1]);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      kf[tt] = ((cf *)(uintptr_t)ksb)[(int64_t)b[tt] * a.num_kv_heads];
+      vf[tt] = ((cf *)(uintptr_t)vsb)[(int64_t)b[tt] * a.num_kv_heads];
+    }
+  }
+
+  // scores and softmax weights of chunk c from the K rows at ks (with the key
+  // and value factors kf, vf per 16-token tile when `scaled`)
+  __device__ __forceinline__ void qk(int c, const char *ks, u32x4 *phi, u32x4 *plo, bool scaled = false,
+                                     const float *kf = nullptr, const float *vf = nullptr) {
     const int cs = CT * c;
     u32x4 kop[2][KS];
 #pragma unroll
@@ -298,16 +321,20 @@ struct PrefillTile {
       f32x4 sc[2];
       core[ct].scores(qop[ct], [&](int tt, int kb) { return kop[tt][kb]; }, sc);
       // with the keys split, a wavefront's first chunks may lie past a column's limit
-      core[ct].template weights<KSP>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct]);
+      if (kFp8 && scaled)
+        core[ct].template weights<KSP, true>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct], kf, vf);
+      else
+        core[ct].template weights<KSP>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct]);
     }
   }
   // output update from the V rows at vs
   __device__ __forceinline__ void pv(const char *vs, const u32x4 *phi, const u32x4 *plo) {
     accumulate_slot_n<NC>(core, phi, plo, vs, [&](int n) { return voff[n]; });
   }
-  __device__ __forceinline__ void compute(int c, const char *ks) {
+  __device__ __forceinline__ void compute(int c, const char *ks, bool scaled = false, const float *kf = nullptr,
+                                          const float *vf = nullptr) {
     u32x4 phi[NC], plo[NC];
-    qk(c, ks, phi, plo);
+    qk(c, ks, phi, plo, scaled, kf, vf);
     pv(ks + HB, phi, plo);
   }
 
@@ -404,6 +431,8 @@ struct PrefillTile {
     u32x4 rows[fp8n<8>()];
     int blk = block_of(0);
     load_fp8<8>(0, 8 * wave, blk, blk, rows);
+    float kf[2], vf[2], nkf[2], nvf[2];  // per-block scales of chunks c and c + 1
+    chunk_scales(0, kf, vf);
     int slot = 0;
     for (int c = 0; c < nch; ++c) {
       stage_fp8<8>(8 * wave, ring + slot * CB, rows);
@@ -412,7 +441,13 @@ struct PrefillTile {
         blk = block_of(c + 1);
         load_fp8<8>(c + 1, 8 * wave, blk, blk, rows);
       }
-      if (CT * c <= wlast) compute(c, ring + slot * CB);
+      chunk_scales(c + 1, nkf, nvf);
+      if (CT * c <= wlast) compute(c, ring + slot * CB, ksb != nullptr, kf, vf);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        kf[tt] = nkf[tt];
+        vf[tt] = nvf[tt];
+      }
       slot = slot + 1 == R ? 0 : slot + 1;
     }
 #pragma unroll
@@ -432,17 +467,25 @@ struct PrefillTile {
     int b0, b1;
     blocks_of(wave, b0, b1);
     load_fp8<32>(wave, 0, b0, b1, rows);
+    float kf[2], vf[2], nkf[2], nvf[2];  // per-block scales of chunks c and c + 4
+    chunk_scales(wave, kf, vf);
     int k = 0;
     for (int c = wave; c < nch; c += kWaves, ++k) {
       char *slot = mine + (k & 1) * CB;
       stage_fp8<32>(0, slot, rows);
       blocks_of(c + kWaves, b0, b1);
       load_fp8<32>(c + kWaves, 0, b0, b1, rows);  // past the end: the last rows again, unused
+      chunk_scales(c + kWaves, nkf, nvf);
       // the transposed reads are inline assembly: keep them after the stores
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      compute(c, slot);
+      compute(c, slot, ksb != nullptr, kf, vf);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        kf[tt] = nkf[tt];
+        vf[tt] = nvf[tt];
+      }
     }
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) core[ct].finish();

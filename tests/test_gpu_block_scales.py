@@ -3,7 +3,8 @@ through the C ABI, against the fp64 oracle: the cache write (each new row
 quantised with its destination block's scales; bit-exact over the whole pool),
 single-layer decode on both kernels (vector ALU for groups of 1-2, matrix
 cores for 4-16) across work splits, multi-layer decode with a slab of scales
-per layer, PA_FLAG_VALIDATE on the scales, and the prefill's refusal."""
+per layer, and PA_FLAG_VALIDATE on the scales.  Prefill with per-block scales
+is in tests/test_gpu_prefill.py (fp8_blocks_* cases)."""
 
 import numpy as np
 import pytest
@@ -98,7 +99,7 @@ def test_layers_take_their_own_block_scales():
     assert err <= TOL_F32["fp8"]
 
 
-def test_validate_names_a_bad_block_scale_and_prefill_refuses_them():
+def test_validate_names_a_bad_block_scale():
     cfg = SMALL["gqa8_f16q"]
     layout, inp = setup(cfg)
     gpu_cache_write(cfg, inp)
@@ -117,10 +118,3 @@ def test_validate_names_a_bad_block_scale_and_prefill_refuses_them():
         pa.cache_write(inp["k_new"], inp["v_new"], inp["k_cache"], inp["v_cache"], inp["slot_mapping"],
                        k_scale=inp["k_scale"], v_scale=bad, validate=True)
     assert e.value.status == -9 and "v_block_scales[0]" in str(e.value), str(e.value)
-    qsl = torch.arange(cfg.num_seqs + 1, dtype=torch.int32, device="cuda")
-    pout = torch.empty_like(inp["q"])
-    with pytest.raises(pa.PaError) as e:
-        pa.prefill(pout, inp["q"], inp["k_cache"], inp["v_cache"], inp["block_tables"], inp["context_lens"], qsl,
-                   cfg.block_size, cfg.softmax_scale, cfg.num_kv_heads, k_scale=inp["k_scale"],
-                   v_scale=inp["v_scale"])
-    assert e.value.status == -5, str(e.value)

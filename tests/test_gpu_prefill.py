@@ -87,6 +87,17 @@ CASES = {
     "fp8_heads_verify_gqa8": P("fp8_heads_verify_gqa8",
                                scaled(get_config("gqa70b_fp8"), num_seqs=12, num_blocks=2000, max_blocks_per_seq=64,
                                       ctx_lo=4, ctx_hi=2048), 4),
+    # fp8 caches with one scale per (physical block, kv head): column mode, G = 4, head_dim 64 ...
+    "fp8_blocks_gqa4_d64": P("fp8_blocks_gqa4_d64",
+                             scaled(get_config("fp8_long"), num_seqs=4, num_heads=16, num_kv_heads=4, head_dim=64,
+                                    q_dtype="bf16", num_blocks=300, max_blocks_per_seq=64, ctx_kind="fixed",
+                                    ctx_fixed=(5, 100, 600, 1000), partition_size=0, fp8_scales="block",
+                                    head_std=(0.25, 4.0)),
+                             (5, 64, 130, 200)),
+    # ... and the key split on the 70B grouped-query shape
+    "fp8_blocks_verify_gqa8": P("fp8_blocks_verify_gqa8",
+                                scaled(get_config("gqa70b_fp8_blocks"), num_seqs=12, num_blocks=2000,
+                                       max_blocks_per_seq=64, ctx_lo=4, ctx_hi=2048), 4),
     # fp8 e4m3fn caches (per-tensor scales), rows decoded into the query's type on the way into LDS:
     # column mode, MHA, f16 q, block 32 ...
     "fp8_mha_bs32": P("fp8_mha_bs32",
