@@ -137,7 +137,9 @@ struct MfmaMath : MfmaCore<MT, D> {
 // fp8 caches: rows are loaded into registers, decoded, and staged in LDS as
 // the operand type (the loads of chunk c+1 are in flight while chunk c is
 // computed).
-template <typename KVT, typename MT, int D, int G, int BS>
+// BSC: one scale per (block, kv head) (a variant of its own, so that the
+// other launches carry none of its work)
+template <typename KVT, typename MT, int D, int G, int BS, bool BSC = false>
 struct MfmaRegSeg : MfmaMath<MT, D, G> {
   using Math = MfmaMath<MT, D, G>;
   using Math::a;
@@ -231,7 +233,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
     p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
     p.last = g.t_hi - 1;
     p.ksb = p.vsb = nullptr;
-    if (a.k_block_scale != nullptr) {
+    if (BSC) {
       const int64_t o = (int64_t)layer_of(a, g.s) * a.num_blocks * a.num_kv_heads + g.kvh;
       p.ksb = a.k_block_scale + o;
       p.vsb = a.v_block_scale + o;
@@ -246,7 +248,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       kf[tt] = vf[tt] = 1.0f;
-      if (ksb != nullptr) {
+      if (BSC) {
         kf[tt] = ((cf *)(uintptr_t)ksb)[(int64_t)blk[tt] * a.num_kv_heads];
         vf[tt] = ((cf *)(uintptr_t)vsb)[(int64_t)blk[tt] * a.num_kv_heads];
       }
@@ -279,7 +281,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
     const Ptrs p = ptrs(g);
     load_q(g, qop);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
-    fetch_scales(p.ksb, p.vsb, blk, kf, vf);
+    if constexpr (BSC) fetch_scales(p.ksb, p.vsb, blk, kf, vf);
     __builtin_amdgcn_sched_barrier(0);
     issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
     __builtin_amdgcn_sched_barrier(0);
@@ -313,7 +315,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
       int nblk[2];
       fetch_blocks(btn, cn, lastn, nblk);
       float nkf[2], nvf[2];
-      fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkf, nvf);
+      if constexpr (BSC) fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkf, nvf);
       __builtin_amdgcn_sched_barrier(0);
 
       // this chunk's K and V rows to LDS, then the next chunk's loads into the
@@ -329,7 +331,7 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
       f32x4 sc[2];
       Math::scores(qop, [&](int tt, int kb) { return k_operand(tt, kb); }, sc);
       u32x4 phi, plo;
-      if (p.ksb != nullptr)
+      if constexpr (BSC)
         Math::weights(sc, cs, p.last, kf, vf, phi, plo);
       else
         Math::weights(sc, cs, p.last, phi, plo);
@@ -338,8 +340,10 @@ struct MfmaRegSeg : MfmaMath<MT, D, G> {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         blk[tt] = nblk[tt];
-        kf[tt] = nkf[tt];
-        vf[tt] = nvf[tt];
+        if constexpr (BSC) {
+          kf[tt] = nkf[tt];
+          vf[tt] = nvf[tt];
+        }
       }
     }
 #pragma unroll
@@ -611,24 +615,25 @@ __device__ __forceinline__ void run_ring_worker(const DecodeArgs &a, int w, int 
   seg.end();
 }
 
-template <typename KVT, typename MT, int D, int G, int BS, bool APPEND>
+// APPEND: the fused step (16-bit caches); BSC: per-block scales (fp8 caches)
+template <typename KVT, typename MT, int D, int G, int BS, bool APPEND, bool BSC>
 struct SegFor {
-  typedef MfmaRegSeg<KVT, MT, D, G, BS> type;
+  typedef MfmaRegSeg<KVT, MT, D, G, BS, BSC> type;
   __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
     run_worker<MT, G, D>(a, w, W, lane, seg);
   }
 };
-template <typename MT, int D, int G, int BS, bool APPEND>
-struct SegFor<MT, MT, D, G, BS, APPEND> {
+template <typename MT, int D, int G, int BS, bool APPEND, bool BSC>
+struct SegFor<MT, MT, D, G, BS, APPEND, BSC> {
   typedef MfmaRingSeg<MT, D, G, BS, APPEND> type;
   __device__ static void run(const DecodeArgs &a, int w, int W, int lane, type &seg) {
     run_ring_worker<MT, G, D, type, APPEND>(a, w, W, lane, seg);
   }
 };
 
-template <typename KVT, typename MT, int D, int G, int BS, bool APPEND>
+template <typename KVT, typename MT, int D, int G, int BS, bool APPEND, bool BSC = false>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs a) {
-  typedef typename SegFor<KVT, MT, D, G, BS, APPEND>::type Seg;
+  typedef typename SegFor<KVT, MT, D, G, BS, APPEND, BSC>::type Seg;
   __shared__ __attribute__((aligned(1024))) char lds[kWavesPerWG][Seg::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -637,7 +642,7 @@ __global__ void __launch_bounds__(64 * kWavesPerWG) decode_mfma(const DecodeArgs
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
   Seg seg(a, lane, lds[wave]);
-  SegFor<KVT, MT, D, G, BS, APPEND>::run(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
+  SegFor<KVT, MT, D, G, BS, APPEND, BSC>::run(a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
 template <typename KVT, typename MT, int D, int G>
@@ -649,6 +654,15 @@ hipError_t launch_g(const DecodeArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16, true>), grid, block, 0, stream, a);
       else
         hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (!__is_same(KVT, MT)) {  // fp8 with per-block scales: their own variant
+    if (a.k_block_scale != nullptr) {
+      if (a.block_size == 16)
+        hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 16, false, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_mfma<KVT, MT, D, G, 32, false, true>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }

@@ -154,7 +154,9 @@ __device__ __forceinline__ void store_vec(void *base, int64_t off, const float *
   }
 }
 
-template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND = false>
+// BSC: fp8 caches with one scale per (block, kv head) (a variant of its own,
+// so that the other launches carry none of its work)
+template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND = false, bool BSC = false>
 struct ValuSeg {
   static constexpr int VEC = Elem<KVT>::kPer16;  // KV elements per 16-byte load
   static constexpr int LPR = D / VEC;            // lanes per token row
@@ -230,7 +232,7 @@ struct ValuSeg {
     p.last = g.t_hi - 1;
     p.nrow = APPEND && g.u_hi == g.n && append_writes(a, g.s) ? g.s * a.num_kv_heads + g.kvh : -1;
     p.ksb = p.vsb = nullptr;
-    if (IS_FP8 && a.k_block_scale != nullptr) {
+    if (BSC) {
       const int64_t o = (int64_t)layer_of(a, g.s) * a.num_blocks * a.num_kv_heads + g.kvh;
       p.ksb = a.k_block_scale + o;
       p.vsb = a.v_block_scale + o;
@@ -240,14 +242,14 @@ struct ValuSeg {
 
   // fp8 caches with per-block scales: the key and value scales of the
   // blocks that load i of a chunk reads (scalar loads, a chunk ahead of their
-  // use); 1 without them
-  static constexpr bool IS_FP8 = __is_same(KVT, fp8_t);
+  // use)
+  static_assert(!BSC || __is_same(KVT, fp8_t), "per-block scales are for fp8 caches");
   __device__ __forceinline__ void fetch_scales(const float *ksb, const float *vsb, const int *blk, float *ks,
                                                float *vs) const {
     typedef const __attribute__((address_space(4))) float cf;
 #pragma unroll
     for (int i = 0; i < NL; ++i) ks[i] = vs[i] = 1.0f;
-    if (!IS_FP8 || ksb == nullptr) return;
+    if (!BSC) return;
 #pragma unroll
     for (int j = 0; j < NBC; ++j) {
       const int i0 = NBC == 1 ? 0 : (j * BS) / TPW;  // the first load in block j of the chunk
@@ -285,7 +287,7 @@ struct ValuSeg {
     const Ptrs p = ptrs(g);
     load_q(g, q);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
-    if constexpr (IS_FP8) fetch_scales(p.ksb, p.vsb, blk, kbs, vbs);
+    if constexpr (BSC) fetch_scales(p.ksb, p.vsb, blk, kbs, vbs);
     __builtin_amdgcn_sched_barrier(0);
     issue<false>(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr, p.nrow);
     __builtin_amdgcn_sched_barrier(0);
@@ -327,7 +329,7 @@ struct ValuSeg {
       int nblk[NL];
       fetch_blocks(btn, cn, lastn, nblk);
       float nkbs[NL], nvbs[NL];
-      if constexpr (IS_FP8) fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkbs, nvbs);
+      if constexpr (BSC) fetch_scales(lastc ? pn.ksb : p.ksb, lastc ? pn.vsb : p.vsb, nblk, nkbs, nvbs);
       // the scheduler would otherwise sink table reads and loads down to their
       // uses and drain the pipeline: keep the program order at these points
       __builtin_amdgcn_sched_barrier(0);
@@ -342,7 +344,7 @@ struct ValuSeg {
       for (int i = 0; i < NL; ++i) {
         const bool valid = cs + i * TPW + tg <= p.last;
 #pragma unroll
-        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * (IS_FP8 ? isc.qk * kbs[i] : isc.qk) : -INFINITY;
+        for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * (BSC ? isc.qk * kbs[i] : isc.qk) : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
       issue<false>(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr, nrn);
@@ -374,7 +376,7 @@ struct ValuSeg {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           l[h] += sc[h][i];
-          const float w = IS_FP8 ? sc[h][i] * vbs[i] : sc[h][i];  // the weight times its block's value scale
+          const float w = BSC ? sc[h][i] * vbs[i] : sc[h][i];  // the weight times its block's value scale
 #pragma unroll
           for (int v = 0; v < VEC; ++v) acc[h][v] = __builtin_fmaf(w, vf[v], acc[h][v]);
         }
@@ -385,7 +387,7 @@ struct ValuSeg {
       cs = cn;
 #pragma unroll
       for (int i = 0; i < NL; ++i) blk[i] = nblk[i];
-      if constexpr (IS_FP8) {
+      if constexpr (BSC) {
 #pragma unroll
         for (int i = 0; i < NL; ++i) {
           kbs[i] = nkbs[i];
@@ -440,7 +442,7 @@ struct ValuSeg {
   }
 };
 
-template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND>
+template <typename KVT, typename QT, int D, int G, int BS, int NL, bool APPEND, bool BSC = false>
 __global__ void __launch_bounds__(64 * kWavesPerWG) decode_valu(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -448,8 +450,8 @@ __global__ void __launch_bounds__(64 * kWavesPerWG) decode_valu(const DecodeArgs
   // XCD's workers hold one contiguous stretch of the work order
   const int nb = gridDim.x, b = blockIdx.x;
   const int bx = (nb % 8 == 0) ? (b % 8) * (nb / 8) + b / 8 : b;
-  ValuSeg<KVT, QT, D, G, BS, NL, APPEND> seg(a, lane);
-  run_worker<QT, G, D, ValuSeg<KVT, QT, D, G, BS, NL, APPEND>, APPEND ? Elem<KVT>::kBytes : 0>(
+  ValuSeg<KVT, QT, D, G, BS, NL, APPEND, BSC> seg(a, lane);
+  run_worker<QT, G, D, ValuSeg<KVT, QT, D, G, BS, NL, APPEND, BSC>, APPEND ? Elem<KVT>::kBytes : 0>(
       a, bx * kWavesPerWG + wave, nb * kWavesPerWG, lane, seg);
 }
 
@@ -467,6 +469,15 @@ hipError_t launch_one(const DecodeArgs &a, hipStream_t stream) {
         hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL, true>), grid, block, 0, stream, a);
       else
         hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL, true>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (__is_same(KVT, fp8_t)) {  // per-block scales: their own variant
+    if (a.k_block_scale != nullptr) {
+      if (a.block_size == 16)
+        hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 16, NL, false, true>), grid, block, 0, stream, a);
+      else
+        hipLaunchKernelGGL((decode_valu<KVT, QT, D, G, 32, NL, false, true>), grid, block, 0, stream, a);
       return hipGetLastError();
     }
   }

@@ -151,7 +151,9 @@ struct TileOrder {
 // chunk, which it loads alone into a private two-slot ring; the four partial
 // softmax states are merged through LDS at the end.  Otherwise the four
 // wavefronts compute different columns over every chunk of one shared stream.
-template <typename MT, typename KVT, int D, int BS, int NC, bool KSP>
+// BSC: fp8 caches with one scale per (block, kv head) (a variant of its own,
+// so that the other launches carry none of its work)
+template <typename MT, typename KVT, int D, int BS, int NC, bool KSP, bool BSC = false>
 struct PrefillTile {
   using Slot = RowSlot<D>;
   static constexpr bool kFp8 = __is_same(KVT, fp8_t);
@@ -218,7 +220,7 @@ struct PrefillTile {
         qk_sc *= a.k_head_scale[kvh];
         v_sc *= a.v_head_scale[kvh];
       }
-      if (a.k_block_scale != nullptr) {
+      if (BSC) {
         ksb = a.k_block_scale + kvh;
         vsb = a.v_block_scale + kvh;
       }
@@ -296,7 +298,7 @@ struct PrefillTile {
   __device__ __forceinline__ void chunk_scales(int c, float *kf, float *vf) const {
     typedef const __attribute__((address_space(4))) float cf;
     kf[0] = kf[1] = vf[0] = vf[1] = 1.0f;
-    if (ksb == nullptr) return;
+    if (!BSC) return;
     int b[2];
     blocks_of(c, b[0], b[1]);
 #pragma unroll
@@ -321,7 +323,7 @@ struct PrefillTile {
       f32x4 sc[2];
       core[ct].scores(qop[ct], [&](int tt, int kb) { return kop[tt][kb]; }, sc);
       // with the keys split, a wavefront's first chunks may lie past a column's limit
-      if (kFp8 && scaled)
+      if (BSC && scaled)
         core[ct].template weights<KSP, true>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct], kf, vf);
       else
         core[ct].template weights<KSP>(sc, cs, last[ct], qk_sc, phi[ct], plo[ct]);
@@ -442,7 +444,7 @@ struct PrefillTile {
         load_fp8<8>(c + 1, 8 * wave, blk, blk, rows);
       }
       chunk_scales(c + 1, nkf, nvf);
-      if (CT * c <= wlast) compute(c, ring + slot * CB, ksb != nullptr, kf, vf);
+      if (CT * c <= wlast) compute(c, ring + slot * CB, BSC, kf, vf);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         kf[tt] = nkf[tt];
@@ -479,7 +481,7 @@ struct PrefillTile {
       // the transposed reads are inline assembly: keep them after the stores
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
-      compute(c, slot, ksb != nullptr, kf, vf);
+      compute(c, slot, BSC, kf, vf);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -664,9 +666,9 @@ struct PrefillTile {
   }
 };
 
-template <typename MT, typename KVT, int D, int BS, int NC, bool KSP>
+template <typename MT, typename KVT, int D, int BS, int NC, bool KSP, bool BSC = false>
 __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const PrefillArgs a) {
-  typedef PrefillTile<MT, KVT, D, BS, NC, KSP> Tile;
+  typedef PrefillTile<MT, KVT, D, BS, NC, KSP, BSC> Tile;
   __shared__ __attribute__((aligned(1024))) char lds[Tile::kLdsBytes];
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -735,35 +737,44 @@ __global__ void __launch_bounds__(64 * kWaves, KSP ? 1 : 2) prefill_mfma(const P
   }
 }
 
-template <typename MT, typename KVT, int D, int BS>
+template <typename MT, typename KVT, int D, int BS, bool BSC>
 hipError_t launch_nc(const PrefillArgs &a, hipStream_t stream) {
   const int64_t n = (int64_t)a.tile_slots * a.num_kv_heads;
   const dim3 grid((unsigned)(a.key_split ? min((int64_t)a.persistent_wgs, n) : (n + 7) / 8 * 8)),
       block(64 * kWaves);
   if (a.key_split) {
     if (a.tile_cols == 32)
-      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, true, BSC>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, true, BSC>), grid, block, 0, stream, a);
   } else {
     if (a.tile_cols == 32 * kWaves)
-      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 2, false, BSC>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_mfma<MT, KVT, D, BS, 1, false, BSC>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
 }
 
-template <typename MT, typename KVT, int D>
+template <typename MT, typename KVT, int D, bool BSC>
 hipError_t launch_bs(const PrefillArgs &a, hipStream_t stream) {
-  return a.block_size == 16 ? launch_nc<MT, KVT, D, 16>(a, stream) : launch_nc<MT, KVT, D, 32>(a, stream);
+  return a.block_size == 16 ? launch_nc<MT, KVT, D, 16, BSC>(a, stream) : launch_nc<MT, KVT, D, 32, BSC>(a, stream);
 }
 
 template <typename MT, typename KVT>
 hipError_t launch_d(const PrefillArgs &a, hipStream_t stream) {
+  if constexpr (__is_same(KVT, fp8_t)) {  // per-block scales: their own variant
+    if (a.k_block_scale != nullptr) {
+      switch (a.head_dim) {
+        case 64: return launch_bs<MT, KVT, 64, true>(a, stream);
+        case 128: return launch_bs<MT, KVT, 128, true>(a, stream);
+      }
+      return hipErrorInvalidValue;
+    }
+  }
   switch (a.head_dim) {
-    case 64: return launch_bs<MT, KVT, 64>(a, stream);
-    case 128: return launch_bs<MT, KVT, 128>(a, stream);
+    case 64: return launch_bs<MT, KVT, 64, false>(a, stream);
+    case 128: return launch_bs<MT, KVT, 128, false>(a, stream);
   }
   return hipErrorInvalidValue;
 }
