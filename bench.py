@@ -60,6 +60,8 @@ def parse():
                     help="comma-separated decode workloads also timed (step and kernel) in the same run; '' for none")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 512 MiB device copy (reference for hardware byte counters)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling measured after the decode legs")
     return ap.parse_args()
 
 
@@ -113,6 +115,66 @@ def back_to_back_ms(fn, sets, steps, stream) -> float:
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
+
+
+READ_CEILING_BYTES = 4 << 30  # 16x the 256 MB last-level cache
+READ_CEILING_GRIDS = (1024, 2048, 4096, 8192, 16384)
+
+
+def read_ceiling(dev, steps: int = 10) -> dict:
+    """The part's practical streaming-read rate: pa_stream_read over a 4 GiB
+    buffer of seeded random words, at five grid sizes x 1, 4 or 8 loads in
+    flight x ordinary or non-temporal loads, each shape timed by HIP events
+    around `steps` launches back to back on one stream.  Every shape's checksum
+    (the XOR of its partials) must equal a separate XOR fold of the buffer."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_447_amd as pa
+
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    buf = torch.empty(READ_CEILING_BYTES // 4, dtype=torch.int32, device=dev).random_(generator=gen)
+    fold = buf
+    while fold.numel() > 1:  # the element count is a power of two
+        h = fold.numel() // 2
+        fold = torch.bitwise_xor(fold[:h], fold[h:])
+    want = int(fold.item()) & 0xFFFFFFFF
+    del fold
+    partials = torch.zeros(max(READ_CEILING_GRIDS), dtype=torch.int32, device=dev)
+    best = {}
+    for nt in (False, True):
+        for loads in (1, 4, 8):
+            for grid in READ_CEILING_GRIDS:
+                def run(_, grid=grid, loads=loads, nt=nt):
+                    pa.stream_read(buf, partials, grid, loads, nt, stream=stream.cuda_stream)
+
+                run(None)
+                torch.cuda.synchronize()
+                got = int(np.bitwise_xor.reduce(partials[:grid].cpu().numpy().view(np.uint32)))
+                if got != want:
+                    raise RuntimeError(f"pa_stream_read checksum {got:#x} != {want:#x} "
+                                       f"(grid {grid}, {loads} loads, nontemporal={nt})")
+                gbs = READ_CEILING_BYTES / (back_to_back_ms(run, [None], steps, stream) * 1e-3) / 1e9
+                key = ("nontemporal" if nt else "ordinary", loads)
+                if key not in best or gbs > best[key][0]:
+                    best[key] = (gbs, grid)
+    del buf, partials
+    torch.cuda.empty_cache()
+    top_key = max(best, key=lambda k: best[k][0])
+    top_gbs, top_grid = best[top_key]
+    return {
+        "GB/s": round(top_gbs, 1),
+        "frac_of_peak": round(top_gbs / HBM_PEAK_GBS, 4),
+        "loads": top_key[0],
+        "loads_in_flight": top_key[1],
+        "workgroups": top_grid,
+        "bytes": READ_CEILING_BYTES,
+        "launches_per_shape": steps,
+        "best_per_kind": {f"{k[0]}_x{k[1]}": {"GB/s": round(v[0], 1), "workgroups": v[1]}
+                          for k, v in sorted(best.items())},
+        "kernel": "pa_stream_read (grid-stride 16-byte loads folded into an XOR checksum)",
+    }
 
 
 def oracle_rate(run_once, seconds: float):
@@ -289,6 +351,12 @@ def main():
     if args.also:
         result["also"] = {name: also_decode(args, name, dev) for name in args.also.split(",")
                           if name and name != cfg.name}
+    if not args.no_read_ceiling:
+        rc = read_ceiling(dev)
+        result["read_ceiling"] = rc
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / rc["GB/s"], 4)
+        for leg in result.get("also", {}).values():
+            leg["frac_of_read_ceiling"] = round(leg["roofline_frac"] * HBM_PEAK_GBS / rc["GB/s"], 4)
 
     if host0 is not None:
         import oracle
@@ -663,6 +731,12 @@ def bench_layers(args, lcfg, dev) -> dict:
             "sample": f"{reps} fp64 decodes of layer 0 of {lcfg.name} (all {cfg.num_seqs} sequences), "
                       f"{el:.1f} s wall, {nthreads} threads",
         }
+    if not args.no_read_ceiling:
+        del sets
+        torch.cuda.empty_cache()
+        rc = read_ceiling(dev)
+        result["read_ceiling"] = rc
+        result["roofline"]["frac_of_read_ceiling"] = round(achieved / rc["GB/s"], 4)
     return result
 
 

@@ -393,6 +393,36 @@ PA_API pa_status pa_cache_write(pa_tensor k, pa_tensor v, pa_tensor k_cache, pa_
 PA_API pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor src_k_cache,
                                 pa_tensor src_v_cache, pa_tensor block_mapping, const pa_opts *opts);
 
+/*
+ * pa_stream_read -- a plain streaming read of one buffer, for measurement.
+ *
+ * Not a step of the attention path.  A decode step gathers each sequence's
+ * K/V range through its block table (page "vLLM框架中的KV cache优化与
+ * PagedAttention机制详解", section 5.1) and reads each of those bytes once, so
+ * its practical ceiling is the rate at which the part can stream-read memory
+ * far larger than its caches; this call measures that rate with the same
+ * 16-byte loads.
+ *
+ *   buf              device memory (or pinned host memory), 16-byte aligned,
+ *                    `bytes` long; read once, never written.
+ *   bytes            > 0, a multiple of 16.
+ *   num_workgroups   1 .. 65536 workgroups of 256 threads, reading the buffer
+ *                    grid-stride in 16-byte vectors.
+ *   loads_in_flight  1, 4 or 8 vectors each thread loads before it uses any.
+ *   nontemporal      non-zero: non-temporal loads (the kind the decode
+ *                    kernels use for K/V rows); zero: ordinary loads.
+ *   partials         [num_workgroups] uint32, device memory, caller-owned:
+ *                    partials[w] becomes the XOR of the 32-bit words workgroup
+ *                    w read, so the XOR of all partials is the XOR of every
+ *                    32-bit word of the buffer, whatever the launch shape.
+ *   opts             stream only (NULL = null stream, flags 0).
+ * Errors: PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_LAYOUT, PA_ERR_ARG,
+ * PA_ERR_UNSUPPORTED as named above, before anything is enqueued.
+ * Work: one launch.
+ */
+PA_API pa_status pa_stream_read(const void *buf, int64_t bytes, int32_t num_workgroups, int32_t loads_in_flight,
+                                int32_t nontemporal, uint32_t *partials, const pa_opts *opts);
+
 /* Static description of a status code. */
 PA_API const char *pa_status_string(pa_status s);
 

@@ -122,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.pa_copy_blocks.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
     lib.pa_cache_write.restype = i32
     lib.pa_cache_write.argtypes = [PaTensor] * 5 + [ctypes.POINTER(PaOpts)]
+    lib.pa_stream_read.restype = i32
+    lib.pa_stream_read.argtypes = [ctypes.c_void_p, i64, i32, i32, i32, ctypes.c_void_p, ctypes.POINTER(PaOpts)]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [i32]
     lib.pa_last_error.restype = ctypes.c_char_p
@@ -481,3 +483,24 @@ def copy_blocks(dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, block_mappin
     if st != 0:
         _raise(lib, st)
     return dst_k_cache, dst_v_cache
+
+
+def stream_read(buf, partials, num_workgroups: int, loads_in_flight: int = 4, nontemporal: bool = True,
+                stream=None):
+    """pa_stream_read: one plain streaming read of the GPU tensor `buf` (its bytes,
+    a multiple of 16), for measuring the read rate; partials (a uint32-sized GPU
+    tensor of at least num_workgroups entries) receives one XOR checksum per
+    workgroup.  Returns partials."""
+    lib = load_library()
+    _check_device(buf, partials)
+    if not buf.is_contiguous() or not partials.is_contiguous():
+        raise ValueError("buf and partials must be contiguous")
+    if partials.element_size() != 4 or partials.numel() < num_workgroups:
+        raise ValueError("partials must hold num_workgroups 32-bit entries")
+    o = PaOpts()
+    o.stream = stream if stream is not None else _current_stream(buf)
+    st = lib.pa_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), num_workgroups, loads_in_flight,
+                            1 if nontemporal else 0, partials.data_ptr(), ctypes.byref(o))
+    if st != 0:
+        _raise(lib, st)
+    return partials

@@ -818,6 +818,32 @@ pa_status pa_copy_blocks(pa_tensor dst_k_cache, pa_tensor dst_v_cache, pa_tensor
   return PA_OK;
 }
 
+pa_status pa_stream_read(const void *buf, int64_t bytes, int32_t num_workgroups, int32_t loads_in_flight,
+                         int32_t nontemporal, uint32_t *partials, const pa_opts *opts) {
+  pa_opts o;
+  std::memset(&o, 0, sizeof o);
+  if (opts) o = *opts;
+  pa_status st;
+  if (!buf || !partials) return fail(PA_ERR_NULL, "buf and partials are required");
+  if ((st = check_flags(o))) return st;
+  if (o.flags & PA_FLAG_VALIDATE) return fail(PA_ERR_ARG, "pa_stream_read: PA_FLAG_VALIDATE has nothing to check");
+  if (bytes <= 0 || bytes % 16) return fail(PA_ERR_SHAPE, "bytes must be a positive multiple of 16, got %lld",
+                                            (long long)bytes);
+  if (reinterpret_cast<uintptr_t>(buf) % 16) return fail(PA_ERR_LAYOUT, "buf must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(partials) % 4) return fail(PA_ERR_LAYOUT, "partials must be 4-byte aligned");
+  if (num_workgroups < 1 || num_workgroups > 65536)
+    return fail(PA_ERR_ARG, "num_workgroups must be in [1, 65536], got %d", num_workgroups);
+  if (loads_in_flight != 1 && loads_in_flight != 4 && loads_in_flight != 8)
+    return fail(PA_ERR_UNSUPPORTED, "loads_in_flight must be 1, 4 or 8, got %d", loads_in_flight);
+  void *db, *dp;
+  if ((st = device_address(buf, "buf", &db))) return st;
+  if ((st = device_address(partials, "partials", &dp))) return st;
+  hipError_t e = pa::launch_stream_read(db, bytes, num_workgroups, loads_in_flight, nontemporal != 0,
+                                        static_cast<uint32_t *>(dp), static_cast<hipStream_t>(o.stream));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "stream-read kernel launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
 const char *pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "ok";

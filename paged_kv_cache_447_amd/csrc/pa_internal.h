@@ -160,6 +160,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // whole-block copies (block_copy.hip)
 int64_t copy_blocks_pieces(int64_t block_bytes);
 hipError_t launch_copy_blocks(const BlockCopyArgs &a, hipStream_t stream);
+// a plain streaming read, for measurement (stream_read.hip)
+hipError_t launch_stream_read(const void *buf, int64_t bytes, int workgroups, int loads, bool nontemporal,
+                              uint32_t *partials, hipStream_t stream);
 
 // Which (kv dtype, q dtype, head_dim, group size) the decode kernels were built for.
 bool decode_supported(int kv_kind, int q_kind, int head_dim, int group);

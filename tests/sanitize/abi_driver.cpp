@@ -193,6 +193,22 @@ void abi_argument_checks() {
     expect_error(pa_copy_blocks(kc, kc, other, other, map, &o));
     expect_error(pa_copy_blocks(kc, kc, kc, kc, map, &o));  // fake pointers: refused, nothing copied
   }
+  {  // the streaming-read probe
+    pa_opts o = Opts(false);
+    uint32_t *parts = static_cast<uint32_t *>(kFake);
+    const char *misaligned = static_cast<const char *>(kFake) + 4;
+    expect_error(pa_stream_read(nullptr, 1024, 4, 4, 1, parts, &o), PA_ERR_NULL);
+    expect_error(pa_stream_read(kFake, 1000, 4, 4, 1, parts, &o), PA_ERR_SHAPE);
+    expect_error(pa_stream_read(kFake, 0, 4, 4, 1, parts, &o), PA_ERR_SHAPE);
+    expect_error(pa_stream_read(misaligned, 1024, 4, 4, 1, parts, &o), PA_ERR_LAYOUT);
+    expect_error(pa_stream_read(kFake, 1024, 0, 4, 1, parts, &o), PA_ERR_ARG);
+    expect_error(pa_stream_read(kFake, 1024, 65537, 4, 1, parts, &o), PA_ERR_ARG);
+    expect_error(pa_stream_read(kFake, 1024, 4, 3, 1, parts, &o), PA_ERR_UNSUPPORTED);
+    o.flags = 1;  // PA_FLAG_VALIDATE: nothing to check here
+    expect_error(pa_stream_read(kFake, 1024, 4, 4, 1, parts, &o), PA_ERR_ARG);
+    o = Opts(false);
+    expect_error(pa_stream_read(kFake, 1024, 4, 4, 1, parts, &o), PA_ERR_ARG);  // fake pointer: refused
+  }
 }
 
 pa::HostInts H(int64_t rows, int64_t cols, std::vector<int64_t> v) {

@@ -23,7 +23,7 @@ SAN_DIR = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "paged_kv_cache_447_amd", "csrc")
 BUILD_DIR = os.path.join(ROOT, "paged_kv_cache_447_amd", "_build")
 KERNEL_OBJECTS = ["decode_valu.hip.o", "decode_mfma.hip.o", "decode_static.hip.o", "prefill_mfma.hip.o",
-                  "cache_write.hip.o", "block_copy.hip.o"]
+                  "cache_write.hip.o", "block_copy.hip.o", "stream_read.hip.o"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 SANITIZE = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
