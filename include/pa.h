@@ -222,9 +222,14 @@ PA_API pa_status pa_decode(pa_tensor out, pa_tensor q, pa_tensor k_cache, pa_ten
  *                  i.e. block_tables[s][(L-1) / block_size] * block_size +
  *                  (L-1) % block_size for L = context_lens[s].
  * Effect: rows k_new[s], v_new[s] are copied to their slot and out is
- * pa_decode's result over the updated cache, bit for bit: the decode reads the
- * new token's K/V from k_new/v_new directly instead of from the slot being
- * written.  A slot < 0 or past the pool is skipped, as in pa_cache_write (for
+ * pa_decode's result over the updated cache: the decode reads the new token's
+ * K/V from k_new/v_new directly instead of from the slot being written.  For
+ * groups of four or more query heads per kv head on 16-bit caches the result
+ * is pa_decode's bit for bit (the new token takes its place in its chunk).
+ * For groups of one or two and for fp32 caches the new token enters its
+ * softmax first instead of last, so the sums run in another order and the
+ * result equals pa_decode's up to fp32 rounding.  A slot < 0 or past the
+ * pool is skipped, as in pa_cache_write (for
  * instance a last token that lies in a block already stored and shared with
  * other sequences): nothing is written and the decode reads position L - 1
  * from the cache as it stands.  If a slot is not the one of position L - 1, or

@@ -190,29 +190,47 @@ struct ValuSeg {
   }
 
   // the block's base address is uniform (scalar registers); each lane adds a
-  // 32-bit offset inside the block.  In a fused step (APPEND) the chunk that
-  // holds an item's last token -- the step's new token, nrow non-null, whose
-  // slot this launch is writing -- reads that token's row from the new rows:
-  // every lane whose (clamped) token is the last one gets the new row's
-  // address, in the same load instructions.
-  template <bool ISV = false>
+  // 32-bit offset inside the block
   __device__ __forceinline__ void issue(const char *base, int64_t sb, int64_t st, int cs, int last, const int *blk,
-                                        u32x4 *dst, int nrow = -1) const {
-    const bool redirect = APPEND && uniform(nrow >= 0 && cs + CH > last);
-    const char *nb = nullptr;
-    if (APPEND) {  // the new row of (sequence, kv head) nrow
-      const int s = nrow / a.num_kv_heads, kvh = nrow - (nrow / a.num_kv_heads) * a.num_kv_heads;
-      nb = reinterpret_cast<const char *>(ISV ? a.v_new : a.k_new) +
-           ((int64_t)s * (ISV ? a.vn_ss : a.kn_ss) + (int64_t)kvh * (ISV ? a.vn_sh : a.kn_sh) + r * VEC) * EB;
-    }
+                                        u32x4 *dst) const {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const int t = min(cs + i * TPW + tg, last);
       const char *bb = base + (int64_t)blk[i] * sb * EB;
       const char *pl = bb + (uint32_t)(((t & (BS - 1)) * (uint32_t)st + r * VEC) * EB);
-      if (APPEND && redirect)  // a scalar branch around the choice only: the load instruction is the same
-        pl = reinterpret_cast<const char *>(t == last ? (uintptr_t)nb : (uintptr_t)pl);
       dst[i] = ld16_stream(pl);
+    }
+  }
+
+  // A fused step (APPEND) whose new token goes to a slot of the pool (the
+  // slot this launch writes): the token stays out of the paged range of its
+  // item's last segment, and opens the item's first segment instead, its K
+  // and V rows read from k_new / v_new.  The softmax over the item is the
+  // same set of scores; only the order of the sums changes.
+  __device__ __forceinline__ int paged_end(const SegInfo &g) const {
+    return g.t_hi - (APPEND && g.u_hi == g.n && append_writes(a, g.s) ? 1 : 0);
+  }
+  __device__ __forceinline__ void load_new(const SegInfo &g, u32x4 &kd, u32x4 &vd) const {
+    const int64_t c = r * VEC;
+    kd = ld16(reinterpret_cast<const char *>(a.k_new) + ((int64_t)g.s * a.kn_ss + (int64_t)g.kvh * a.kn_sh + c) * EB);
+    vd = ld16(reinterpret_cast<const char *>(a.v_new) + ((int64_t)g.s * a.vn_ss + (int64_t)g.kvh * a.vn_sh + c) * EB);
+  }
+  // the running state after the new token alone: its score is the reference
+  // maximum (the same on every lane: each lane group holds the whole row), and
+  // token group 0 holds its weight 1 and its value row
+  __device__ __forceinline__ void open_with_new(float qk) {
+    float sn[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sn[h] = q[h].dot(kn);
+    group_sum_n<LPR, G>(sn);
+    float vf[VEC];
+    Elem<KVT>::unpack(vn, vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = sn[h] * qk;
+      l[h] = tg == 0 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) acc[h][v] = tg == 0 ? vf[v] : 0.0f;
     }
   }
 
@@ -220,8 +238,7 @@ struct ValuSeg {
   struct Ptrs {
     const_i32 *bt;
     const char *kb, *vb;
-    int last;
-    int nrow;  // fused step, the item's last segment: the (sequence * kv heads + kv head) of the new token's rows; else -1
+    int last;  // the last token of the paged range (loads past it read it again)
     const float *ksb, *vsb;  // fp8 per-block scales: this layer's and kv head's (stride num_kv_heads per block), or null
   };
   __device__ __forceinline__ Ptrs ptrs(const SegInfo &g) const {
@@ -229,8 +246,10 @@ struct ValuSeg {
     p.bt = as_const(a.block_tables) + (int64_t)seq_of(a, g.s) * a.bt_ss;
     p.kb = reinterpret_cast<const char *>(a.k_cache) + (k_layer(a, g.s) + (int64_t)g.kvh * a.k_sh) * EB;  // uniform
     p.vb = reinterpret_cast<const char *>(a.v_cache) + (v_layer(a, g.s) + (int64_t)g.kvh * a.v_sh) * EB;
-    p.last = g.t_hi - 1;
-    p.nrow = APPEND && g.u_hi == g.n && append_writes(a, g.s) ? g.s * a.num_kv_heads + g.kvh : -1;
+    // a fused step's segment that holds only the new token has an empty paged
+    // range: the loads issued ahead for it read the token before (for a
+    // sequence of one token, position 0), in bounds, and are never used
+    p.last = APPEND ? max(paged_end(g) - 1, 0) : g.t_hi - 1;
     p.ksb = p.vsb = nullptr;
     if (BSC) {
       const int64_t o = (int64_t)layer_of(a, g.s) * a.num_blocks * a.num_kv_heads + g.kvh;
@@ -274,6 +293,7 @@ struct ValuSeg {
   int blk[NL];
   float kbs[NL], vbs[NL];  // the current chunk's per-load block scales (fp8 with per-block scales; else 1)
   u32x4 kr[NL], vr[NL];
+  u32x4 kn, vn;  // fused step: the new token's K and V row slices of the current segment's item
 
   // q, block ids and the K / V loads of g's first chunk; K before V, so that
   // the first wait of the chunk loop is for K alone
@@ -286,12 +306,13 @@ struct ValuSeg {
   __device__ void begin(const SegInfo &g) {
     const Ptrs p = ptrs(g);
     load_q(g, q);
+    if constexpr (APPEND) load_new(g, kn, vn);
     fetch_blocks(p.bt, g.t_lo, p.last, blk);
     if constexpr (BSC) fetch_scales(p.ksb, p.vsb, blk, kbs, vbs);
     __builtin_amdgcn_sched_barrier(0);
-    issue<false>(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr, p.nrow);
+    issue(p.kb, a.k_sb, a.k_st, g.t_lo, p.last, blk, kr);
     __builtin_amdgcn_sched_barrier(0);
-    issue<true>(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr, p.nrow);
+    issue(p.vb, a.v_sb, a.v_st, g.t_lo, p.last, blk, vr);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -303,20 +324,28 @@ struct ValuSeg {
 #pragma unroll
       for (int v = 0; v < VEC; ++v) acc[h][v] = 0.0f;
     }
-    if (g.t_hi <= g.t_lo) {  // only if context_lens changed under the launch
+    const ItemScale isc = seg_scale<KVT>(a, g.s, g.kvh);
+    vsc = isc.v;
+    if constexpr (APPEND) {
+      if (g.u_lo == 0 && append_writes(a, g.s)) open_with_new(isc.qk);
+    }
+    const int pend = APPEND ? paged_end(g) : g.t_hi;
+    // empty: a fused step's segment holding only the new token (its state is
+    // complete in token group 0), or context_lens changed under the launch
+    if (pend <= g.t_lo) {
       if (has) begin(nx);
       return;
     }
     const Ptrs p = ptrs(g);
-    const ItemScale isc = seg_scale<KVT>(a, g.s, g.kvh);
-    vsc = isc.v;
     // the chunk after this segment's last one: the next segment's first (or,
     // for the range's last segment, this last chunk again -- a cache hit, unused)
     const Ptrs pn = has ? ptrs(nx) : p;
     QSlice<KVT, QT> qn[G];
     load_q(has ? nx : g, qn);
+    u32x4 knn, vnn;
+    if constexpr (APPEND) load_new(has ? nx : g, knn, vnn);
 
-    const int nch = (g.t_hi - g.t_lo + CH - 1) / CH;
+    const int nch = (pend - g.t_lo + CH - 1) / CH;
     int cs = g.t_lo;
     for (int c = 0; c < nch; ++c) {
       const bool lastc = c + 1 == nch;
@@ -325,7 +354,6 @@ struct ValuSeg {
       const char *kbn = lastc ? pn.kb : p.kb;
       const char *vbn = lastc ? pn.vb : p.vb;
       const int lastn = lastc ? pn.last : p.last;
-      const int nrn = lastc ? pn.nrow : p.nrow;
       int nblk[NL];
       fetch_blocks(btn, cn, lastn, nblk);
       float nkbs[NL], nvbs[NL];
@@ -347,7 +375,7 @@ struct ValuSeg {
         for (int h = 0; h < G; ++h) sc[h][i] = valid ? sc[h][i] * (BSC ? isc.qk * kbs[i] : isc.qk) : -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue<false>(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr, nrn);
+      issue(kbn, a.k_sb, a.k_st, cn, lastn, nblk, kr);
       __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -382,7 +410,7 @@ struct ValuSeg {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      issue<true>(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr, nrn);
+      issue(vbn, a.v_sb, a.v_st, cn, lastn, nblk, vr);
       __builtin_amdgcn_sched_barrier(0);
       cs = cn;
 #pragma unroll
@@ -397,6 +425,10 @@ struct ValuSeg {
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) q[h] = qn[h];
+    if constexpr (APPEND) {
+      kn = knn;
+      vn = vnn;
+    }
 
     // every lane ends with the totals of its row slice over all tokens of the segment
 #pragma unroll
