@@ -122,11 +122,14 @@ struct Windows {
 
 __device__ __forceinline__ void load_windows(const DecodeArgs &a, int lane, Windows &ws) {
   int L[kWin];
+  // all loads in flight together: every lane loads (lanes past the last
+  // sequence read the last one's length again), and the lengths are chosen
+  // afterwards -- a load under a per-lane condition would be awaited before
+  // the next one is issued
 #pragma unroll
-  for (int i = 0; i < kWin; ++i) {  // all loads in flight together
-    const int s = 64 * i + lane;
-    L[i] = s < a.num_seqs ? clamp_ctx(a.context_lens[seq_of(a, s)], a.max_ctx) : 0;
-  }
+  for (int i = 0; i < kWin; ++i) L[i] = a.context_lens[seq_of(a, min(64 * i + lane, a.num_seqs - 1))];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) L[i] = 64 * i + lane < a.num_seqs ? clamp_ctx(L[i], a.max_ctx) : 0;
   ws.nw = 0;
 #pragma unroll
   for (int i = 0; i < kWin; ++i) {
@@ -303,29 +306,39 @@ struct AppendRows {
   static constexpr int PPI = 64 / LPP;     // pieces per wave-wide instruction
   static_assert(LPP >= 1 && LPP <= 64 && 64 % LPP == 0, "a piece is a whole number of lanes");
   u32x4 v;
-  int64_t p, slot;
+  int64_t p;
+  uint32_t slot_lo, slot_hi;  // the slot's two 32-bit halves (an int32 slot: its value twice)
   int ctx;
 
   // Issue the loads of piece p (this lane's 16 bytes, the slot, the length);
-  // nothing here waits for them.
+  // nothing here waits for them.  Every lane loads -- a piece past the last
+  // reads the last one's again, and store() skips it -- and through pointers
+  // the compiler knows to be global: a load under a per-lane condition was
+  // awaited at once, and a flat one made the next wait for a scalar load
+  // wait for it too, each a memory round trip ahead of the decode work.
   __device__ __forceinline__ void load(const DecodeArgs &a, int64_t piece, int lane) {
     p = piece;
-    if (p >= 2 * (int64_t)a.num_seqs * a.num_kv_heads) return;
-    const int kvh = (int)(p % a.num_kv_heads);
-    const bool is_v = (p / a.num_kv_heads) & 1;
-    const int64_t n = p / (2 * (int64_t)a.num_kv_heads);
+    const int64_t pieces = 2 * (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t q = p < pieces ? p : pieces - 1;
+    const int kvh = (int)(q % a.num_kv_heads);
+    const bool is_v = (q / a.num_kv_heads) & 1;
+    const int64_t n = q / (2 * (int64_t)a.num_kv_heads);
     const int64_t c = (int64_t)(lane % LPP) * (16 / EB);  // this lane's element of the row
     // both candidate addresses as values (a choice between fields of the
-    // kernel's argument block would place that block in private memory)
+    // kernel's argument block would place that block in private memory), the
+    // load through a global-memory pointer made from the chosen one
+    typedef const __attribute__((address_space(1))) u32x4 global_u32x4;
     const uintptr_t src_k = (uintptr_t)a.k_new + (uintptr_t)((n * a.kn_ss + kvh * a.kn_sh + c) * EB);
     const uintptr_t src_v = (uintptr_t)a.v_new + (uintptr_t)((n * a.vn_ss + kvh * a.vn_sh + c) * EB);
-    v = ld16(reinterpret_cast<const void *>(is_v ? src_v : src_k));
-    slot = a.slot_i64 ? reinterpret_cast<const int64_t *>(a.slot_mapping)[n]
-                      : (int64_t)reinterpret_cast<const int32_t *>(a.slot_mapping)[n];
+    v = *reinterpret_cast<global_u32x4 *>(is_v ? src_v : src_k);
+    const char *sp = static_cast<const char *>(a.slot_mapping) + n * (a.slot_i64 ? 8 : 4);
+    slot_lo = *reinterpret_cast<const uint32_t *>(sp);
+    slot_hi = *reinterpret_cast<const uint32_t *>(sp + (a.slot_i64 ? 4 : 0));
     ctx = a.context_lens[n];
   }
   // Store the piece to its slot (after the loads have arrived).
   __device__ __forceinline__ void store(const DecodeArgs &a, int lane) const {
+    const int64_t slot = a.slot_i64 ? (int64_t)(((uint64_t)slot_hi << 32) | slot_lo) : (int64_t)(int32_t)slot_lo;
     if (p >= 2 * (int64_t)a.num_seqs * a.num_kv_heads || slot < 0 || slot >= a.num_slots || ctx <= 0) return;
     const int kvh = (int)(p % a.num_kv_heads);
     const bool is_v = (p / a.num_kv_heads) & 1;
