@@ -19,10 +19,12 @@ NTHREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 # q-dtype bound is the stated target; the fp32-output bound isolates the
 # kernel's own error (fp32 accumulation, hardware exp2) from output rounding:
 # 1e-5 for 16-bit and fp32 caches (fp32 sums over <= 128k tokens of |v| ~ 1
-# with weights kept to ~16 bits past one rounding), 1e-3 for fp8 caches
-# (the same arithmetic on values ~ 2^-4 coarser; measured ~2e-5).
+# with weights kept to ~16 bits past one rounding), 5e-4 for fp8 caches:
+# their workloads draw per-head and per-block magnitudes, so outputs reach
+# |out| ~ 16, and the error follows the output's size (measured up to 2.0e-4
+# at |out| ~ 13, about 1.5e-5 of it); a tenfold regression still fails.
 TOL_OUT = {"f32": 2e-3, "f16": 2e-3, "bf16": 2e-3, "fp8": 3e-2}
-TOL_F32 = {"f32": 1e-5, "f16": 1e-5, "bf16": 1e-5, "fp8": 1e-3}
+TOL_F32 = {"f32": 1e-5, "f16": 1e-5, "bf16": 1e-5, "fp8": 5e-4}
 
 
 def log(*args):
